@@ -1,0 +1,113 @@
+// plan.h -- launch planning for the fused attention forward kernels.
+//
+// Pure C++ (no HIP types), so the host-side tests can compile it with g++.
+// The same decode runs on the GPU at the top of every workgroup.
+//
+// Work partitioning (the FlashAttention-2 change the pages describe on
+// "FlashAttention-4震撼发布" and "FlashAttention (SV)", section
+// "FlashAttention-2 (2023)": parallelise over query blocks as well as over
+// batch and heads):
+//   * one wave owns `qpw` consecutive query rows of one query head and keeps
+//     them for the whole pass (the resident Q tile);
+//   * a workgroup holds `nw` waves that share every K/V tile staged in LDS,
+//     so all its waves read the same key/value head: it covers `hw` query
+//     heads of one GQA group (hw divides both nw and Hq/Hkv) times
+//     `pos` = qpw*nw/hw query positions;
+//   * workgroups are numbered group-major (group = batch, kv head, head
+//     subset) with the query blocks of a group consecutive; for causal
+//     masking the heaviest query block (the last one) comes first;
+//   * the hardware hands workgroup ids round-robin to the 8 XCDs of an
+//     MI355X, each with its own L2.  When the count divides by 8 the id is
+//     remapped so that XCD x runs the x-th contiguous eighth of that order,
+//     which keeps the workgroups that read one K/V head on one L2.
+#ifndef FA_PLAN_H
+#define FA_PLAN_H
+
+#if defined(__HIPCC__)
+#define FA_HD __host__ __device__
+#else
+#define FA_HD
+#endif
+
+struct fa_plan_t {
+  int B, Hq, Hkv, Nq, Nk;
+  int causal;
+  int G;      // Hq / Hkv, query heads per key/value head
+  int qpw;    // query rows per wave
+  int nw;     // waves per workgroup
+  int hw;     // query heads per workgroup
+  int pos;    // query positions per workgroup
+  int nqb;    // query blocks per head: ceil(Nq / pos)
+  int nhg;    // head subsets per GQA group: G / hw
+  int xcd;    // 1 if workgroup ids are remapped XCD-contiguously
+  long long nwg;  // workgroups in the grid
+};
+
+// Largest of {nw, nw/2, ..., 1} that divides g (nw is a power of two).
+FA_HD inline int fa_heads_per_wg(int g, int nw) {
+  int hw = nw;
+  while (hw > 1 && (g % hw) != 0) hw >>= 1;
+  return hw;
+}
+
+FA_HD inline fa_plan_t fa_make_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int qpw, int nw) {
+  fa_plan_t p;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.causal = causal;
+  p.G = Hq / Hkv;
+  p.qpw = qpw;
+  p.nw = nw;
+  p.hw = fa_heads_per_wg(p.G, nw);
+  p.pos = qpw * nw / p.hw;
+  p.nqb = (Nq + p.pos - 1) / p.pos;
+  p.nhg = p.G / p.hw;
+  p.nwg = (long long)B * Hkv * p.nhg * p.nqb;
+  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  return p;
+}
+
+// Waves per workgroup: the largest of 4, 2, 1 that still leaves at least
+// `min_wg` workgroups (enough to fill the chip several times); 1 otherwise.
+FA_HD inline fa_plan_t fa_choose_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int qpw,
+                                      long long min_wg) {
+  for (int nw = 4; nw > 1; nw >>= 1) {
+    fa_plan_t p = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, nw);
+    if (p.nwg >= min_wg) return p;
+  }
+  return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 1);
+}
+
+struct fa_work_t {
+  int b, hkv, hq0, qpos0;  // batch, kv head, first query head, first query position
+};
+
+// Workgroup hardware id -> its work.  A bijection of [0, nwg) onto the
+// (group, query block) pairs.
+FA_HD inline fa_work_t fa_decode(const fa_plan_t& p, long long id) {
+  long long L = p.xcd ? (id % 8) * (p.nwg / 8) + id / 8 : id;
+  long long g = L / p.nqb;
+  int qi = (int)(L % p.nqb);
+  if (p.causal) qi = p.nqb - 1 - qi;
+  fa_work_t w;
+  int hg = (int)(g % p.nhg);
+  g /= p.nhg;
+  w.hkv = (int)(g % p.Hkv);
+  w.b = (int)(g / p.Hkv);
+  w.hq0 = w.hkv * p.G + hg * p.hw;
+  w.qpos0 = qi * p.pos;
+  return w;
+}
+
+// Number of key tiles of `bc` keys a workgroup starting at query position
+// qpos0 must stream (causal: bottom-right aligned visibility j <= i + Nk - Nq).
+FA_HD inline int fa_num_kv_tiles(const fa_plan_t& p, int qpos0, int bc) {
+  int klast = p.Nk - 1;
+  if (p.causal) {
+    int qlast = qpos0 + p.pos - 1;
+    if (qlast > p.Nq - 1) qlast = p.Nq - 1;
+    int k = qlast + p.Nk - p.Nq;
+    if (k < klast) klast = k;
+  }
+  return klast < 0 ? 0 : klast / bc + 1;
+}
+
+#endif  // FA_PLAN_H

@@ -1,0 +1,97 @@
+/*
+ * fa.h -- C ABI of libfa.so, a fused exact-attention forward pass for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * What is computed (the definition on "FlashAttention (SV)", section
+ * "Problematik med standard-attention"):
+ *
+ *     O   = softmax(scale * Q K^T) V            per (batch b, query head h)
+ *     LSE = ln sum_j exp(scale * q_i . k_j)     natural log, scale included
+ *
+ * without ever writing the N x N score matrix to memory: Q, K and V are tiled
+ * through on-chip memory, the softmax is computed online with a running row
+ * maximum and a running sum of exponentials ("FlashAttention (SV)", sections
+ * "Tiling och blockbearbetning" and "Online-beräkning av Softmax"), and one
+ * kernel does Q K^T, masking, softmax and the product with V (section
+ * "Sammanslagning av operationer").  The output rescaling that the online
+ * softmax needs is skipped while the running maximum stays within 2^8 of the
+ * value the exponentials were taken against ("FlashAttention-4震撼发布",
+ * first of the two algorithmic improvements); the result is exact either way.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Layout: contiguous row-major tensors
+ *     q, o : [B][Hq][Nq][d]        k, v : [B][Hkv][Nk][d]
+ *     lse  : [B][Hq][Nq] float32   (may be NULL: then it is not written)
+ * GQA/MQA ("FlashAttention-4震撼发布", FlashAttention-2 list): Hq must be a
+ *     multiple of Hkv; query head h reads key/value head h / (Hq / Hkv).
+ *     Hkv == Hq is ordinary multi-head attention, Hkv == 1 is MQA.
+ * Head dimension d: 64, 128 or 256 (FlashAttention-2 list: head sizes up to
+ *     256).
+ * causal: 0 or 1.  With causal = 1 key j is visible to query i iff
+ *     j <= i + (Nk - Nq) (bottom-right alignment; for Nq == Nk this is the
+ *     usual lower triangle).  A query that sees no key gets O = 0 and
+ *     LSE = -inf.
+ * scale: finite and > 0 (usually 1/sqrt(d)).
+ * Memory: every pointer is device memory owned by the caller, 16-byte
+ *     aligned.  The library allocates, frees and synchronises nothing and
+ *     keeps no per-call state; calls are asynchronous on `stream` (a
+ *     hipStream_t, NULL = the default stream), so buffers must stay alive
+ *     until the enqueued work is done.  Outputs must not overlap inputs.
+ *     Calls are thread-safe.
+ * Errors: argument errors are detected on the host before any HIP call and
+ *     nothing is enqueued.  A failed launch returns FA_ERR_HIP.  Faults inside
+ *     a kernel surface at the caller's next synchronisation.  No C++
+ *     exception crosses this interface.
+ */
+#ifndef FA_H
+#define FA_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,       /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,      /* B, Hq, Hkv, Nq or Nk < 1, or a tensor too large to index */
+  FA_ERR_HEAD_DIM = 3,   /* d not in {64, 128, 256} */
+  FA_ERR_GQA_RATIO = 4,  /* Hq not a multiple of Hkv */
+  FA_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 6,      /* scale not finite or not > 0 */
+  FA_ERR_HIP = 7,        /* the HIP runtime refused the launch */
+  FA_ERR_FLAG = 8        /* causal not 0 or 1 */
+} fa_status;
+
+/* Version of this interface; bumped on any incompatible change. */
+#define FA_ABI_VERSION 1
+int fa_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_status_string(fa_status s);
+
+/*
+ * bfloat16 forward pass.  q, k, v, o hold bf16 values; lse is float32.
+ * Products are accumulated in fp32; the probabilities multiply V in bf16;
+ * O is rounded to bf16 (nearest even).
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, void* stream);
+
+/*
+ * float32 forward pass: q, k, v, o hold float32 values.  The kernel splits
+ * every fp32 operand into a bf16 head and a bf16 tail (x = hi + lo, exact to
+ * about 2^-16 relative) and forms each product from the three largest
+ * partial products on bf16 MFMA, so scores and the output carry close to
+ * fp32 accuracy.
+ */
+fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                     int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */
