@@ -1,0 +1,199 @@
+"""Benchmark of the fused attention forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
+
+A step is one fa_fwd call over one batch of synthetic input of the chosen
+standing workload (default: the causal GQA long-context workload B=2, Hq=32,
+Hkv=8, N=8192, d=128, bf16).  Inputs are resident in HBM before timing
+starts; K steps are timed back to back with HIP events on the stream the
+kernel runs on.  Prints one JSON line on stdout (diagnostics go to stderr):
+
+  value     attention forward TFLOP/s = 4*B*Hq*Nq*Nk*d (halved when causal) / time
+  roofline  the kernel against the MI355X dense MFMA peak for its dtype, and
+            the HBM traffic measured by rocprofv3 counters for the same kernel
+            source (null when the source changed since the counters were taken)
+  cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
+            sample of the same workload (whole heads), as a reported baseline
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s + % of MFMA peak (bf16, causal GQA, N=8K, d=128)"
+# MI355X published dense peaks (no sparsity), TFLOP/s
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "fp8": 5000.0}
+KERNEL_SOURCES = ["exact_attention_07_amd/csrc/fa_fwd.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(cfg: int):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_config{cfg}.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """Time the fp64 oracle on whole (b, h) heads of the workload until budget_s elapsed."""
+    from oracle import attention_fp64
+    from oracle.formats import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    g = w.Hq // w.Hkv
+    done, flops, t_total = 0, 0.0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for b, h in heads:
+        q = bf16_bits_to_f64(x["q"][b:b + 1, h:h + 1])
+        k = bf16_bits_to_f64(x["k"][b:b + 1, h // g:h // g + 1])
+        v = bf16_bits_to_f64(x["v"][b:b + 1, h // g:h // g + 1])
+        t0 = time.perf_counter()
+        attention_fp64(q, k, v, w.softmax_scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        f = 4.0 * w.Nq * w.Nk * w.d
+        flops += f / 2 if w.causal else f
+        if t_total >= budget_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, fp64 two-pass oracle "
+                      f"(S and P materialised), {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--check", action="store_true", help="compare sampled rows with the oracle (stderr)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one 1 GiB device copy (reference for rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_attention_07_amd import api, gen
+
+    w, x = gen.make_config(args.config)
+    log(f"workload: {w.name}")
+    dev = torch.device("cuda:0")
+
+    def dev_tensor(a):
+        if w.dtype == "f32":
+            return torch.from_numpy(a).to(dev)
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if w.dtype == "fp8":
+        raise SystemExit("the fp8 workload is not benchmarked by this harness yet")
+    q, k, v = (dev_tensor(x[t]) for t in "qkv")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    fwd = api.fa_fwd if w.dtype == "bf16" else api.fa_fwd_f32
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    log(f"{args.steps} launches: {ms:.4f} ms/launch (events), {wall / args.steps * 1e3:.4f} ms/launch (wall), "
+        f"{tflops:.1f} TFLOP/s")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device copy done")
+
+    if args.check:
+        from oracle import attention_rows_fp64
+        from oracle.formats import bf16_bits_to_f64
+        rows = [(0, 0, 0), (w.B - 1, w.Hq - 1, w.Nq - 1), (0, w.Hq // 2, w.Nq // 3)]
+        conv = (lambda a: a.astype(np.float64)) if w.dtype == "f32" else bf16_bits_to_f64
+        o_ref, l_ref = attention_rows_fp64(conv(x["q"]), conv(x["k"]), conv(x["v"]), w.softmax_scale, w.causal,
+                                           rows)
+        oo = o.float().cpu().numpy()
+        ll = lse.cpu().numpy()
+        err = max(float(np.abs(oo[b, h, i] - o_ref[r]).max()) for r, (b, h, i) in enumerate(rows))
+        lerr = max(abs(float(ll[b, h, i]) - l_ref[r]) for r, (b, h, i) in enumerate(rows))
+        log(f"check on {len(rows)} rows: max|dO|={err:.2e} max|dLSE|={lerr:.2e}")
+
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = load_traffic(args.config)
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1), generated on the host, resident in HBM before timing)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                   "causal": w.causal, "kernel": "fa_fwd_kernel"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
