@@ -1,0 +1,87 @@
+// Host-side checks of the launch plan (compiled with g++ by tests/test_plan.py).
+#include <cstdio>
+#include <cstdlib>
+#include <set>
+#include <tuple>
+#include <vector>
+
+#include "plan.h"
+
+#define CHECK(c)                                                        \
+  do {                                                                  \
+    if (!(c)) {                                                         \
+      std::printf("FAIL %s:%d %s\n", __FILE__, __LINE__, #c);           \
+      std::exit(1);                                                     \
+    }                                                                   \
+  } while (0)
+
+static void check_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int qpw, int nw) {
+  fa_plan_t p = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, nw);
+  CHECK(p.hw >= 1 && nw % p.hw == 0 && p.G % p.hw == 0);
+  CHECK(p.pos * p.hw == qpw * nw);
+  // every (b, query head, query row) is covered by exactly one wave
+  std::vector<int> cover((size_t)B * Hq * Nq, 0);
+  std::set<std::tuple<int, int, int>> seen;
+  long long last_work = -1;
+  for (long long id = 0; id < p.nwg; ++id) {
+    fa_work_t w = fa_decode(p, id);
+    CHECK(w.b >= 0 && w.b < B && w.hkv >= 0 && w.hkv < Hkv);
+    CHECK(w.qpos0 >= 0 && w.qpos0 < Nq && w.qpos0 % p.pos == 0);
+    CHECK(seen.insert({w.b, w.hq0, w.qpos0}).second);  // bijection
+    for (int wave = 0; wave < nw; ++wave) {
+      int hq = w.hq0 + wave % p.hw;
+      CHECK(hq / (Hq / Hkv) == w.hkv);                 // GQA: the head reads its own kv head
+      int q0 = w.qpos0 + (wave / p.hw) * qpw;
+      for (int i = q0; i < q0 + qpw && i < Nq; ++i) cover[((size_t)w.b * Hq + hq) * Nq + i]++;
+    }
+    // tile count: the last visible key of the workgroup's last row
+    int nt = fa_num_kv_tiles(p, w.qpos0, 64);
+    int qlast = w.qpos0 + p.pos - 1 < Nq - 1 ? w.qpos0 + p.pos - 1 : Nq - 1;
+    int klast = causal ? (qlast + Nk - Nq < Nk - 1 ? qlast + Nk - Nq : Nk - 1) : Nk - 1;
+    CHECK(nt == (klast < 0 ? 0 : klast / 64 + 1));
+    if (nt > 0) CHECK(nt * 64 >= klast + 1 && (nt - 1) * 64 <= klast);
+    (void)last_work;
+  }
+  CHECK((long long)seen.size() == p.nwg);
+  for (int c : cover) CHECK(c == 1);
+  // without the XCD remap, causal workgroups of one group come heaviest first
+  if (causal && !p.xcd && p.nqb > 1) {
+    fa_work_t a = fa_decode(p, 0), b = fa_decode(p, 1);
+    CHECK(a.qpos0 > b.qpos0);
+  }
+}
+
+int main() {
+  for (int causal = 0; causal < 2; ++causal)
+    for (int nw : {1, 2, 4})
+      for (int qpw : {32, 64}) {
+        check_plan(2, 32, 8, 8192, 8192, causal, qpw, nw);
+        check_plan(8, 12, 12, 1024, 1024, causal, qpw, nw);
+        check_plan(1, 6, 2, 257, 257, causal, qpw, nw);
+        check_plan(2, 4, 2, 200, 333, causal, qpw, nw);
+        check_plan(1, 8, 1, 130, 130, causal, qpw, nw);
+        check_plan(1, 3, 3, 1, 77, causal, qpw, nw);
+        check_plan(1, 2, 2, 150, 40, causal, qpw, nw);
+        check_plan(3, 5, 5, 100, 100, causal, qpw, nw);
+      }
+  // XCD remap: the ids that land on one XCD (id % 8) form one contiguous block of the logical order
+  fa_plan_t p = fa_make_plan(2, 32, 8, 8192, 8192, 1, 64, 4);
+  CHECK(p.xcd == 1 && p.nwg == 2048);
+  for (int x = 0; x < 8; ++x) {
+    std::set<int> groups;
+    for (long long id = x; id < p.nwg; id += 8) {
+      fa_work_t w = fa_decode(p, id);
+      groups.insert(w.b * p.Hkv + w.hkv);
+    }
+    CHECK(groups.size() == 2);  // 16 (b, kv head) groups over 8 XCDs
+  }
+  // the first ids of an XCD get the heaviest (last) query block
+  CHECK(fa_decode(p, 0).qpos0 == 8192 - 64 && fa_decode(p, 8).qpos0 == 8192 - 128);
+  // plan choice keeps >= 1024 workgroups when possible
+  fa_plan_t c2 = fa_choose_plan(8, 12, 12, 1024, 1024, 1, 64, 1024);
+  CHECK(c2.nw == 1 && c2.nwg == 8 * 12 * 16);
+  fa_plan_t c3 = fa_choose_plan(2, 32, 8, 8192, 8192, 1, 64, 1024);
+  CHECK(c3.nw == 4 && c3.hw == 4);
+  std::printf("plan checks passed\n");
+  return 0;
+}

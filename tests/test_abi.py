@@ -1,0 +1,71 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/fa.h declares, and rejects invalid arguments on the host before any
+HIP call (so these calls launch nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_attention_07_amd import api
+    if not os.path.exists(api.LIB_PATH):
+        from exact_attention_07_amd import build
+        build.build()
+    return api.lib()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("fa_fwd", "fa_fwd_f32", "fa_status_string", "fa_abi_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.fa_abi_version() == 1
+    for s in range(9):
+        assert len(lib.fa_status_string(s)) > 0
+    assert lib.fa_status_string(123) == b"unknown status"
+
+
+P = 1 << 20          # a 16-byte-aligned fake device address; never dereferenced (validation fails first)
+GOOD = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=10, Nk=10, d=128, scale=0.1, causal=0)
+
+
+def call(lib, fn="fa_fwd", **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    f = getattr(lib, fn)
+    return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+             ctypes.c_float(a["scale"]), a["causal"], None)
+
+
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(o=None), 1),
+    (dict(B=0), 2), (dict(Hq=0), 2), (dict(Hkv=-1), 2), (dict(Nq=0), 2), (dict(Nk=0), 2),
+    (dict(d=96), 3), (dict(d=32), 3), (dict(d=512), 3),
+    (dict(Hq=6, Hkv=4), 4),
+    (dict(q=P + 8), 5), (dict(o=P + 4), 5), (dict(lse=P + 4), 5),
+    (dict(scale=0.0), 6), (dict(scale=-1.0), 6), (dict(scale=float("inf")), 6), (dict(scale=float("nan")), 6),
+    (dict(causal=2), 8), (dict(causal=-1), 8),
+    (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Nq=1 << 30, Nk=1 << 30), 2),
+])
+def test_invalid_arguments_are_rejected_on_the_host(lib, fn, kw, status):
+    assert call(lib, fn, **kw) == status
