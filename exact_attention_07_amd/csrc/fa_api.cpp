@@ -28,9 +28,11 @@ fa_status validate(const void* q, const void* k, const void* v, const void* o, c
     return FA_ERR_ALIGN;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
-  // every element offset must fit in 63 bits and the grid in 31 bits
+  // every element offset must fit in 63 bits, and one key/value head (the
+  // range of a buffer resource) in 31 bits
   const double elems = (double)B * (double)(Hq > Hkv ? Hq : Hkv) * (double)(Nq > Nk ? Nq : Nk) * d;
   if (elems > 9.0e18) return FA_ERR_SHAPE;
+  if ((double)Nk * d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -38,8 +40,10 @@ fa_status forward(const void* q, const void* k, const void* v, void* o, float* l
                   int Nk, int d, float scale, int causal, void* stream, int f32) {
   fa_status st = validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
   if (st != FA_OK) return st;
-  const fa_plan_t p =
-      fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, fa::queries_per_wave(d, f32), MIN_WORKGROUPS);
+  const int qpw = fa::queries_per_wave(d, f32);
+  // the fp32 path is instantiated for 4-wave workgroups only
+  const fa_plan_t p = f32 ? fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4)
+                          : fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS);
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
   const float c = (float)((double)scale * LOG2E);
   hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, (hipStream_t)stream);

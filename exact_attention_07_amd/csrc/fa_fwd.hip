@@ -7,16 +7,19 @@
 //
 // Mapping onto CDNA4
 // ------------------
-// * Each wave owns QPW query rows (two 32-row blocks for d <= 128, one for
-//   d = 256) and keeps their Q fragments in VGPRs for the whole pass.
-// * A workgroup of nw waves (plan.h) streams K/V tiles of BC = 64 keys
+// * Each wave owns QPW query rows (two 32-row blocks for d = 64, one for
+//   d >= 128) and keeps their Q fragments in VGPRs for the whole pass; at
+//   d <= 128 a wave needs at most 256 VGPRs, so two waves share each SIMD and
+//   one wave's softmax overlaps the other's matrix products.
+// * A workgroup of NW waves (plan.h) streams K/V tiles of BC = 64 keys
 //   through LDS.  bf16 tiles are copied HBM -> LDS directly with
-//   global_load_lds_dwordx4 (16 B per lane), double buffered, so the copy of
-//   tile j+1 overlaps the math on tile j (the asynchronous next-block load of
-//   "FlashAttention-3 — 闪电注意力-3", section on minimising memory
-//   operations).  Rows are stored with an XOR swizzle of their 16-byte
-//   chunks so that both the row reads of K and the transposed reads of V hit
-//   distinct LDS banks.
+//   buffer_load_dwordx4 ... lds (16 B per lane, bounds-checked by the buffer
+//   resource so rows past the end read as zero), double buffered, so the copy
+//   of tile j+1 overlaps the math on tile j (the asynchronous next-block load
+//   of "FlashAttention-3 — 闪电注意力-3", section on minimising memory
+//   operations).  LDS rows are padded so that both the row reads of K and the
+//   transposed reads of V hit distinct banks with plain "lane base +
+//   constant" addresses.
 // * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
 //   the accumulator then holds, in each lane, 16 keys of ONE query, so a row
 //   maximum is an in-lane max plus one v_permlane32_swap, and the fp32
@@ -62,29 +65,31 @@ constexpr float LN2 = 0.693147180559945309f;
 
 template <int D, bool F32>
 struct Cfg {
-  static constexpr int QPW = (D <= 128 && !F32) ? 64 : 32;  // query rows per wave
-  static constexpr int QB = QPW / 32;                        // 32-row query blocks per wave
-  static constexpr int KB = BC / 32;                         // 32-key blocks per tile
-  static constexpr int DS = D / 16;                          // k-steps of S^T = K Q^T
-  static constexpr int DB = D / 32;                          // 32-row blocks of O^T
-  static constexpr int PS = BC / 16;                         // k-steps of O^T += V^T P^T
-  static constexpr int CPR = D / 8;                          // 16-byte chunks per row
-  static constexpr int TILE = BC * D * 2;                    // bytes of one bf16 tile
+  // query rows per wave: d = 64 keeps 64 rows, d >= 128 keeps 32 so that
+  // (d = 128) the whole wave state fits in 256 VGPRs and two waves share a SIMD
+  static constexpr int QPW = (D == 64 && !F32) ? 64 : 32;
+  static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
+  static constexpr int QB = QPW / 32;  // 32-row query blocks per wave
+  static constexpr int KB = BC / 32;   // 32-key blocks per tile
+  static constexpr int DS = D / 16;    // k-steps of S^T = K Q^T
+  static constexpr int DB = D / 32;    // 32-row blocks of O^T
+  static constexpr int PS = BC / 16;   // k-steps of O^T += V^T P^T
+  // LDS tile: BC rows of D bf16, each row padded by PAD 16-byte slots.  The
+  // row stride RS makes both access patterns conflict-free on the 64 banks:
+  // 16 lanes reading one 16-byte chunk of 16 consecutive rows (K fragments),
+  // and 16 lanes reading a pair of adjacent chunks of 4 consecutive rows (the
+  // transposed V reads), while every address stays "lane base + constant".
+  static constexpr int CPR = D / 8;                    // data slots per row
+  static constexpr int PAD = (D == 64) ? 1 : 3;
+  static constexpr int SPR = CPR + PAD;                // slots per LDS row
+  static constexpr int RS = SPR * 16;                  // LDS row stride, bytes
+  static constexpr int TILE = BC * RS;                 // bytes of one tile
+  static constexpr int SLOTS = BC * SPR;
+  static constexpr int INS = (SLOTS + 63) / 64;        // 64-lane copy instructions per tile
   static constexpr int STAGES = F32 ? 1 : 2;
-  static constexpr int TILES_PER_STAGE = F32 ? 4 : 2;        // K,V (bf16) or Khi,Klo,Vhi,Vlo
+  static constexpr int TILES_PER_STAGE = F32 ? 4 : 2;  // K,V (bf16) or Khi,Klo,Vhi,Vlo
   static constexpr int LDS = STAGES * TILES_PER_STAGE * TILE;
 };
-
-// XOR swizzle of the 16-byte chunk index within a row.  For 16 consecutive
-// rows read at one chunk, and for any 4 consecutive rows (aligned) read at a
-// pair of adjacent chunks, the swizzled positions fall on distinct banks.
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (CPR == 8) return (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
-  else return ((r & 7) << 1) | ((r >> 3) & 1);
-}
-template <int CPR>
-__device__ __forceinline__ int slot(int r, int c) { return r * CPR + (c ^ swz<CPR>(r)); }
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -101,50 +106,72 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bf16x8 lds_b128(const char* p) { return *(const bf16x8*)p; }
+__device__ __forceinline__ bf16x8 lds_b128(LDS_AS const char* p) { return *(LDS_AS const bf16x8*)p; }
 
 __device__ __forceinline__ bf16x8 join(i16x4 a, i16x4 b) {
   i16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// V^T fragment for O^T += V^T P^T, k-step ps (keys ps*16..ps*16+15 of the
-// tile in the order the S^T accumulator holds them), rows db*32..db*32+31 of
-// d.  Element e of lane l is V[ps*16 + (e/4)*8 + (l/32)*4 + e%4][db*32 + l%32].
-// ds_read_b64_tr_b16 gives output lane t (of each 16-lane group) element c =
-// element t%4 of the 8 bytes addressed by lane 4c + t/4 of that group.
-template <int CPR>
-__device__ __forceinline__ bf16x8 v_frag(const char* vt, int ps, int db, int lane) {
+// Per-lane byte offset of the K fragment (A operand of S^T = K Q^T):
+// row lane%32 of the 32-key block, chunk lane/32 of the 16-element k-step.
+template <int RS>
+__device__ __forceinline__ int k_lane_off(int lane) { return (lane & 31) * RS + (lane >> 5) * 16; }
+
+// Per-lane byte offset of the transposed V read.  The V^T fragment of k-step
+// ps and d-block db holds, in element e of lane l, V[ps*16 + (e/4)*8 +
+// (l/32)*4 + e%4][db*32 + l%32] (the key order of the S^T accumulator).
+// ds_read_b64_tr_b16 gives output lane t of each 16-lane group element c =
+// element t%4 of the 8 bytes addressed by lane 4c + t/4 of the group, so lane
+// (16g + s) addresses row (g/2)*4 + s/4 (+ ps*16 + 8h), columns
+// db*32 + 16(g%2) + 4(s%4) .. +3.
+template <int RS>
+__device__ __forceinline__ int v_lane_off(int lane) {
   const int g = lane >> 4, s = lane & 15;
-  i16x4 h[2];
-#pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int r = ps * 16 + 8 * hh + (g >> 1) * 4 + (s >> 2);
-    const int c = db * 4 + 2 * (g & 1) + ((s & 3) >> 1);
-    const int off = slot<CPR>(r, c) * 16 + (s & 1) * 8;
-    h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vt + off));
-  }
-  return join(h[0], h[1]);
+  return ((g >> 1) * 4 + (s >> 2)) * RS + (2 * (g & 1) + ((s & 3) >> 1)) * 16 + (s & 1) * 8;
 }
 
-// Issue the HBM -> LDS copy of one bf16 tile (BC rows of D elements starting
-// at key j0; rows past Nk repeat row Nk-1 so every read stays in bounds).
-// Instruction `ins` fills LDS bytes [ins*1024, ins*1024 + 1024): lane t the
-// 16-byte slot ins*64 + t, which holds chunk (slot % CPR) ^ swz(row).
-template <int D>
-__device__ __forceinline__ void issue_tile_copy(const __bf16* src, int j0, int Nk, char* tile, int wave, int nw,
-                                                int lane) {
-  constexpr int CPR = D / 8;
-  constexpr int INS = BC * CPR / 64;
-  for (int ins = wave; ins < INS; ins += nw) {
-    const int sl = ins * 64 + lane;
-    const int r = sl / CPR, pp = sl % CPR;
-    const int c = pp ^ swz<CPR>(r);
-    const int key = min(j0 + r, Nk - 1);
-    const __bf16* g = src + (size_t)key * D + c * 8;
-    __builtin_amdgcn_global_load_lds((const void*)g, (LDS_AS void*)(tile + ins * 1024), 16, 0, 0);
-  }
+template <int RS>
+__device__ __forceinline__ bf16x8 v_frag(LDS_AS const char* vlane, int ps, int db) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vlane + (ps * 16) * RS + db * 64));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vlane + (ps * 16 + 8) * RS + db * 64));
+  return join(a, b);
 }
+
+// HBM -> LDS copy plan of one wave: copy instruction i of the wave (global
+// instruction index i*NW + wave) fills LDS bytes [ins*1024, ins*1024 + 1024)
+// of the tile, lane t the slot ins*64 + t (BC*SPR is a multiple of 64, so
+// the last instruction ends exactly at the end of the tile).  goff is the
+// byte offset of the slot's data within the tile's rows in HBM (rows of D
+// bf16, contiguous); padding slots get an offset past any buffer range, so
+// their load reads zero and writes it into the (never read) padding.
+template <int D, int NW>
+struct CopyPlan {
+  using C = Cfg<D, false>;
+  static constexpr int MI = (C::INS + NW - 1) / NW;
+  static constexpr unsigned OUT_OF_RANGE = 0x7ffffff0u;
+  unsigned goff[MI];
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int sl = (i * NW + wave) * 64 + lane;
+      const int r = sl / C::SPR, pp = sl % C::SPR;
+      goff[i] = pp < C::CPR ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
+    }
+  }
+  // Copy BC rows starting at key j0 of a [Nk][D] bf16 matrix; rows >= Nk
+  // fall outside the buffer range and read as zero.
+  __device__ __forceinline__ void issue(const __bf16* base, int j0, int Nk, LDS_AS char* tile, int wave) const {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j0 * D), (short)0, (Nk - j0) * (D * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (i * NW + wave < C::INS)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tile + (i * NW + wave) * 1024), 16, goff[i], 0,
+                                                 0, 0);
+    }
+  }
+};
 
 __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -155,35 +182,39 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
   }
 }
 
-// fp32 tile -> (hi, lo) bf16 tiles through registers (synchronous).
+// fp32 tile -> (hi, lo) bf16 tiles through registers (synchronous); rows past
+// Nk are zero.
 template <int D>
-__device__ __forceinline__ void copy_tile_f32(const float* src, int j0, int Nk, char* tile_hi, char* tile_lo) {
-  constexpr int CPR = D / 8;
-  for (int sl = threadIdx.x; sl < BC * CPR; sl += blockDim.x) {
-    const int r = sl / CPR, pp = sl % CPR;
-    const int c = pp ^ swz<CPR>(r);
-    const int key = min(j0 + r, Nk - 1);
-    const f32x4* g = (const f32x4*)(src + (size_t)key * D + c * 8);
-    f32x4 a = g[0], b = g[1];
-    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-    bf16x8 hi, lo;
-    split8(x, hi, lo);
-    *(bf16x8*)(tile_hi + sl * 16) = hi;
-    *(bf16x8*)(tile_lo + sl * 16) = lo;
+__device__ __forceinline__ void copy_tile_f32(const float* src, int j0, int Nk, LDS_AS char* tile_hi,
+                                              LDS_AS char* tile_lo) {
+  using C = Cfg<D, true>;
+  for (int sl = threadIdx.x; sl < C::SLOTS; sl += blockDim.x) {
+    const int r = sl / C::SPR, pp = sl % C::SPR;
+    if (pp >= C::CPR) continue;
+    bf16x8 hi = {}, lo = {};
+    if (j0 + r < Nk) {
+      const f32x4* g = (const f32x4*)(src + (size_t)(j0 + r) * D + pp * 8);
+      f32x4 a = g[0], b = g[1];
+      float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      split8(x, hi, lo);
+    }
+    *(LDS_AS bf16x8*)(tile_hi + sl * 16) = hi;
+    *(LDS_AS bf16x8*)(tile_lo + sl * 16) = lo;
   }
 }
 
-template <int D, bool CAUSAL, bool F32>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(const void* __restrict__ Qp, const void* __restrict__ Kp,
-                                                     const void* __restrict__ Vp, void* __restrict__ Op,
-                                                     float* __restrict__ LSE, fa_plan_t p, float c) {
+template <int D, bool CAUSAL, bool F32, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, F32>::WAVES_PER_SIMD)))
+void fa_fwd_kernel(const void* __restrict__ Qp, const void* __restrict__ Kp, const void* __restrict__ Vp,
+                   void* __restrict__ Op, float* __restrict__ LSE, fa_plan_t p, float c) {
   using C = Cfg<D, F32>;
-  constexpr int QPW = C::QPW, QB = C::QB, KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, CPR = C::CPR;
-  __shared__ __attribute__((aligned(1024))) char smem[C::LDS];
+  constexpr int QPW = C::QPW, QB = C::QB, KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RS = C::RS;
+  __shared__ __attribute__((aligned(1024))) char smem_[C::LDS];
+  LDS_AS char* const smem = (LDS_AS char*)smem_;
 
   const fa_work_t w = fa_decode(p, blockIdx.x);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int nw = p.nw;
+  // the wave index is uniform across the wave: keep it in an SGPR
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hq = w.hq0 + wave % p.hw;
   const int q0w = w.qpos0 + (wave / p.hw) * QPW;
   const int Nq = p.Nq, Nk = p.Nk;
@@ -229,19 +260,25 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const void* __restrict__ Qp
     for (int db = 0; db < DB; ++db) o[qb][db] = (f32x16){};
   }
 
+  const int koff_l = k_lane_off<RS>(lane);
+  const int voff_l = v_lane_off<RS>(lane);
+  const __bf16* kbase = (const __bf16*)Kp + kvoff;
+  const __bf16* vbase = (const __bf16*)Vp + kvoff;
+  CopyPlan<D, NW> cp;
   if constexpr (!F32) {
+    cp.init(wave, lane);
     if (ntiles > 0) {
-      issue_tile_copy<D>((const __bf16*)Kp + kvoff, 0, Nk, smem, wave, nw, lane);
-      issue_tile_copy<D>((const __bf16*)Vp + kvoff, 0, Nk, smem + C::TILE, wave, nw, lane);
+      cp.issue(kbase, 0, Nk, smem, wave);
+      cp.issue(vbase, 0, Nk, smem + C::TILE, wave);
     }
   }
 
   for (int j = 0; j < ntiles; ++j) {
     const int j0 = j * BC;
-    const char* kt;
-    const char* vt;
-    const char* ktl = nullptr;
-    const char* vtl = nullptr;
+    LDS_AS const char* kt;
+    LDS_AS const char* vt;
+    LDS_AS const char* ktl = nullptr;
+    LDS_AS const char* vtl = nullptr;
     if constexpr (F32) {
       __syncthreads();
       copy_tile_f32<D>((const float*)Kp + kvoff, j0, Nk, smem, smem + C::TILE);
@@ -255,9 +292,9 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const void* __restrict__ Qp
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (j + 1 < ntiles) {
-        char* nxt = smem + ((j + 1) & 1) * 2 * C::TILE;
-        issue_tile_copy<D>((const __bf16*)Kp + kvoff, j0 + BC, Nk, nxt, wave, nw, lane);
-        issue_tile_copy<D>((const __bf16*)Vp + kvoff, j0 + BC, Nk, nxt + C::TILE, wave, nw, lane);
+        LDS_AS char* nxt = smem + ((j + 1) & 1) * 2 * C::TILE;
+        cp.issue(kbase, j0 + BC, Nk, nxt, wave);
+        cp.issue(vbase, j0 + BC, Nk, nxt + C::TILE, wave);
       }
       kt = smem + (j & 1) * 2 * C::TILE;
       vt = kt + C::TILE;
@@ -270,19 +307,21 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const void* __restrict__ Qp
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[kb][qb] = (f32x16){};
+    LDS_AS const char* klane = kt + koff_l;
+    LDS_AS const char* klane_lo = F32 ? ktl + koff_l : nullptr;
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int off = slot<CPR>(kb * 32 + (lane & 31), ds * 2 + (lane >> 5)) * 16;
-        const bf16x8 kf = lds_b128(kt + off);
+        const int off = kb * 32 * RS + ds * 32;
+        const bf16x8 kf = lds_b128(klane + off);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           s[kb][qb] = mfma(kf, qf[qb][ds], s[kb][qb]);
           if constexpr (F32) s[kb][qb] = mfma(kf, qlo[qb][ds], s[kb][qb]);
         }
         if constexpr (F32) {
-          const bf16x8 kl = lds_b128(ktl + off);
+          const bf16x8 kl = lds_b128(klane_lo + off);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma(kl, qf[qb][ds], s[kb][qb]);
         }
@@ -296,12 +335,10 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const void* __restrict__ Qp
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           const int query = q0w + qb * 32 + (lane & 31);
-          const int kmax = CAUSAL ? min(Nk - 1, query + Nk - Nq) : Nk - 1;
+          const int kmax = (CAUSAL ? min(Nk - 1, query + Nk - Nq) : Nk - 1) - j0 - kb * 32 - (lane >> 5) * 4;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = j0 + kb * 32 + (i >> 2) * 8 + (lane >> 5) * 4 + (i & 3);
-            if (key > kmax) s[kb][qb][i] = NEG_INF;
-          }
+          for (int i = 0; i < 16; ++i)
+            if ((i >> 2) * 8 + (i & 3) > kmax) s[kb][qb][i] = NEG_INF;
         }
     }
 
@@ -360,18 +397,20 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const void* __restrict__ Qp
     }
 
     // ---- O^T += V^T P^T
+    LDS_AS const char* vlane = vt + voff_l;
+    LDS_AS const char* vlane_lo = F32 ? vtl + voff_l : nullptr;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps) {
-        const bf16x8 vf = v_frag<CPR>(vt, ps, db, lane);
+        const bf16x8 vf = v_frag<RS>(vlane, ps, db);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           o[qb][db] = mfma(vf, pf[qb][ps], o[qb][db]);
           if constexpr (F32) o[qb][db] = mfma(vf, pl[qb][ps], o[qb][db]);
         }
         if constexpr (F32) {
-          const bf16x8 vl = v_frag<CPR>(vtl, ps, db, lane);
+          const bf16x8 vl = v_frag<RS>(vlane_lo, ps, db);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma(vl, pf[qb][ps], o[qb][db]);
         }
@@ -411,25 +450,37 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(const void* __restrict__ Qp
 }
 
 // ---------------------------------------------------------------- launchers
-template <int D, bool CAUSAL, bool F32>
-static hipError_t launch(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p,
-                         float c, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, F32>), dim3((unsigned)p.nwg), dim3(64 * p.nw), 0, stream, q, k, v,
-                     o, lse, p, c);
-  return hipGetLastError();
-}
+// Every variant is instantiated explicitly (implicit instantiation through
+// the launch expression alone does not always emit the host-side stub).
+#define FA_INST(DD, CC, FF, NN)                                                                        \
+  template __global__ void fa_fwd_kernel<DD, CC, FF, NN>(const void* __restrict__, const void* __restrict__, \
+                                                         const void* __restrict__, void* __restrict__,    \
+                                                         float* __restrict__, fa_plan_t, float);
+#define FA_VARIANTS(X)                                                                                  \
+  X(64, false, false, 1) X(64, false, false, 2) X(64, false, false, 4)                                  \
+  X(64, true, false, 1) X(64, true, false, 2) X(64, true, false, 4)                                     \
+  X(128, false, false, 1) X(128, false, false, 2) X(128, false, false, 4)                               \
+  X(128, true, false, 1) X(128, true, false, 2) X(128, true, false, 4)                                  \
+  X(256, false, false, 1) X(256, false, false, 2) X(256, false, false, 4)                               \
+  X(256, true, false, 1) X(256, true, false, 2) X(256, true, false, 4)                                  \
+  X(64, false, true, 4) X(64, true, true, 4) X(128, false, true, 4) X(128, true, true, 4)               \
+  X(256, false, true, 4) X(256, true, true, 4)
+FA_VARIANTS(FA_INST)
 
 int queries_per_wave(int d, int f32) {
   if (f32) return 32;
-  return d <= 128 ? 64 : 32;
+  return d == 64 ? 64 : 32;
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
                       float c, int f32, hipStream_t stream) {
-#define FA_CASE(DD, CC, FF) \
-  if (d == DD && p.causal == CC && f32 == FF) return launch<DD, CC, FF>(q, k, v, o, lse, p, c, stream);
-  FA_CASE(64, 0, 0) FA_CASE(64, 1, 0) FA_CASE(128, 0, 0) FA_CASE(128, 1, 0) FA_CASE(256, 0, 0) FA_CASE(256, 1, 0)
-  FA_CASE(64, 0, 1) FA_CASE(64, 1, 1) FA_CASE(128, 0, 1) FA_CASE(128, 1, 1) FA_CASE(256, 0, 1) FA_CASE(256, 1, 1)
+#define FA_CASE(DD, CC, FF, NN)                                                                      \
+  if (d == DD && (p.causal != 0) == CC && (f32 != 0) == FF && p.nw == NN) {                          \
+    hipLaunchKernelGGL((fa_fwd_kernel<DD, CC, FF, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream, q, k, v, \
+                       o, lse, p, c);                                                                \
+    return hipGetLastError();                                                                        \
+  }
+  FA_VARIANTS(FA_CASE)
 #undef FA_CASE
   return hipErrorInvalidValue;
 }
