@@ -7,8 +7,8 @@
 //
 // Mapping onto CDNA4
 // ------------------
-// * Each wave owns QPW query rows (two 32-row blocks for d = 64, one for
-//   d >= 128) and keeps their Q fragments in VGPRs for the whole pass; at
+// * Each wave owns 32 query rows and keeps their Q fragments in VGPRs for
+//   the whole pass; at
 //   d <= 128 a wave needs at most 256 VGPRs, so two waves share each SIMD and
 //   one wave's softmax overlaps the other's matrix products.
 // * A workgroup of NW waves (plan.h) streams K/V tiles of BC = 64 keys
@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_kernels.h"
 #include "plan.h"
 
@@ -62,12 +64,13 @@ constexpr float TAU = 8.0f;     // rescale threshold, log2 units
 constexpr int BC = 64;          // keys per K/V tile
 constexpr float NEG_INF = -__builtin_inff();
 constexpr float LN2 = 0.693147180559945309f;
+constexpr float TAU_EXP2 = 256.0f;  // 2^TAU
 
 template <int D, bool F32>
 struct Cfg {
-  // query rows per wave: d = 64 keeps 64 rows, d >= 128 keeps 32 so that
-  // (d = 128) the whole wave state fits in 256 VGPRs and two waves share a SIMD
-  static constexpr int QPW = (D == 64 && !F32) ? 64 : 32;
+  // query rows per wave: 32, so that (d <= 128) the whole wave state fits in
+  // 256 VGPRs and two waves share a SIMD
+  static constexpr int QPW = 32;
   static constexpr int WAVES_PER_SIMD = (D <= 128) ? 2 : 1;
   static constexpr int QB = QPW / 32;  // 32-row query blocks per wave
   static constexpr int KB = BC / 32;   // 32-key blocks per tile
@@ -86,10 +89,12 @@ struct Cfg {
   static constexpr int TILE = BC * RS;                 // bytes of one tile
   static constexpr int SLOTS = BC * SPR;
   static constexpr int INS = (SLOTS + 63) / 64;        // 64-lane copy instructions per tile
-  static constexpr int STAGES = F32 ? 1 : 2;
-  static constexpr int TILES_PER_STAGE = F32 ? 4 : 2;  // K,V (bf16) or Khi,Klo,Vhi,Vlo
-  static constexpr int LDS = STAGES * TILES_PER_STAGE * TILE;
 };
+
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int SG_VALU = 0x002;
+constexpr int SG_MFMA = 0x008;
+constexpr int SG_DS_READ = 0x100;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -154,21 +159,25 @@ struct CopyPlan {
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int sl = (i * NW + wave) * 64 + lane;
+      const int ins = i * NW + wave;
+      const int sl = ins * 64 + lane;
       const int r = sl / C::SPR, pp = sl % C::SPR;
-      goff[i] = pp < C::CPR ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
+      goff[i] = (ins < C::INS && pp < C::CPR) ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
     }
   }
   // Copy BC rows starting at key j0 of a [Nk][D] bf16 matrix; rows >= Nk
-  // fall outside the buffer range and read as zero.
-  __device__ __forceinline__ void issue(const __bf16* base, int j0, int Nk, LDS_AS char* tile, int wave) const {
+  // fall outside the buffer range and read as zero.  Every wave issues MI
+  // instructions; those past the tile (when NW does not divide INS) read
+  // nothing and write zeros into the 1 KB block `spare`.
+  __device__ __forceinline__ void issue(const __bf16* base, int j0, int Nk, LDS_AS char* tile, LDS_AS char* spare,
+                                        int wave) const {
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j0 * D), (short)0, (Nk - j0) * (D * 2), 0x00020000);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      if (i * NW + wave < C::INS)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(tile + (i * NW + wave) * 1024), 16, goff[i], 0,
-                                                 0, 0);
+      const int ins = i * NW + wave;
+      LDS_AS char* dst = (C::INS % NW == 0 || ins < C::INS) ? tile + ins * 1024 : spare;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], 0, 0, 0);
     }
   }
 };
@@ -203,285 +212,435 @@ __device__ __forceinline__ void copy_tile_f32(const float* src, int j0, int Nk, 
   }
 }
 
-template <int D, bool CAUSAL, bool F32, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, F32>::WAVES_PER_SIMD)))
-void fa_fwd_kernel(const void* __restrict__ Qp, const void* __restrict__ Kp, const void* __restrict__ Vp,
-                   void* __restrict__ Op, float* __restrict__ LSE, fa_plan_t p, float c) {
-  using C = Cfg<D, F32>;
-  constexpr int QPW = C::QPW, QB = C::QB, KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RS = C::RS;
-  __shared__ __attribute__((aligned(1024))) char smem_[C::LDS];
+// fp32 operands: each is split into bf16 hi + lo parts as it is staged
+// (synchronously, one tile at a time) and every product uses hi*hi + hi*lo +
+// lo*hi on the same MFMA layouts as the bf16 path.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void fa_fwd_f32_kernel(const float* __restrict__ Q, const float* __restrict__ K,
+                                                          const float* __restrict__ V, float* __restrict__ O,
+                                                          float* __restrict__ LSE, fa_plan_t p, float c) {
+  using C = Cfg<D, true>;
+  constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RS = C::RS;
+  __shared__ __attribute__((aligned(1024))) char smem_[4 * C::TILE];
   LDS_AS char* const smem = (LDS_AS char*)smem_;
+  LDS_AS char* const kt = smem;
+  LDS_AS char* const ktl = smem + C::TILE;
+  LDS_AS char* const vt = smem + 2 * C::TILE;
+  LDS_AS char* const vtl = smem + 3 * C::TILE;
 
   const fa_work_t w = fa_decode(p, blockIdx.x);
-  // the wave index is uniform across the wave: keep it in an SGPR
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hq = w.hq0 + wave % p.hw;
-  const int q0w = w.qpos0 + (wave / p.hw) * QPW;
+  const int q0w = w.qpos0 + (wave / p.hw) * 32;
   const int Nq = p.Nq, Nk = p.Nk;
   const int ntiles = fa_num_kv_tiles(p, w.qpos0, BC);
 
-  // keys visible to the wave: to some row (klast_w) and to every row (kfull_w)
   const bool live = q0w < Nq;
-  const int qlast_w = min(Nq - 1, q0w + QPW - 1);
+  const int qlast_w = min(Nq - 1, q0w + 31);
   const int klast_w = CAUSAL ? min(Nk - 1, qlast_w + Nk - Nq) : Nk - 1;
   const int kfull_w = CAUSAL ? min(Nk - 1, q0w + Nk - Nq) : Nk - 1;
 
   const size_t qoff = (size_t)(w.b * p.Hq + hq) * Nq * D;
   const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
 
-  // ---- resident Q fragments (B operand of S^T = K Q^T): column = query, k = d
-  bf16x8 qf[QB][DS];
-  bf16x8 qlo[F32 ? QB : 1][F32 ? DS : 1];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int qrow = min(q0w + qb * 32 + (lane & 31), Nq - 1);
+  bf16x8 qf[DS], qlo[DS];
+  {
+    const int qrow = min(q0w + (lane & 31), Nq - 1);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) {
-      const size_t off = qoff + (size_t)qrow * D + ds * 16 + (lane >> 5) * 8;
-      if constexpr (F32) {
-        const f32x4* g = (const f32x4*)((const float*)Qp + off);
-        f32x4 a = g[0], b = g[1];
-        float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        split8(x, qf[qb][ds], qlo[qb][ds]);
-      } else {
-        qf[qb][ds] = *(const bf16x8*)((const __bf16*)Qp + off);
-      }
+      const f32x4* g = (const f32x4*)(Q + qoff + (size_t)qrow * D + ds * 16 + (lane >> 5) * 8);
+      f32x4 a = g[0], b = g[1];
+      float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      split8(x, qf[ds], qlo[ds]);
     }
   }
 
-  f32x16 o[QB][DB];
-  float m_ref[QB], m_run[QB], lsum[QB];
+  f32x16 o[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_ref[qb] = NEG_INF;
-    m_run[qb] = NEG_INF;
-    lsum[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) o[qb][db] = (f32x16){};
-  }
-
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
   const int koff_l = k_lane_off<RS>(lane);
   const int voff_l = v_lane_off<RS>(lane);
-  const __bf16* kbase = (const __bf16*)Kp + kvoff;
-  const __bf16* vbase = (const __bf16*)Vp + kvoff;
-  CopyPlan<D, NW> cp;
-  if constexpr (!F32) {
-    cp.init(wave, lane);
-    if (ntiles > 0) {
-      cp.issue(kbase, 0, Nk, smem, wave);
-      cp.issue(vbase, 0, Nk, smem + C::TILE, wave);
-    }
-  }
 
   for (int j = 0; j < ntiles; ++j) {
     const int j0 = j * BC;
-    LDS_AS const char* kt;
-    LDS_AS const char* vt;
-    LDS_AS const char* ktl = nullptr;
-    LDS_AS const char* vtl = nullptr;
-    if constexpr (F32) {
-      __syncthreads();
-      copy_tile_f32<D>((const float*)Kp + kvoff, j0, Nk, smem, smem + C::TILE);
-      copy_tile_f32<D>((const float*)Vp + kvoff, j0, Nk, smem + 2 * C::TILE, smem + 3 * C::TILE);
-      __syncthreads();
-      kt = smem;
-      ktl = smem + C::TILE;
-      vt = smem + 2 * C::TILE;
-      vtl = smem + 3 * C::TILE;
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-      if (j + 1 < ntiles) {
-        LDS_AS char* nxt = smem + ((j + 1) & 1) * 2 * C::TILE;
-        cp.issue(kbase, j0 + BC, Nk, nxt, wave);
-        cp.issue(vbase, j0 + BC, Nk, nxt + C::TILE, wave);
-      }
-      kt = smem + (j & 1) * 2 * C::TILE;
-      vt = kt + C::TILE;
-    }
+    __syncthreads();
+    copy_tile_f32<D>(K + kvoff, j0, Nk, kt, ktl);
+    copy_tile_f32<D>(V + kvoff, j0, Nk, vt, vtl);
+    __syncthreads();
     if (!live || j0 > klast_w) continue;  // wave-uniform: nothing visible to this wave
 
-    // ---- S^T = K Q^T
-    f32x16 s[KB][QB];
+    // ---- S^T = K Q^T (three partial products)
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = (f32x16){};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int off = koff_l + kb * 32 * RS + ds * 32;
+        const bf16x8 kh = lds_b128(kt + off), kl = lds_b128(ktl + off);
+        s[kb] = mfma(kh, qf[ds], s[kb]);
+        s[kb] = mfma(kh, qlo[ds], s[kb]);
+        s[kb] = mfma(kl, qf[ds], s[kb]);
+      }
+
+    if (j0 + BC - 1 > kfull_w) {
+      const int query = q0w + (lane & 31);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int kmax = (CAUSAL ? min(Nk - 1, query + Nk - Nq) : Nk - 1) - j0 - kb * 32 - (lane >> 5) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((i >> 2) * 8 + (i & 3) > kmax) s[kb][i] = NEG_INF;
+      }
+    }
+
+    float mx = NEG_INF;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = (f32x16){};
-    LDS_AS const char* klane = kt + koff_l;
-    LDS_AS const char* klane_lo = F32 ? ktl + koff_l : nullptr;
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    m_run = fmaxf(m_run, xhalf_max(mx) * c);
+    if (__ballot(m_run > m_ref + TAU)) {
+      const float alpha = (m_run == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_run);
+      lsum *= alpha;
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) {
+      for (int db = 0; db < DB; ++db) o[db] *= alpha;
+      m_ref = m_run;
+    }
+
+    // ---- P = 2^(S c - m_ref) split into bf16 hi + lo; row sums from the fp32 P
+    const float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
+    bf16x8 ph[PS], pl[PS];
+    float part = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const int off = kb * 32 * RS + ds * 32;
-        const bf16x8 kf = lds_b128(klane + off);
+    for (int ps = 0; ps < PS; ++ps) {
+      float x[8];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          s[kb][qb] = mfma(kf, qf[qb][ds], s[kb][qb]);
-          if constexpr (F32) s[kb][qb] = mfma(kf, qlo[qb][ds], s[kb][qb]);
-        }
-        if constexpr (F32) {
-          const bf16x8 kl = lds_b128(klane_lo + off);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma(kl, qf[qb][ds], s[kb][qb]);
-        }
+      for (int e = 0; e < 8; ++e) {
+        x[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[ps >> 1][(ps & 1) * 8 + e], c, -mu));
+        part += x[e];
       }
+      split8(x, ph[ps], pl[ps]);
     }
+    lsum += part;
 
-    // ---- mask: only tiles that cross the diagonal or the end of the keys
-    if (j0 + BC - 1 > kfull_w) {
+    // ---- O^T += V^T P^T (three partial products)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int query = q0w + qb * 32 + (lane & 31);
-          const int kmax = (CAUSAL ? min(Nk - 1, query + Nk - Nq) : Nk - 1) - j0 - kb * 32 - (lane >> 5) * 4;
+      for (int ps = 0; ps < PS; ++ps) {
+        const bf16x8 vh = v_frag<RS>(vt + voff_l, ps, db), vl = v_frag<RS>(vtl + voff_l, ps, db);
+        o[db] = mfma(vh, ph[ps], o[db]);
+        o[db] = mfma(vh, pl[ps], o[db]);
+        o[db] = mfma(vl, ph[ps], o[db]);
+      }
+  }
+
+  if (!live) return;
+  const float lt = xhalf_sum(lsum);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const int query = q0w + (lane & 31);
+  if (query >= Nq) return;
+  const size_t orow = qoff + (size_t)query * D;
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if ((i >> 2) * 8 + (i & 3) > kmax) s[kb][qb][i] = NEG_INF;
-        }
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      f32x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = o[db][i4 * 4 + e] * inv;
+      *(f32x4*)(O + orow + db * 32 + i4 * 8 + (lane >> 5) * 4) = r;
     }
+  if (LSE != nullptr && lane < 32)
+    LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
+}
 
-    // ---- running maximum; rescale O and l only past the threshold
-    bool grow = false;
+// ---------------------------------------------------------------- pipelined bf16 kernel
+// The bf16 path software-pipelines each wave: while the exponentials of
+// key tile j are computed on the VALU, the MFMAs of S^T for tile j+1 are
+// already in flight (the softmax / matrix-product overlap FlashAttention-3
+// obtains with ping-pong warpgroups, "FlashAttention-3 — 闪电注意力-3",
+// section on asynchrony).  K therefore runs one tile ahead of V in LDS:
+// iteration j reads K_{j+1} and V_j and refills the slots of K_j and V_{j-1}
+// with K_{j+2} and V_{j+1}.
+
+// Scores of one wave for one key tile (S^T blocks [kb][qb]).
+template <int D>
+struct Scores {
+  using C = Cfg<D, false>;
+  f32x16 v[C::KB][C::QB];
+};
+
+// S^T = K Q^T for one tile, fully in one go (prologue).
+template <int D>
+__device__ __forceinline__ void scores_full(Scores<D>& s, LDS_AS const char* klane,
+                                            const bf16x8 (&qf)[Cfg<D, false>::QB][Cfg<D, false>::DS]) {
+  using C = Cfg<D, false>;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) s.v[kb][qb] = (f32x16){};
+#pragma unroll
+  for (int ds = 0; ds < C::DS; ++ds)
+#pragma unroll
+    for (int kb = 0; kb < C::KB; ++kb) {
+      const bf16x8 kf = lds_b128(klane + kb * 32 * C::RS + ds * 32);
+#pragma unroll
+      for (int qb = 0; qb < C::QB; ++qb) s.v[kb][qb] = mfma(kf, qf[qb][ds], s.v[kb][qb]);
+    }
+}
+
+// Mask keys past the visible range of each query (tiles that cross the
+// causal diagonal or the end of the keys only).
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int q0w, int Nq, int Nk, int lane) {
+  using C = Cfg<D, false>;
+#pragma unroll
+  for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < C::QB; ++qb) {
+      const int query = q0w + qb * 32 + (lane & 31);
+      const int kmax = (CAUSAL ? min(Nk - 1, query + Nk - Nq) : Nk - 1) - j0 - kb * 32 - (lane >> 5) * 4;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if ((i >> 2) * 8 + (i & 3) > kmax) s.v[kb][qb][i] = NEG_INF;
+    }
+}
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
+void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                        __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c) {
+  using C = Cfg<D, false>;
+  constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RS = C::RS;
+  static_assert(C::QB == 1, "one 32-row query block per wave");
+  constexpr int NMF = DS * KB;   // MFMAs of one S^T tile
+  constexpr int NPV = DB * PS;   // MFMAs of one P V product
+  constexpr int SPS = KB * 16 / NMF;  // exponentials per S^T MFMA
+  static_assert(SPS * NMF == KB * 16, "score / MFMA interleave");
+  constexpr int KPF = 4;         // K fragment reads in flight ahead of the S^T MFMAs
+  constexpr int VPF = 4;         // V fragments in flight ahead of the P V MFMAs
+  static_assert(VPF <= NMF && KPF <= NMF, "prefetch depth");
+  constexpr int SPARE = (C::INS % NW) ? 1024 : 0;  // sink of the padding copy instructions
+  __shared__ __attribute__((aligned(1024))) char smem_[4 * C::TILE + SPARE];
+  LDS_AS char* const smem = (LDS_AS char*)smem_;
+  // LDS: K slots 0, 1, V slots 0, 1, spare block
+  auto kslot = [&](int i) { return smem + i * C::TILE; };
+  auto vslot = [&](int i) { return smem + (2 + i) * C::TILE; };
+  LDS_AS char* const spare = smem + 4 * C::TILE;
+
+  const fa_work_t w = fa_decode(p, blockIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hq = w.hq0 + wave % p.hw;
+  const int q0w = w.qpos0 + (wave / p.hw) * 32;
+  const int Nq = p.Nq, Nk = p.Nk;
+  const int nt = fa_num_kv_tiles(p, w.qpos0, BC);
+
+  const bool live = q0w < Nq;
+  const int qlast_w = min(Nq - 1, q0w + 31);
+  const int klast_w = CAUSAL ? min(Nk - 1, qlast_w + Nk - Nq) : Nk - 1;
+  const int kfull_w = CAUSAL ? min(Nk - 1, q0w + Nk - Nq) : Nk - 1;
+  const int ntw = (live && klast_w >= 0) ? min(nt, klast_w / BC + 1) : 0;  // tiles this wave computes
+
+  const size_t qoff = (size_t)(w.b * p.Hq + hq) * Nq * D;
+  const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
+
+  // resident Q fragments (B operand of S^T = K Q^T): column = query, k = d
+  bf16x8 qf[1][DS];
+  {
+    const int qrow = min(q0w + (lane & 31), Nq - 1);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[0][ds] = *(const bf16x8*)(Q + qoff + (size_t)qrow * D + ds * 16 + (lane >> 5) * 8);
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
+
+  const int koff_l = k_lane_off<RS>(lane);
+  const int voff_l = v_lane_off<RS>(lane);
+  const __bf16* kbase = K + kvoff;
+  const __bf16* vbase = V + kvoff;
+  CopyPlan<D, NW> cp;
+  cp.init(wave, lane);
+
+  // prologue: K_0, V_0, K_1 in LDS; S_0 computed
+  if (nt > 0) {
+    cp.issue(kbase, 0, Nk, kslot(0), spare, wave);
+    cp.issue(vbase, 0, Nk, vslot(0), spare, wave);
+  }
+  if (nt > 1) cp.issue(kbase, BC, Nk, kslot(1), spare, wave);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  Scores<D> sa, sb;
+  if (ntw > 0) scores_full<D>(sa, kslot(0) + koff_l, qf);
+
+  // One key tile: the scores of tile j are in s; the scores of tile j+1 are
+  // produced into sn.  Two score buffers alternate (the loop below is
+  // unrolled by two), so no register copies are needed between tiles.
+  auto step = [&](int j, Scores<D>& s, Scores<D>& sn) {
+    const int j0 = j * BC;
+    // K_{j+1} and V_j (issued one iteration ago) are complete and visible;
+    // every wave is done with K_j and V_{j-1}, whose slots are refilled now
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (j + 2 < nt) cp.issue(kbase, j0 + 2 * BC, Nk, kslot(j & 1), spare, wave);
+    if (j + 1 < nt) cp.issue(vbase, j0 + BC, Nk, vslot((j + 1) & 1), spare, wave);
+    if (j >= ntw) return;  // wave-uniform: nothing visible to this wave
+
+    LDS_AS const char* knext = kslot((j + 1) & 1) + koff_l;
+    LDS_AS const char* vlane = vslot(j & 1) + voff_l;
+    // the first K fragments of S_{j+1} load while the row maxima are formed
+    bf16x8 kbuf[KPF], vbuf[VPF];
+#pragma unroll
+    for (int t = 0; t < KPF; ++t) kbuf[t] = lds_b128(knext + (t % KB) * 32 * RS + (t / KB) * 32);
+
+    if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q0w, Nq, Nk, lane);
+
+    // ---- S_{j+1} = K_{j+1} Q^T interleaved with P_j = 2^(S_j c - m_ref),
+    // taken against the current reference maximum m_ref (fast path).
+    // Chunk t issues MFMA t of S_{j+1}, the LDS read of the K fragment KPF
+    // chunks ahead, and SPS exponentials; sched_barrier fences keep the
+    // chunks in this order.  S_{j+1} is computed unconditionally (on a wave's
+    // last tile the K slot holds stale data and the result is discarded), so
+    // the whole step is one branch-free block.
+    float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
+    bf16x8 pf[PS];
+    float part0 = 0.f, part1 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) sn.v[kb][0] = (f32x16){};
+#pragma unroll
+    for (int t = 0; t < NMF; ++t) {
+      const int ds = t / KB, kb = t % KB;
+      sn.v[kb][0] = mfma(kbuf[t % KPF], qf[0][ds], sn.v[kb][0]);
+      if (t + KPF < NMF) kbuf[t % KPF] = lds_b128(knext + ((t + KPF) % KB) * 32 * RS + ((t + KPF) / KB) * 32);
+#pragma unroll
+      for (int u = 0; u < SPS; ++u) {
+        const int sc = t * SPS + u;  // score index [kb][i]
+        const int skb = sc / 16, si = sc % 16;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s.v[skb][0][si], c, -mu));
+        if (sc & 1) part1 += pv;
+        else part0 += pv;
+        pf[skb * 2 + si / 8][si % 8] = (__bf16)pv;
+      }
+      if (t >= NMF - VPF) {  // first V fragments of the P V product
+        const int tv = t - (NMF - VPF);
+        vbuf[tv] = v_frag<RS>(vlane, tv / DB, tv % DB);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float part = part0 + part1;
+
+    // ---- slow path: if some probability may exceed 2^TAU (a lane's partial
+    // row sum does), or a row has no reference yet, form the row maximum,
+    // rescale O and l when it grew by more than TAU, and redo the
+    // exponentials.  Otherwise every probability is at most 2^TAU and the
+    // reference maximum stands, exactly as the max-first rule would decide.
+    if (__ballot(!(part <= TAU_EXP2) || m_ref == NEG_INF)) {
       float mx = NEG_INF;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = xhalf_max(mx);
-      m_run[qb] = fmaxf(m_run[qb], mx * c);
-      grow |= m_run[qb] > m_ref[qb] + TAU;
-    }
-    if (__ballot(grow)) {
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s.v[kb][0][i]);
+      m_run = fmaxf(m_run, xhalf_max(mx) * c);
+      if (__ballot(m_run > m_ref + TAU)) {
+        const float alpha = (m_run == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_run);
+        lsum *= alpha;
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float alpha = (m_run[qb] == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_ref[qb] - m_run[qb]);
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) o[qb][db] *= alpha;
-        m_ref[qb] = m_run[qb];
+        for (int db = 0; db < DB; ++db) o[db] *= alpha;
+        m_ref = m_run;
       }
-    }
-
-    // ---- P = 2^(S c - m_ref), row sums, bf16 operands of the second product
-    bf16x8 pf[QB][PS];
-    bf16x8 pl[F32 ? QB : 1][F32 ? PS : 1];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mu = (m_ref[qb] == NEG_INF) ? 0.f : m_ref[qb];
-      float part = 0.f;
+      mu = (m_ref == NEG_INF) ? 0.f : m_ref;
+      part = 0.f;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][i], c, -mu));
-          s[kb][qb][i] = pv;
+          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s.v[kb][0][i], c, -mu));
           part += pv;
+          pf[kb * 2 + i / 8][i % 8] = (__bf16)pv;
         }
-      lsum[qb] += part;
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = s[ps >> 1][qb][(ps & 1) * 8 + e];
-        if constexpr (F32) {
-          split8(x, pf[qb][ps], pl[qb][ps]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) pf[qb][ps][e] = (__bf16)x[e];
-        }
-      }
     }
+    lsum += part;
 
-    // ---- O^T += V^T P^T
-    LDS_AS const char* vlane = vt + voff_l;
-    LDS_AS const char* vlane_lo = F32 ? vtl + voff_l : nullptr;
+    // ---- O^T += V_j^T P_j^T: MFMA t uses k-step t/DB and d-block t%DB (the
+    // accumulators rotate), the V fragment read VPF MFMAs ahead
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-#pragma unroll
-      for (int ps = 0; ps < PS; ++ps) {
-        const bf16x8 vf = v_frag<RS>(vlane, ps, db);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          o[qb][db] = mfma(vf, pf[qb][ps], o[qb][db]);
-          if constexpr (F32) o[qb][db] = mfma(vf, pl[qb][ps], o[qb][db]);
-        }
-        if constexpr (F32) {
-          const bf16x8 vl = v_frag<RS>(vlane_lo, ps, db);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) o[qb][db] = mfma(vl, pf[qb][ps], o[qb][db]);
-        }
-      }
+    for (int t = 0; t < NPV; ++t) {
+      const int ps = t / DB, db = t % DB;
+      o[db] = mfma(vbuf[t % VPF], pf[ps], o[db]);
+      if (t + VPF < NPV) vbuf[t % VPF] = v_frag<RS>(vlane, (t + VPF) / DB, (t + VPF) % DB);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  for (int j = 0; j < nt; j += 2) {
+    step(j, sa, sb);
+    if (j + 1 < nt) step(j + 1, sb, sa);
   }
 
   // ---- epilogue: O / l, LSE = ln2 * (m_ref + log2 l)
   if (!live) return;
+  const float lt = xhalf_sum(lsum);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const int query = q0w + (lane & 31);
+  if (query >= Nq) return;
+  const size_t orow = qoff + (size_t)query * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float lt = xhalf_sum(lsum[qb]);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    const int query = q0w + qb * 32 + (lane & 31);
-    if (query >= Nq) continue;
-    const size_t orow = qoff + (size_t)query * D;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = db * 32 + i4 * 8 + (lane >> 5) * 4;
+      bf16x4 r;
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d0 = db * 32 + i4 * 8 + (lane >> 5) * 4;
-        if constexpr (F32) {
-          f32x4 r;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = o[qb][db][i4 * 4 + e] * inv;
-          *(f32x4*)((float*)Op + orow + d0) = r;
-        } else {
-          bf16x4 r;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) r[e] = (__bf16)(o[qb][db][i4 * 4 + e] * inv);
-          *(bf16x4*)((__bf16*)Op + orow + d0) = r;
-        }
-      }
-    if (LSE != nullptr && lane < 32)
-      LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lt > 0.f ? (m_ref[qb] + log2f(lt)) * LN2 : NEG_INF;
-  }
+      for (int e = 0; e < 4; ++e) r[e] = (__bf16)(o[db][i4 * 4 + e] * inv);
+      *(bf16x4*)(O + orow + d0) = r;
+    }
+  if (LSE != nullptr && lane < 32)
+    LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
 }
 
 // ---------------------------------------------------------------- launchers
 // Every variant is instantiated explicitly (implicit instantiation through
 // the launch expression alone does not always emit the host-side stub).
-#define FA_INST(DD, CC, FF, NN)                                                                        \
-  template __global__ void fa_fwd_kernel<DD, CC, FF, NN>(const void* __restrict__, const void* __restrict__, \
-                                                         const void* __restrict__, void* __restrict__,    \
-                                                         float* __restrict__, fa_plan_t, float);
-#define FA_VARIANTS(X)                                                                                  \
-  X(64, false, false, 1) X(64, false, false, 2) X(64, false, false, 4)                                  \
-  X(64, true, false, 1) X(64, true, false, 2) X(64, true, false, 4)                                     \
-  X(128, false, false, 1) X(128, false, false, 2) X(128, false, false, 4)                               \
-  X(128, true, false, 1) X(128, true, false, 2) X(128, true, false, 4)                                  \
-  X(256, false, false, 1) X(256, false, false, 2) X(256, false, false, 4)                               \
-  X(256, true, false, 1) X(256, true, false, 2) X(256, true, false, 4)                                  \
-  X(64, false, true, 4) X(64, true, true, 4) X(128, false, true, 4) X(128, true, true, 4)               \
-  X(256, false, true, 4) X(256, true, true, 4)
-FA_VARIANTS(FA_INST)
+#define FA_INST_F32(DD, CC)                                                                               \
+  template __global__ void fa_fwd_f32_kernel<DD, CC>(const float* __restrict__, const float* __restrict__,       \
+                                                     const float* __restrict__, float* __restrict__,             \
+                                                     float* __restrict__, fa_plan_t, float);
+#define FA_INST_BF16(DD, CC, NN)                                                                              \
+  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN>(const __bf16* __restrict__, const __bf16* __restrict__, \
+                                                          const __bf16* __restrict__, __bf16* __restrict__,       \
+                                                          float* __restrict__, fa_plan_t, float);
+#define FA_F32_VARIANTS(X) X(64, false) X(64, true) X(128, false) X(128, true) X(256, false) X(256, true)
+#define FA_BF16_VARIANTS(X)                                                                                \
+  X(64, false, 1) X(64, false, 2) X(64, false, 4) X(64, true, 1) X(64, true, 2) X(64, true, 4)              \
+  X(128, false, 1) X(128, false, 2) X(128, false, 4) X(128, true, 1) X(128, true, 2) X(128, true, 4)        \
+  X(256, false, 1) X(256, false, 2) X(256, false, 4) X(256, true, 1) X(256, true, 2) X(256, true, 4)
+FA_F32_VARIANTS(FA_INST_F32)
+FA_BF16_VARIANTS(FA_INST_BF16)
 
-int queries_per_wave(int d, int f32) {
-  if (f32) return 32;
-  return d == 64 ? 64 : 32;
-}
+int queries_per_wave(int, int) { return 32; }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
                       float c, int f32, hipStream_t stream) {
-#define FA_CASE(DD, CC, FF, NN)                                                                      \
-  if (d == DD && (p.causal != 0) == CC && (f32 != 0) == FF && p.nw == NN) {                          \
-    hipLaunchKernelGGL((fa_fwd_kernel<DD, CC, FF, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream, q, k, v, \
-                       o, lse, p, c);                                                                \
-    return hipGetLastError();                                                                        \
+#define FA_CASE_F32(DD, CC)                                                                               \
+  if (f32 && d == DD && (p.causal != 0) == CC) {                                                        \
+    hipLaunchKernelGGL((fa_fwd_f32_kernel<DD, CC>), dim3((unsigned)p.nwg), dim3(256), 0, stream, (const float*)q, \
+                       (const float*)k, (const float*)v, (float*)o, lse, p, c);                        \
+    return hipGetLastError();                                                                           \
   }
-  FA_VARIANTS(FA_CASE)
-#undef FA_CASE
+#define FA_CASE_BF16(DD, CC, NN)                                                                          \
+  if (!f32 && d == DD && (p.causal != 0) == CC && p.nw == NN) {                                         \
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream,    \
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c);   \
+    return hipGetLastError();                                                                           \
+  }
+  FA_F32_VARIANTS(FA_CASE_F32)
+  FA_BF16_VARIANTS(FA_CASE_BF16)
+#undef FA_CASE_F32
+#undef FA_CASE_BF16
   return hipErrorInvalidValue;
 }
 
