@@ -42,8 +42,9 @@ fa_status forward(const void* q, const void* k, const void* v, void* o, float* l
   if (st != FA_OK) return st;
   const int qpw = fa::queries_per_wave(d, f32);
   // the fp32 path is instantiated for 4-wave workgroups only
+  // bf16: up to 4 waves per workgroup (two workgroups share a CU at d <= 128)
   const fa_plan_t p = f32 ? fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4)
-                          : fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS);
+                          : fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS, 4);
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
   const float c = (float)((double)scale * LOG2E);
   hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, (hipStream_t)stream);

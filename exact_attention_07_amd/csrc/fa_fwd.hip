@@ -96,6 +96,14 @@ constexpr int SG_VALU = 0x002;
 constexpr int SG_MFMA = 0x008;
 constexpr int SG_DS_READ = 0x100;
 
+// s_waitcnt vmcnt(N): wait until at most N vector memory operations of this
+// wave are outstanding (they complete in issue order for loads into LDS)
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -165,20 +173,32 @@ struct CopyPlan {
       goff[i] = (ins < C::INS && pp < C::CPR) ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
     }
   }
-  // Copy BC rows starting at key j0 of a [Nk][D] bf16 matrix; rows >= Nk
-  // fall outside the buffer range and read as zero.  Every wave issues MI
-  // instructions; those past the tile (when NW does not divide INS) read
-  // nothing and write zeros into the 1 KB block `spare`.
+  // Buffer resource over rows [j0, j0 + rows) of a [Nk][D] bf16 matrix;
+  // offsets past it read as zero (rows <= 0: the whole copy reads zeros).
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const __bf16* base, int j0, int rows) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j0 * D), (short)0, rows > 0 ? rows * (D * 2) : 0,
+                                             0x00020000);
+  }
+  // Copy instruction i of this wave.  Instructions past the tile (when NW
+  // does not divide INS) read nothing and write zeros into the 1 KB block
+  // `spare`.
+  __device__ __forceinline__ void issue_one(const __amdgpu_buffer_rsrc_t& rs, LDS_AS char* tile, LDS_AS char* spare,
+                                            int wave, int i) const {
+    const int ins = i * NW + wave;
+    LDS_AS char* dst = (C::INS % NW == 0 || ins < C::INS) ? tile + ins * 1024 : spare;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], 0, 0, 0);
+  }
+  // Copy BC rows starting at key j0 (rows >= Nk read as zero).
   __device__ __forceinline__ void issue(const __bf16* base, int j0, int Nk, LDS_AS char* tile, LDS_AS char* spare,
                                         int wave) const {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j0 * D), (short)0, (Nk - j0) * (D * 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(base, j0, Nk - j0);
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int ins = i * NW + wave;
-      LDS_AS char* dst = (C::INS % NW == 0 || ins < C::INS) ? tile + ins * 1024 : spare;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], 0, 0, 0);
-    }
+    for (int i = 0; i < MI; ++i) issue_one(rs, tile, spare, wave, i);
+  }
+  __device__ __forceinline__ void issue_all(const __amdgpu_buffer_rsrc_t& rs, LDS_AS char* tile, LDS_AS char* spare,
+                                            int wave) const {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) issue_one(rs, tile, spare, wave, i);
   }
 };
 
@@ -409,7 +429,8 @@ __device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int q0w, int N
     }
 }
 
-template <int D, bool CAUSAL, int NW>
+// NST: slots per K and V ring in LDS; copies run NST-1 tiles ahead.
+template <int D, bool CAUSAL, int NW, int NST>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                         __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c) {
@@ -423,13 +444,14 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   constexpr int KPF = 4;         // K fragment reads in flight ahead of the S^T MFMAs
   constexpr int VPF = 4;         // V fragments in flight ahead of the P V MFMAs
   static_assert(VPF <= NMF && KPF <= NMF, "prefetch depth");
-  constexpr int SPARE = (C::INS % NW) ? 1024 : 0;  // sink of the padding copy instructions
-  __shared__ __attribute__((aligned(1024))) char smem_[4 * C::TILE + SPARE];
+  constexpr int PF = NST - 1;     // copy distance in tiles
+  constexpr int MI = CopyPlan<D, NW>::MI;
+  __shared__ __attribute__((aligned(1024))) char smem_[2 * NST * C::TILE + 1024];
   LDS_AS char* const smem = (LDS_AS char*)smem_;
-  // LDS: K slots 0, 1, V slots 0, 1, spare block
-  auto kslot = [&](int i) { return smem + i * C::TILE; };
-  auto vslot = [&](int i) { return smem + (2 + i) * C::TILE; };
-  LDS_AS char* const spare = smem + 4 * C::TILE;
+  // LDS: K slots 0..NST-1, V slots 0..NST-1, spare block
+  auto kslot = [&](int i) { return smem + (i % NST) * C::TILE; };
+  auto vslot = [&](int i) { return smem + (NST + i % NST) * C::TILE; };
+  LDS_AS char* const spare = smem + 2 * NST * C::TILE;
 
   const fa_work_t w = fa_decode(p, blockIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -467,32 +489,47 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   CopyPlan<D, NW> cp;
   cp.init(wave, lane);
 
-  // prologue: K_0, V_0, K_1 in LDS; S_0 computed
-  if (nt > 0) {
-    cp.issue(kbase, 0, Nk, kslot(0), spare, wave);
-    cp.issue(vbase, 0, Nk, vslot(0), spare, wave);
+  // Copy of K_t / V_t into its ring slot.  Every copy is issued, also past
+  // the workgroup's last tile (then with an empty range: it reads nothing
+  // and writes zeros into a slot whose tile is no longer used), so each wave
+  // has a fixed number of copies in flight and vmcnt can count them.
+  auto copy_k = [&](int t) {
+    cp.issue_all(cp.rsrc(kbase, t * BC, t < nt ? Nk - t * BC : 0), kslot(t), spare, wave);
+  };
+  auto copy_v = [&](int t) {
+    cp.issue_all(cp.rsrc(vbase, t * BC, t < nt ? Nk - t * BC : 0), vslot(t), spare, wave);
+  };
+  // prologue: K_0, V_0, K_1 complete (S_0 computed); K_2..K_PF, V_1..V_{PF-1} in flight
+  copy_k(0);
+  copy_v(0);
+  copy_k(1);
+#pragma unroll
+  for (int t = 1; t < PF; ++t) {
+    copy_k(t + 1);
+    copy_v(t);
   }
-  if (nt > 1) cp.issue(kbase, BC, Nk, kslot(1), spare, wave);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vm_wait<(PF - 1) * 2 * MI>();
   __syncthreads();
   Scores<D> sa, sb;
   if (ntw > 0) scores_full<D>(sa, kslot(0) + koff_l, qf);
+  (void)vslot;
 
   // One key tile: the scores of tile j are in s; the scores of tile j+1 are
   // produced into sn.  Two score buffers alternate (the loop below is
   // unrolled by two), so no register copies are needed between tiles.
   auto step = [&](int j, Scores<D>& s, Scores<D>& sn) {
     const int j0 = j * BC;
-    // K_{j+1} and V_j (issued one iteration ago) are complete and visible;
+    // K_{j+1} and V_j (issued PF iterations ago) are complete and visible
+    // (the copies of the last PF-1 iterations may still be in flight);
     // every wave is done with K_j and V_{j-1}, whose slots are refilled now
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vm_wait<(PF - 1) * 2 * MI>();
     __syncthreads();
-    if (j + 2 < nt) cp.issue(kbase, j0 + 2 * BC, Nk, kslot(j & 1), spare, wave);
-    if (j + 1 < nt) cp.issue(vbase, j0 + BC, Nk, vslot((j + 1) & 1), spare, wave);
+    copy_k(j + 1 + PF);
+    copy_v(j + PF);
     if (j >= ntw) return;  // wave-uniform: nothing visible to this wave
 
-    LDS_AS const char* knext = kslot((j + 1) & 1) + koff_l;
-    LDS_AS const char* vlane = vslot(j & 1) + voff_l;
+    LDS_AS const char* knext = kslot(j + 1) + koff_l;
+    LDS_AS const char* vlane = vslot(j) + voff_l;
     // the first K fragments of S_{j+1} load while the row maxima are formed
     bf16x8 kbuf[KPF], vbuf[VPF];
 #pragma unroll
@@ -609,15 +646,18 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   template __global__ void fa_fwd_f32_kernel<DD, CC>(const float* __restrict__, const float* __restrict__,       \
                                                      const float* __restrict__, float* __restrict__,             \
                                                      float* __restrict__, fa_plan_t, float);
-#define FA_INST_BF16(DD, CC, NN)                                                                              \
-  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN>(const __bf16* __restrict__, const __bf16* __restrict__, \
-                                                          const __bf16* __restrict__, __bf16* __restrict__,       \
-                                                          float* __restrict__, fa_plan_t, float);
+#define FA_INST_BF16(DD, CC, NN, SS)                                                                              \
+  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN, SS>(const __bf16* __restrict__, const __bf16* __restrict__, \
+                                                              const __bf16* __restrict__, __bf16* __restrict__,       \
+                                                              float* __restrict__, fa_plan_t, float);
 #define FA_F32_VARIANTS(X) X(64, false) X(64, true) X(128, false) X(128, true) X(256, false) X(256, true)
+// (head dim, causal, waves per workgroup, ring slots)
 #define FA_BF16_VARIANTS(X)                                                                                \
-  X(64, false, 1) X(64, false, 2) X(64, false, 4) X(64, true, 1) X(64, true, 2) X(64, true, 4)              \
-  X(128, false, 1) X(128, false, 2) X(128, false, 4) X(128, true, 1) X(128, true, 2) X(128, true, 4)        \
-  X(256, false, 1) X(256, false, 2) X(256, false, 4) X(256, true, 1) X(256, true, 2) X(256, true, 4)
+  X(64, false, 1, 2) X(64, false, 2, 2) X(64, false, 4, 2) X(64, true, 1, 2) X(64, true, 2, 2)              \
+  X(64, true, 4, 2) X(128, false, 1, 2) X(128, false, 2, 2) X(128, false, 4, 2) X(128, false, 8, 4)         \
+  X(128, true, 1, 2) X(128, true, 2, 2) X(128, true, 4, 2) X(128, true, 8, 4)                               \
+  X(256, false, 1, 2) X(256, false, 2, 2) X(256, false, 4, 2) X(256, true, 1, 2) X(256, true, 2, 2)         \
+  X(256, true, 4, 2)
 FA_F32_VARIANTS(FA_INST_F32)
 FA_BF16_VARIANTS(FA_INST_BF16)
 
@@ -631,9 +671,9 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                        (const float*)k, (const float*)v, (float*)o, lse, p, c);                        \
     return hipGetLastError();                                                                           \
   }
-#define FA_CASE_BF16(DD, CC, NN)                                                                          \
+#define FA_CASE_BF16(DD, CC, NN, SS)                                                                      \
   if (!f32 && d == DD && (p.causal != 0) == CC && p.nw == NN) {                                         \
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream,    \
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN, SS>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream, \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c);   \
     return hipGetLastError();                                                                           \
   }

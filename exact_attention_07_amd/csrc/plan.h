@@ -65,11 +65,12 @@ FA_HD inline fa_plan_t fa_make_plan(int B, int Hq, int Hkv, int Nq, int Nk, int 
   return p;
 }
 
-// Waves per workgroup: the largest of 4, 2, 1 that still leaves at least
-// `min_wg` workgroups (enough to fill the chip several times); 1 otherwise.
+// Waves per workgroup: the largest power of two <= max_nw that still leaves
+// at least `min_wg` workgroups (enough to fill the chip several times); 1
+// otherwise.
 FA_HD inline fa_plan_t fa_choose_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int qpw,
-                                      long long min_wg) {
-  for (int nw = 4; nw > 1; nw >>= 1) {
+                                      long long min_wg, int max_nw) {
+  for (int nw = max_nw; nw > 1; nw >>= 1) {
     fa_plan_t p = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, nw);
     if (p.nwg >= min_wg) return p;
   }

@@ -53,7 +53,7 @@ static void check_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int q
 
 int main() {
   for (int causal = 0; causal < 2; ++causal)
-    for (int nw : {1, 2, 4})
+    for (int nw : {1, 2, 4, 8})
       for (int qpw : {32, 64}) {
         check_plan(2, 32, 8, 8192, 8192, causal, qpw, nw);
         check_plan(8, 12, 12, 1024, 1024, causal, qpw, nw);
@@ -78,10 +78,10 @@ int main() {
   // the first ids of an XCD get the heaviest (last) query block
   CHECK(fa_decode(p, 0).qpos0 == 8192 - 64 && fa_decode(p, 8).qpos0 == 8192 - 128);
   // plan choice keeps >= 1024 workgroups when possible
-  fa_plan_t c2 = fa_choose_plan(8, 12, 12, 1024, 1024, 1, 64, 1024);
-  CHECK(c2.nw == 1 && c2.nwg == 8 * 12 * 16);
-  fa_plan_t c3 = fa_choose_plan(2, 32, 8, 8192, 8192, 1, 64, 1024);
-  CHECK(c3.nw == 4 && c3.hw == 4);
+  fa_plan_t c2 = fa_choose_plan(8, 12, 12, 1024, 1024, 1, 32, 1024, 8);
+  CHECK(c2.nw == 2 && c2.nwg == 8 * 12 * 16);
+  fa_plan_t c3 = fa_choose_plan(2, 32, 8, 8192, 8192, 1, 32, 1024, 8);
+  CHECK(c3.nw == 8 && c3.hw == 4 && c3.pos == 64 && c3.nwg == 2048);
   std::printf("plan checks passed\n");
   return 0;
 }
