@@ -173,32 +173,25 @@ struct CopyPlan {
       goff[i] = (ins < C::INS && pp < C::CPR) ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
     }
   }
-  // Buffer resource over rows [j0, j0 + rows) of a [Nk][D] bf16 matrix;
-  // offsets past it read as zero (rows <= 0: the whole copy reads zeros).
-  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const __bf16* base, int j0, int rows) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (size_t)j0 * D), (short)0, rows > 0 ? rows * (D * 2) : 0,
-                                             0x00020000);
+  // Buffer resource over a whole [Nk][D] bf16 matrix; the hardware range
+  // check covers voffset + soffset, so rows >= Nk read as zero.
+  __device__ __forceinline__ static __amdgpu_buffer_rsrc_t rsrc(const __bf16* base, int Nk) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, Nk * (D * 2), 0x00020000);
   }
-  // Copy instruction i of this wave.  Instructions past the tile (when NW
-  // does not divide INS) read nothing and write zeros into the 1 KB block
-  // `spare`.
-  __device__ __forceinline__ void issue_one(const __amdgpu_buffer_rsrc_t& rs, LDS_AS char* tile, LDS_AS char* spare,
-                                            int wave, int i) const {
+  // Copy instruction i of this wave for the tile at byte offset soff (soff at
+  // or past the range: the copy reads nothing and writes zeros).
+  // Instructions past the tile (when NW does not divide INS) write into the
+  // 1 KB block `spare`.
+  __device__ __forceinline__ void issue_one(const __amdgpu_buffer_rsrc_t& rs, int soff, LDS_AS char* tile,
+                                            LDS_AS char* spare, int wave, int i) const {
     const int ins = i * NW + wave;
     LDS_AS char* dst = (C::INS % NW == 0 || ins < C::INS) ? tile + ins * 1024 : spare;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], soff, 0, 0);
   }
-  // Copy BC rows starting at key j0 (rows >= Nk read as zero).
-  __device__ __forceinline__ void issue(const __bf16* base, int j0, int Nk, LDS_AS char* tile, LDS_AS char* spare,
-                                        int wave) const {
-    const __amdgpu_buffer_rsrc_t rs = rsrc(base, j0, Nk - j0);
+  __device__ __forceinline__ void issue_all(const __amdgpu_buffer_rsrc_t& rs, int soff, LDS_AS char* tile,
+                                            LDS_AS char* spare, int wave) const {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) issue_one(rs, tile, spare, wave, i);
-  }
-  __device__ __forceinline__ void issue_all(const __amdgpu_buffer_rsrc_t& rs, LDS_AS char* tile, LDS_AS char* spare,
-                                            int wave) const {
-#pragma unroll
-    for (int i = 0; i < MI; ++i) issue_one(rs, tile, spare, wave, i);
+    for (int i = 0; i < MI; ++i) issue_one(rs, soff, tile, spare, wave, i);
   }
 };
 
@@ -429,8 +422,11 @@ __device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int q0w, int N
     }
 }
 
-// NST: slots per K and V ring in LDS; copies run NST-1 tiles ahead.
-template <int D, bool CAUSAL, int NW, int NST>
+// NST: slots per K and V ring in LDS.  PP (ping-pong, 8 waves): the upper
+// half of the workgroup runs its loop half an iteration behind, so on each
+// SIMD one wave is in its exponential-heavy phase while the other is in its
+// MFMA-heavy P V phase.
+template <int D, bool CAUSAL, int NW, int NST, bool PP>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                         __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c) {
@@ -441,16 +437,24 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   constexpr int NPV = DB * PS;   // MFMAs of one P V product
   constexpr int SPS = KB * 16 / NMF;  // exponentials per S^T MFMA
   static_assert(SPS * NMF == KB * 16, "score / MFMA interleave");
-  constexpr int KPF = 4;         // K fragment reads in flight ahead of the S^T MFMAs
-  constexpr int VPF = 4;         // V fragments in flight ahead of the P V MFMAs
+  constexpr int KPF = PP ? 3 : 4;  // K fragment reads in flight ahead of the S^T MFMAs
+  constexpr int VPF = 3;         // V fragments in flight ahead of the P V MFMAs
   static_assert(VPF <= NMF && KPF <= NMF, "prefetch depth");
-  constexpr int PF = NST - 1;     // copy distance in tiles
+  // Iteration j copies K_{j+KD} and V_{j+VD}.  It reads K_{j+1} and V_j (and,
+  // in the late half of a ping-pong workgroup, V_{j-1}); a copy overwrites
+  // the slot of a tile read two barriers ago at the latest.  The copies of
+  // the last WIF iterations may still be in flight when an iteration starts.
+  static_assert(!PP || (NW == 8 && NST == 4), "ping-pong layout");
+  static_assert(NST == 2 || NST == 4, "ring size");
+  constexpr int KD = PP ? NST - 1 : NST;
+  constexpr int VD = PP ? NST - 2 : NST - 1;
+  constexpr int WIF = (KD - 1 < VD ? KD - 1 : VD) - 1;
   constexpr int MI = CopyPlan<D, NW>::MI;
   __shared__ __attribute__((aligned(1024))) char smem_[2 * NST * C::TILE + 1024];
   LDS_AS char* const smem = (LDS_AS char*)smem_;
   // LDS: K slots 0..NST-1, V slots 0..NST-1, spare block
-  auto kslot = [&](int i) { return smem + (i % NST) * C::TILE; };
-  auto vslot = [&](int i) { return smem + (NST + i % NST) * C::TILE; };
+  auto kslot = [&](int i) { return smem + (i & (NST - 1)) * C::TILE; };
+  auto vslot = [&](int i) { return smem + (NST + (i & (NST - 1))) * C::TILE; };
   LDS_AS char* const spare = smem + 2 * NST * C::TILE;
 
   const fa_work_t w = fa_decode(p, blockIdx.x);
@@ -490,62 +494,66 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   cp.init(wave, lane);
 
   // Copy of K_t / V_t into its ring slot.  Every copy is issued, also past
-  // the workgroup's last tile (then with an empty range: it reads nothing
-  // and writes zeros into a slot whose tile is no longer used), so each wave
-  // has a fixed number of copies in flight and vmcnt can count them.
+  // the workgroup's last tile (then out of range: it reads nothing and
+  // writes zeros into a slot whose tile is no longer used), so each wave has
+  // a fixed number of copies in flight and vmcnt can count them.
+  const __amdgpu_buffer_rsrc_t kres = cp.rsrc(kbase, Nk), vres = cp.rsrc(vbase, Nk);
+  const int kv_bytes = Nk * (D * 2);
+  auto tile_off = [&](int t) { return t < nt ? t * (BC * D * 2) : kv_bytes; };
+  // (the slot offset passes through an opaque scalar move so that the
+  // destinations are formed at each copy instead of being kept in SGPRs)
+  auto opaque = [](int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+  };
   auto copy_k = [&](int t) {
-    cp.issue_all(cp.rsrc(kbase, t * BC, t < nt ? Nk - t * BC : 0), kslot(t), spare, wave);
+    cp.issue_all(kres, tile_off(t), smem + opaque((t & (NST - 1)) * C::TILE), spare, wave);
   };
   auto copy_v = [&](int t) {
-    cp.issue_all(cp.rsrc(vbase, t * BC, t < nt ? Nk - t * BC : 0), vslot(t), spare, wave);
+    cp.issue_all(vres, tile_off(t), smem + opaque((NST + (t & (NST - 1))) * C::TILE), spare, wave);
   };
-  // prologue: K_0, V_0, K_1 complete (S_0 computed); K_2..K_PF, V_1..V_{PF-1} in flight
-  copy_k(0);
-  copy_v(0);
-  copy_k(1);
+  // prologue: the copies iterations -KD..-1 would have made; then S_0
 #pragma unroll
-  for (int t = 1; t < PF; ++t) {
-    copy_k(t + 1);
-    copy_v(t);
+  for (int i = -(KD > VD ? KD : VD); i < 0; ++i) {
+    if (i + KD >= 0) copy_k(i + KD);
+    if (i + VD >= 0) copy_v(i + VD);
   }
-  vm_wait<(PF - 1) * 2 * MI>();
+  vm_wait<WIF * 2 * MI>();
   __syncthreads();
   Scores<D> sa, sb;
   if (ntw > 0) scores_full<D>(sa, kslot(0) + koff_l, qf);
-  (void)vslot;
 
-  // One key tile: the scores of tile j are in s; the scores of tile j+1 are
-  // produced into sn.  Two score buffers alternate (the loop below is
-  // unrolled by two), so no register copies are needed between tiles.
-  auto step = [&](int j, Scores<D>& s, Scores<D>& sn) {
-    const int j0 = j * BC;
-    // K_{j+1} and V_j (issued PF iterations ago) are complete and visible
-    // (the copies of the last PF-1 iterations may still be in flight);
-    // every wave is done with K_j and V_{j-1}, whose slots are refilled now
-    vm_wait<(PF - 1) * 2 * MI>();
+  // top of iteration j: wait for this wave's old copies, make every wave's
+  // copies visible, refill the slots read two barriers ago
+  auto top = [&](int j) {
+    vm_wait<WIF * 2 * MI>();
     __syncthreads();
-    copy_k(j + 1 + PF);
-    copy_v(j + PF);
-    if (j >= ntw) return;  // wave-uniform: nothing visible to this wave
+    copy_k(j + KD);
+    copy_v(j + VD);
+  };
 
+  // Softmax phase of tile j: the scores of tile j are in s; the scores of
+  // tile j+1 are produced into sn (K_{j+1} is in LDS), interleaved with the
+  // exponentials P_j = 2^(S_j c - m_ref) into pf.
+  auto softmax_phase = [&](int j, Scores<D>& s, Scores<D>& sn, bf16x8 (&pf)[PS], bf16x8 (&vbuf)[VPF]) {
+    const int j0 = j * BC;
     LDS_AS const char* knext = kslot(j + 1) + koff_l;
     LDS_AS const char* vlane = vslot(j) + voff_l;
-    // the first K fragments of S_{j+1} load while the row maxima are formed
-    bf16x8 kbuf[KPF], vbuf[VPF];
+    // the first K fragments of S_{j+1} load while the mask is applied
+    bf16x8 kbuf[KPF];
 #pragma unroll
     for (int t = 0; t < KPF; ++t) kbuf[t] = lds_b128(knext + (t % KB) * 32 * RS + (t / KB) * 32);
 
     if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q0w, Nq, Nk, lane);
 
-    // ---- S_{j+1} = K_{j+1} Q^T interleaved with P_j = 2^(S_j c - m_ref),
-    // taken against the current reference maximum m_ref (fast path).
     // Chunk t issues MFMA t of S_{j+1}, the LDS read of the K fragment KPF
-    // chunks ahead, and SPS exponentials; sched_barrier fences keep the
-    // chunks in this order.  S_{j+1} is computed unconditionally (on a wave's
-    // last tile the K slot holds stale data and the result is discarded), so
-    // the whole step is one branch-free block.
+    // chunks ahead, and SPS exponentials taken against the current reference
+    // maximum m_ref (fast path); sched_barrier fences keep the chunks in
+    // this order.  S_{j+1} is computed unconditionally (on a wave's last tile
+    // the K slot holds stale data and the result is discarded), so the whole
+    // phase is one branch-free block.  The last chunks also start the V
+    // fragment reads of P V.
     float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-    bf16x8 pf[PS];
     float part0 = 0.f, part1 = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sn.v[kb][0] = (f32x16){};
@@ -563,7 +571,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         else part0 += pv;
         pf[skb * 2 + si / 8][si % 8] = (__bf16)pv;
       }
-      if (t >= NMF - VPF) {  // first V fragments of the P V product
+      if (!PP && t >= NMF - VPF) {
         const int tv = t - (NMF - VPF);
         vbuf[tv] = v_frag<RS>(vlane, tv / DB, tv % DB);
       }
@@ -571,8 +579,8 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     }
     float part = part0 + part1;
 
-    // ---- slow path: if some probability may exceed 2^TAU (a lane's partial
-    // row sum does), or a row has no reference yet, form the row maximum,
+    // slow path: if some probability may exceed 2^TAU (a lane's partial row
+    // sum does), or a row has no reference yet, form the row maximum,
     // rescale O and l when it grew by more than TAU, and redo the
     // exponentials.  Otherwise every probability is at most 2^TAU and the
     // reference maximum stands, exactly as the max-first rule would decide.
@@ -602,9 +610,17 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         }
     }
     lsum += part;
+  };
 
-    // ---- O^T += V_j^T P_j^T: MFMA t uses k-step t/DB and d-block t%DB (the
-    // accumulators rotate), the V fragment read VPF MFMAs ahead
+  // P V phase of tile j: O^T += V_j^T P_j^T.  MFMA t uses k-step t/DB and
+  // d-block t%DB (the accumulators rotate); the V fragment is read VPF MFMAs
+  // ahead (the first VPF are already in vbuf unless `fresh`).
+  auto pv_phase = [&](int j, const bf16x8 (&pf)[PS], bf16x8 (&vbuf)[VPF], bool fresh) {
+    LDS_AS const char* vlane = vslot(j) + voff_l;
+    if (fresh) {
+#pragma unroll
+      for (int t = 0; t < VPF; ++t) vbuf[t] = v_frag<RS>(vlane, t / DB, t % DB);
+    }
 #pragma unroll
     for (int t = 0; t < NPV; ++t) {
       const int ps = t / DB, db = t % DB;
@@ -613,9 +629,40 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int j = 0; j < nt; j += 2) {
-    step(j, sa, sb);
-    if (j + 1 < nt) step(j + 1, sb, sa);
+
+  const bool late = PP && wave >= NW / 2;  // wave-uniform
+  if (!late) {
+    // two score buffers alternate (unrolled by two): no copies between tiles
+    for (int j = 0; j < nt; j += 2) {
+      top(j);
+      if (j < ntw) {
+        bf16x8 pf[PS], vbuf[VPF];
+        softmax_phase(j, sa, sb, pf, vbuf);
+        pv_phase(j, pf, vbuf, PP);
+      }
+      if (j + 1 < nt) {
+        top(j + 1);
+        if (j + 1 < ntw) {
+          bf16x8 pf[PS], vbuf[VPF];
+          softmax_phase(j + 1, sb, sa, pf, vbuf);
+          pv_phase(j + 1, pf, vbuf, PP);
+        }
+      }
+    }
+  } else {
+    // late half: P V of the previous tile first, then the softmax phase
+    bf16x8 pf[PS], vbuf[VPF];
+    for (int j = 0; j < nt; j += 2) {
+      top(j);
+      if (j >= 1 && j - 1 < ntw) pv_phase(j - 1, pf, vbuf, true);
+      if (j < ntw) softmax_phase(j, sa, sb, pf, vbuf);
+      if (j + 1 < nt) {
+        top(j + 1);
+        if (j < ntw) pv_phase(j, pf, vbuf, true);
+        if (j + 1 < ntw) softmax_phase(j + 1, sb, sa, pf, vbuf);
+      }
+    }
+    if (nt >= 1 && nt - 1 < ntw) pv_phase(nt - 1, pf, vbuf, true);
   }
 
   // ---- epilogue: O / l, LSE = ln2 * (m_ref + log2 l)
@@ -646,18 +693,19 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   template __global__ void fa_fwd_f32_kernel<DD, CC>(const float* __restrict__, const float* __restrict__,       \
                                                      const float* __restrict__, float* __restrict__,             \
                                                      float* __restrict__, fa_plan_t, float);
-#define FA_INST_BF16(DD, CC, NN, SS)                                                                              \
-  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN, SS>(const __bf16* __restrict__, const __bf16* __restrict__, \
-                                                              const __bf16* __restrict__, __bf16* __restrict__,       \
-                                                              float* __restrict__, fa_plan_t, float);
+#define FA_INST_BF16(DD, CC, NN, SS, PP)                                                                    \
+  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN, SS, PP>(                                           \
+      const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, __bf16* __restrict__, \
+      float* __restrict__, fa_plan_t, float);
 #define FA_F32_VARIANTS(X) X(64, false) X(64, true) X(128, false) X(128, true) X(256, false) X(256, true)
-// (head dim, causal, waves per workgroup, ring slots)
+// (head dim, causal, waves per workgroup, ring slots, ping-pong)
 #define FA_BF16_VARIANTS(X)                                                                                \
-  X(64, false, 1, 2) X(64, false, 2, 2) X(64, false, 4, 2) X(64, true, 1, 2) X(64, true, 2, 2)              \
-  X(64, true, 4, 2) X(128, false, 1, 2) X(128, false, 2, 2) X(128, false, 4, 2) X(128, false, 8, 4)         \
-  X(128, true, 1, 2) X(128, true, 2, 2) X(128, true, 4, 2) X(128, true, 8, 4)                               \
-  X(256, false, 1, 2) X(256, false, 2, 2) X(256, false, 4, 2) X(256, true, 1, 2) X(256, true, 2, 2)         \
-  X(256, true, 4, 2)
+  X(64, false, 1, 2, false) X(64, false, 2, 2, false) X(64, false, 4, 2, false)                             \
+  X(64, true, 1, 2, false) X(64, true, 2, 2, false) X(64, true, 4, 2, false)                                \
+  X(128, false, 1, 2, false) X(128, false, 2, 2, false) X(128, false, 4, 2, false) X(128, false, 8, 4, true) \
+  X(128, true, 1, 2, false) X(128, true, 2, 2, false) X(128, true, 4, 2, false) X(128, true, 8, 4, true)    \
+  X(256, false, 1, 2, false) X(256, false, 2, 2, false) X(256, false, 4, 2, false)                          \
+  X(256, true, 1, 2, false) X(256, true, 2, 2, false) X(256, true, 4, 2, false)
 FA_F32_VARIANTS(FA_INST_F32)
 FA_BF16_VARIANTS(FA_INST_BF16)
 
@@ -671,9 +719,9 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                        (const float*)k, (const float*)v, (float*)o, lse, p, c);                        \
     return hipGetLastError();                                                                           \
   }
-#define FA_CASE_BF16(DD, CC, NN, SS)                                                                      \
+#define FA_CASE_BF16(DD, CC, NN, SS, PP)                                                                  \
   if (!f32 && d == DD && (p.causal != 0) == CC && p.nw == NN) {                                         \
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN, SS>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream, \
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN, SS, PP>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream, \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c);   \
     return hipGetLastError();                                                                           \
   }
