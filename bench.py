@@ -2,14 +2,18 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 3]
 
-A step is one fa_fwd call over one batch of synthetic input of the chosen
-standing workload (default: the causal GQA long-context workload B=2, Hq=32,
-Hkv=8, N=8192, d=128, bf16).  Inputs are resident in HBM before timing
-starts; K steps are timed back to back with HIP events on the stream the
-kernel runs on.  Prints one JSON line on stdout (diagnostics go to stderr):
+A step is one pass of the attention over one batch of synthetic input of the
+chosen standing workload (default: the causal GQA long-context workload B=2,
+Hq=32, Hkv=8, N=8192, d=128, bf16): one fa_fwd (or fa_fwd_f32) call, or for
+the fp8 workload (config 5) fa_fp8_prepare (Hadamard rotation of Q and K,
+per-tensor scales, e4m3 codes) followed by fa_fwd_fp8.  Inputs are resident
+in HBM before timing starts; K steps are timed back to back with HIP events
+on the stream the kernels run on.  Prints one JSON line on stdout
+(diagnostics go to stderr):
 
-  value     attention forward TFLOP/s = 4*B*Hq*Nq*Nk*d (halved when causal) / time
-  roofline  the kernel against the MI355X dense MFMA peak for its dtype, and
+  value     attention forward TFLOP/s = 4*B*Hq*Nq*Nk*d (halved when causal) / step time
+  roofline  the attention kernel (its own launch time, from events around
+            each launch) against the MI355X dense MFMA peak for its dtype, and
             the HBM traffic measured by rocprofv3 counters for the same kernel
             source (null when the source changed since the counters were taken)
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
@@ -33,15 +37,17 @@ METRIC = "attention fwd TFLOP/s + % of MFMA peak (bf16, causal GQA, N=8K, d=128)
 # MI355X published dense peaks (no sparsity), TFLOP/s
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "fp8": 5000.0}
 KERNEL_SOURCES = ["exact_attention_07_amd/csrc/fa_fwd.hip"]
+KERNEL_NAME = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel"}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash() -> str:
+def source_hash(cfg: int = 3) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    extra = ["exact_attention_07_amd/csrc/fa_fp8_prepare.hip"] if cfg == 5 else []
+    for p in KERNEL_SOURCES + extra:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -58,7 +64,7 @@ def load_traffic(cfg: int):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != source_hash():
+    if fields.get("kernel_source_sha256") != source_hash(cfg):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -125,30 +131,61 @@ def main():
             return torch.from_numpy(a).to(dev)
         return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    if w.dtype == "fp8":
-        raise SystemExit("the fp8 workload is not benchmarked by this harness yet")
     q, k, v = (dev_tensor(x[t]) for t in "qkv")
-    o = torch.empty_like(q)
+    o = torch.empty(q.shape, dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    fwd = api.fa_fwd if w.dtype == "bf16" else api.fa_fwd_f32
     stream = torch.cuda.current_stream()
+    if w.dtype == "fp8":
+        signs = torch.from_numpy(x["signs"]).to(dev)
+        q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+        k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+        v8t = torch.empty((w.B, w.Hkv, w.d, api.padded_keys(w.Nk)), dtype=torch.uint8, device=dev)
+        descale = torch.empty(3, dtype=torch.float32, device=dev)
+        amax_ws = torch.empty(3, dtype=torch.int32, device=dev)
+
+        def prepare():
+            api.fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, stream)
+
+        def attend():
+            api.fa_fwd_fp8(q8, k8, v8t, descale, o, lse, w.softmax_scale, w.causal, stream)
+    else:
+        fwd = api.fa_fwd if w.dtype == "bf16" else api.fa_fwd_f32
+
+        def prepare():
+            pass
+
+        def attend():
+            fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
 
     for _ in range(args.warmup):
-        fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+        prepare()
+        attend()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
+
+    # events around every attention launch give its own duration; the step
+    # time is the span from the first to the last event
+    marks = [(event(), event()) for _ in range(args.steps)]
+    e0, e1 = event(), event()
     t0 = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
-        fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+    for a, b in marks:
+        prepare()
+        a.record(stream)
+        attend()
+        b.record(stream)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
+    kernel_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"{args.steps} launches: {ms:.4f} ms/launch (events), {wall / args.steps * 1e3:.4f} ms/launch (wall), "
-        f"{tflops:.1f} TFLOP/s")
+    kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
+    log(f"{args.steps} steps: {ms:.4f} ms/step (events), {wall / args.steps * 1e3:.4f} ms/step (wall), "
+        f"{tflops:.1f} TFLOP/s; attention kernel {kernel_ms:.4f} ms/launch, {kernel_tflops:.1f} TFLOP/s")
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -172,6 +209,10 @@ def main():
 
     peak = PEAK_TFLOPS[w.dtype]
     traffic = load_traffic(args.config)
+    data = "synthetic (seeded N(0,1), generated on the host, resident in HBM before timing)"
+    if w.dtype == "fp8":
+        data = ("synthetic (seeded N(0,1) bf16, Q and K with +-50 outliers at p=0.001; quantised to e4m3 "
+                "inside every step; resident in HBM before timing)")
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -184,12 +225,16 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1), generated on the host, resident in HBM before timing)",
+        "data": data,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "kernel": "fa_fwd_kernel"},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": traffic},
+                   "causal": w.causal, "kernel": KERNEL_NAME[w.dtype]},
+        "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(kernel_tflops / peak, 4), "traffic": traffic,
+                     "kernel_ms": round(kernel_ms, 5)},
     }
+    if w.dtype == "fp8":
+        line["config"]["steps_in_a_step"] = "fa_fp8_prepare (rotation, scales, e4m3) + fa_fwd_fp8"
+        line["prepare_ms"] = round(ms - kernel_ms, 5)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
     print(json.dumps(line), flush=True)

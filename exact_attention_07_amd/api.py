@@ -40,6 +40,10 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = fwd_args
         fn.restype = ctypes.c_int
+    L.fa_fp8_prepare.argtypes = [vp] * 9 + [i] * 6 + [vp]
+    L.fa_fp8_prepare.restype = ctypes.c_int
+    L.fa_fwd_fp8.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp]
+    L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_abi_version.argtypes = []
@@ -116,3 +120,74 @@ def attention(q, k, v, causal: bool = False, scale: float | None = None, stream=
     else:
         raise TypeError(f"unsupported dtype {q.dtype}")
     return o, lse
+
+
+def padded_keys(nk: int) -> int:
+    """Key count of the transposed fp8 V (a multiple of 64)."""
+    return (nk + 63) // 64 * 64
+
+
+def fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs=None, stream=None) -> None:
+    """Rotate (if signs is given) and quantise bf16 q, k, v into e4m3 codes (uint8 tensors)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("fa_fp8_prepare takes bfloat16 q, k, v")
+    if tuple(q8.shape) != tuple(q.shape) or tuple(k8.shape) != tuple(k.shape) or \
+            tuple(v8t.shape) != (B, Hkv, d, padded_keys(Nk)) or tuple(v.shape) != tuple(k.shape):
+        raise ValueError("code tensor shapes: q8 like q, k8 like k, v8t [B, Hkv, d, Nk rounded up to 64]")
+    for t in (q8, k8, v8t):
+        if t.dtype != torch.uint8:
+            raise TypeError("code tensors are uint8")
+    if descale.numel() < 3 or descale.dtype != torch.float32 or amax_ws.numel() < 3 or amax_ws.dtype != torch.int32:
+        raise ValueError("descale: 3 float32, amax_ws: 3 int32")
+    for t in (q, k, v, q8, k8, v8t, descale, amax_ws) + ((signs,) if signs is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous GPU tensors")
+    if signs is not None and (signs.numel() != d or signs.dtype != torch.float32):
+        raise ValueError("signs: d float32 values")
+    _check(lib().fa_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8t), _ptr(descale),
+                                _ptr(amax_ws), _ptr(signs), B, Hq, Hkv, Nq, Nk, d, _stream(stream)),
+           "fa_fp8_prepare")
+
+
+def fa_fwd_fp8(q8, k8, v8t, descale, o, lse, scale: float, causal: bool, stream=None) -> None:
+    """fp8 forward pass on codes from fa_fp8_prepare into o (bf16) and lse (fp32 or None)."""
+    import torch
+    B, Hq, Nq, d = q8.shape
+    _, Hkv, Nk, _ = k8.shape
+    if tuple(v8t.shape) != (B, Hkv, d, padded_keys(Nk)) or tuple(o.shape) != tuple(q8.shape):
+        raise ValueError("shape mismatch")
+    if o.dtype != torch.bfloat16:
+        raise TypeError("o is bfloat16")
+    if lse is not None and tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be [B, Hq, Nq]")
+    for t in (q8, k8, v8t, descale, o) + ((lse,) if lse is not None else ()):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous GPU tensors")
+    _check(lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(descale), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk,
+                            d, float(scale), int(bool(causal)), _stream(stream)), "fa_fwd_fp8")
+
+
+def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None, signs=None, stream=None):
+    """Quantise bf16 q, k, v (optionally rotating q and k) and run the fp8 forward pass.
+
+    Returns (o, lse, prep) with prep = dict(q8, k8, v8t, descale).
+    """
+    import torch
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dev = q.device
+    q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
+    k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
+    v8t = torch.empty((B, Hkv, d, padded_keys(Nk)), dtype=torch.uint8, device=dev)
+    descale = torch.empty(3, dtype=torch.float32, device=dev)
+    amax_ws = torch.empty(3, dtype=torch.int32, device=dev)
+    fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, stream)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
+    fa_fwd_fp8(q8, k8, v8t, descale, o, lse, scale, causal, stream)
+    return o, lse, {"q8": q8, "k8": k8, "v8t": v8t, "descale": descale}

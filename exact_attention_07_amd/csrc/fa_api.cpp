@@ -16,25 +16,34 @@ constexpr double LOG2E = 1.4426950408889634074;
 constexpr long long MIN_WORKGROUPS = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Shape checks shared by every entry point.
+fa_status validate_shape(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA_RATIO;
+  const double elems = (double)B * (double)(Hq > Hkv ? Hq : Hkv) * (double)(Nq > Nk ? Nq : Nk) * d;
+  if (elems > 9.0e18) return FA_ERR_SHAPE;
+  // one key/value head (the range of a buffer resource) fits in 31 bits
+  if (((double)Nk + 64.0) * d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
+  return FA_OK;
+}
 
 // Checks shared by the forward entry points; nothing touches HIP.
 fa_status validate(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int Hq,
                    int Hkv, int Nq, int Nk, int d, float scale, int causal) {
   if (!q || !k || !v || !o) return FA_ERR_NULL;
-  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128 && d != 256) return FA_ERR_HEAD_DIM;
-  if (Hq % Hkv != 0) return FA_ERR_GQA_RATIO;
+  const fa_status st = validate_shape(B, Hq, Hkv, Nq, Nk, d);
+  if (st != FA_OK) return st;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return FA_ERR_ALIGN;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
-  // every element offset must fit in 63 bits, and one key/value head (the
-  // range of a buffer resource) in 31 bits
-  const double elems = (double)B * (double)(Hq > Hkv ? Hq : Hkv) * (double)(Nq > Nk ? Nq : Nk) * d;
-  if (elems > 9.0e18) return FA_ERR_SHAPE;
-  if ((double)Nk * d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
   return FA_OK;
 }
+
+fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int f32);
 
 fa_status forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
                   int Nk, int d, float scale, int causal, void* stream, int f32) {
@@ -49,6 +58,15 @@ fa_status forward(const void* q, const void* k, const void* v, void* o, float* l
   const float c = (float)((double)scale * LOG2E);
   hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int f32) {
+  const int qpw = fa::queries_per_wave(d, f32);
+  // the fp32 path is instantiated for 4-wave workgroups only; the bf16 and
+  // fp8 paths use up to 4 waves per workgroup (two workgroups share a CU at
+  // d <= 128)
+  return f32 ? fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4)
+             : fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS, 4);
 }
 
 }  // namespace
@@ -80,6 +98,38 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv,
                      int Nq, int Nk, int d, float scale, int causal, void* stream) {
   return forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream, 1);
+}
+
+fa_status fa_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t, float* descale,
+                         unsigned* amax_ws, const float* signs, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                         void* stream) {
+  if (!q || !k || !v || !q8 || !k8 || !v8t || !descale || !amax_ws) return FA_ERR_NULL;
+  const fa_status st = validate_shape(B, Hq, Hkv, Nq, Nk, d);
+  if (st != FA_OK) return st;
+  if (fa::fp8_prepare_too_large(B, Hq, Hkv, Nq, Nk)) return FA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t) ||
+      !aligned4(descale) || !aligned4(amax_ws) || (signs && !aligned4(signs)))
+    return FA_ERR_ALIGN;
+  const hipError_t e =
+      fa::launch_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, B, Hq, Hkv, Nq, Nk, d, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+  if (!q8 || !k8 || !v8t || !descale || !o) return FA_ERR_NULL;
+  const fa_status st = validate_shape(B, Hq, Hkv, Nq, Nk, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) || (lse && !aligned16(lse)) ||
+      !aligned4(descale))
+    return FA_ERR_ALIGN;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_FLAG;
+  const fa_plan_t p = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, 0);
+  if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const hipError_t e =
+      fa::launch_fwd_fp8(q8, k8, v8t, descale, o, lse, p, d, (float)((double)scale * LOG2E), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

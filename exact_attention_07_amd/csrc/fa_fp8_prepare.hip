@@ -1,0 +1,261 @@
+// fa_fp8_prepare.hip -- FP8 "incoherent processing" step for gfx950.
+//
+// "FlashAttention-3 — 闪电注意力-3", section on low precision (FP8): Q and K
+// are multiplied by a random orthogonal matrix (a Hadamard matrix with random
+// signs) before they are quantised, which spreads outlier channels over all
+// channels while leaving Q K^T unchanged; then every tensor is quantised to
+// 8-bit floating point.  Here:
+//   * M = diag(signs) H_d / sqrt(d) (H_d the Sylvester Hadamard matrix),
+//     applied on the right, x -> x M, to every row of Q and K; V is not
+//     rotated; signs == NULL skips the rotation.  x M is computed as a fast
+//     Walsh-Hadamard transform of (x * signs) scaled by 1/sqrt(d), in fp32.
+//   * one scale per tensor: s = amax|x| / 448 (s = 1 for an all-zero
+//     tensor); codes = e4m3(x / s), rounded to nearest even by
+//     v_cvt_pk_fp8_f32 (OCP E4M3, largest finite 448).
+//   * V is written transposed, [B][Hkv][d][Nkp] with Nkp = Nk rounded up to
+//     a multiple of 64; within each block of 64 keys the keys are stored in
+//     the order the attention kernel's P fragments use (see fa.h); padding
+//     keys are zero.
+//
+// Work layout: a row of d elements is handled by 8 consecutive lanes, each
+// holding d/8 consecutive elements; the transform runs its first log2(d/8)
+// butterfly stages inside each lane and the last three across the 8 lanes
+// (__shfl_xor).  Three kernels run in order on the caller's stream: zero the
+// amax words, rotate + amax (atomicMax on the float bits, all values >= 0),
+// rotate + quantise.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float E4M3_MAX = 448.0f;
+constexpr int FP8_BC = 64;  // key block of the V^T permutation (the attention kernel's tile)
+
+// Position of key k (0..63) of a 64-key block in the permuted V^T order:
+// key bits [b5 | b4 b3 | b2 | b1 b0] -> position bits [b2 | b5 | b4 b3 | b1 b0].
+__device__ __forceinline__ int v_perm64(int k) {
+  return (((k >> 2) & 1) << 5) | (((k >> 5) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+}
+
+// Load the EPL = D/8 elements of lane `sub` (0..7) of a row as fp32.
+template <int D>
+__device__ __forceinline__ void load_row_part(const __bf16* row, int sub, float (&x)[D / 8]) {
+  constexpr int EPL = D / 8;
+#pragma unroll
+  for (int c = 0; c < EPL / 8; ++c) {
+    const bf16x8 v = *(const bf16x8*)(row + sub * EPL + c * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[c * 8 + e] = (float)v[e];
+  }
+}
+
+// x <- (x * signs) H_d / sqrt(d) for the row spread over 8 lanes.
+template <int D>
+__device__ __forceinline__ void rotate(float (&x)[D / 8], const float* signs, int sub) {
+  constexpr int EPL = D / 8;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] *= signs[sub * EPL + e];
+  // in-lane butterflies, strides 1 .. EPL/2
+#pragma unroll
+  for (int h = 1; h < EPL; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      if ((e & h) == 0) {
+        const float a = x[e], b = x[e + h];
+        x[e] = a + b;
+        x[e + h] = a - b;
+      }
+  // cross-lane butterflies, strides EPL, 2 EPL, 4 EPL (lanes sub ^ 1, 2, 4)
+#pragma unroll
+  for (int bit = 1; bit < 8; bit <<= 1) {
+    const bool upper = (sub & bit) != 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      const float other = __shfl_xor(x[e], bit, 64);
+      x[e] = upper ? other - x[e] : x[e] + other;
+    }
+  }
+  const float inv = 1.0f / __builtin_sqrtf((float)D);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) x[e] *= inv;
+}
+
+__device__ __forceinline__ void amax_to(unsigned* word, float m) {
+  // reduce over the wave, then one atomic per wave; m >= 0 so the float bit
+  // pattern orders like the value
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(word, __float_as_uint(m));
+}
+
+__device__ __forceinline__ float scale_of(unsigned amax_bits) {
+  const float a = __uint_as_float(amax_bits);
+  return a > 0.f ? a / E4M3_MAX : 1.0f;
+}
+
+// 4 floats -> 4 e4m3 bytes (round to nearest even)
+__device__ __forceinline__ unsigned pack4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (unsigned)w;
+}
+
+__global__ void zero3_kernel(unsigned* w) {
+  if (threadIdx.x < 3) w[threadIdx.x] = 0u;
+}
+
+// pass 1: amax of the rotated Q and K rows (tensor 0, 1) and of V (tensor 2)
+template <int D>
+__global__ __launch_bounds__(256) void amax_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                   const __bf16* __restrict__ v, const float* __restrict__ signs,
+                                                   long long rows_q, long long rows_k, unsigned* __restrict__ amax) {
+  const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
+  const int tensor = blockIdx.y;  // 0: Q, 1: K, 2: V
+  const long long rows = tensor == 0 ? rows_q : rows_k;
+  const __bf16* base = tensor == 0 ? q : tensor == 1 ? k : v;
+  // rows past the end are zero (the shuffles of rotate() stay uniform)
+  float x[D / 8] = {};
+  if (row < rows) load_row_part<D>(base + row * D, sub, x);
+  if (tensor < 2 && signs != nullptr) rotate<D>(x, signs, sub);
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < D / 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  amax_to(&amax[tensor], m);
+}
+
+// pass 2 for Q and K: rotate again and quantise; descale written by block 0
+template <int D>
+__global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+                                                       const float* __restrict__ signs, long long rows_q,
+                                                       long long rows_k, uint8_t* __restrict__ q8,
+                                                       uint8_t* __restrict__ k8, const unsigned* __restrict__ amax,
+                                                       float* __restrict__ descale) {
+  const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
+  const int tensor = blockIdx.y;  // 0: Q, 1: K
+  const long long rows = tensor == 0 ? rows_q : rows_k;
+  const float s = scale_of(amax[tensor]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    descale[tensor] = s;
+    if (tensor == 0) descale[2] = scale_of(amax[2]);
+  }
+  const float inv = 1.0f / s;
+  float x[D / 8] = {};
+  const bool ok = row < rows;
+  if (ok) load_row_part<D>((tensor == 0 ? q : k) + row * D, sub, x);
+  if (signs != nullptr) rotate<D>(x, signs, sub);
+  if (!ok) return;
+  uint8_t* out = (tensor == 0 ? q8 : k8) + row * D + sub * (D / 8);
+#pragma unroll
+  for (int c = 0; c < D / 8 / 16; ++c) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = c * 16 + e * 4;
+      w[e] = pack4(x[i] * inv, x[i + 1] * inv, x[i + 2] * inv, x[i + 3] * inv);
+    }
+    *(u32x4*)(out + c * 16) = w;
+  }
+  if constexpr (D / 8 < 16) {  // d = 64: 8 bytes per lane
+    unsigned w0 = pack4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+    unsigned w1 = pack4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+    *(unsigned long long*)out = ((unsigned long long)w1 << 32) | w0;
+  }
+}
+
+// pass 2 for V: quantise a block of 64 keys x D of one (b, h_kv), write it
+// transposed with the keys of the block permuted; keys >= Nk are zero.
+template <int D>
+__global__ __launch_bounds__(256) void quant_v_kernel(const __bf16* __restrict__ v, int Nk, int Nkp,
+                                                      uint8_t* __restrict__ v8t, const unsigned* __restrict__ amax) {
+  __shared__ uint8_t tile[FP8_BC][D + 4];
+  const int nblk = Nkp / FP8_BC;
+  const int blk = (int)(blockIdx.x % nblk);          // key block
+  const long long head = blockIdx.x / nblk;          // b * Hkv + h_kv
+  const float inv = 1.0f / scale_of(amax[2]);
+  const __bf16* src = v + head * (long long)Nk * D;
+  // load + quantise: 64 rows x D, 8 elements per thread-step
+  for (int idx = threadIdx.x; idx < FP8_BC * D / 8; idx += blockDim.x) {
+    const int r = idx / (D / 8), c8 = (idx % (D / 8)) * 8;
+    const int key = blk * FP8_BC + r;
+    float x[8] = {};
+    if (key < Nk) {
+      const bf16x8 t = *(const bf16x8*)(src + (long long)key * D + c8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (float)t[e] * inv;
+    }
+    const unsigned w0 = pack4(x[0], x[1], x[2], x[3]), w1 = pack4(x[4], x[5], x[6], x[7]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[r][c8 + e] = (uint8_t)(w0 >> (8 * e));
+      tile[r][c8 + 4 + e] = (uint8_t)(w1 >> (8 * e));
+    }
+  }
+  __syncthreads();
+  // write: row d of V^T gets 64 bytes, byte p = key with v_perm64(key) == p
+  uint8_t* dst = v8t + head * (long long)D * Nkp + (long long)blk * FP8_BC;
+  for (int idx = threadIdx.x; idx < D * (FP8_BC / 4); idx += blockDim.x) {
+    const int d = idx / (FP8_BC / 4), p4 = (idx % (FP8_BC / 4)) * 4;
+    unsigned w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // inverse permutation: the key stored at position p
+      const int p = p4 + e;
+      const int key = (((p >> 5) & 1) << 2) | (((p >> 4) & 1) << 5) | (((p >> 2) & 3) << 3) | (p & 3);
+      w |= (unsigned)tile[key][d] << (8 * e);
+    }
+    *(unsigned*)(dst + (long long)d * Nkp + p4) = w;
+  }
+}
+
+}  // namespace
+
+template <int D>
+static hipError_t launch_prepare_d(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
+                                   float* descale, unsigned* amax, const float* signs, long long rows_q,
+                                   long long rows_k, long long heads_kv, int Nk, hipStream_t stream) {
+  const int Nkp = (Nk + FP8_BC - 1) / FP8_BC * FP8_BC;
+  hipLaunchKernelGGL(zero3_kernel, dim3(1), dim3(64), 0, stream, amax);
+  const long long rmax = rows_q > rows_k ? rows_q : rows_k;
+  const dim3 g1((unsigned)((rmax + 31) / 32), 3);
+  hipLaunchKernelGGL(amax_kernel<D>, g1, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
+                     (const __bf16*)v, signs, rows_q, rows_k, amax);
+  const dim3 g2((unsigned)((rmax + 31) / 32), 2);
+  hipLaunchKernelGGL(quant_qk_kernel<D>, g2, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k, signs, rows_q,
+                     rows_k, (uint8_t*)q8, (uint8_t*)k8, (const unsigned*)amax, descale);
+  const dim3 g3((unsigned)((long long)(Nkp / FP8_BC) * heads_kv));
+  hipLaunchKernelGGL(quant_v_kernel<D>, g3, dim3(256), 0, stream, (const __bf16*)v, Nk, Nkp, (uint8_t*)v8t,
+                     (const unsigned*)amax);
+  return hipGetLastError();
+}
+
+bool fp8_prepare_too_large(int B, int Hq, int Hkv, int Nq, int Nk) {
+  // every grid is one-dimensional with fewer than 2^31 workgroups
+  const long long rows_q = (long long)B * Hq * Nq, rows_k = (long long)B * Hkv * Nk;
+  const long long rmax = rows_q > rows_k ? rows_q : rows_k;
+  return (rmax + 31) / 32 > 0x7fffffffLL ||
+         (long long)((Nk + FP8_BC - 1) / FP8_BC) * ((long long)B * Hkv) > 0x7fffffffLL;
+}
+
+hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
+                              float* descale, unsigned* amax, const float* signs, int B, int Hq, int Hkv, int Nq,
+                              int Nk, int d, hipStream_t stream) {
+  const long long rows_q = (long long)B * Hq * Nq, rows_k = (long long)B * Hkv * Nk;
+  const long long heads_kv = (long long)B * Hkv;
+  if (fp8_prepare_too_large(B, Hq, Hkv, Nq, Nk)) return hipErrorInvalidValue;
+  if (d == 64) return launch_prepare_d<64>(q, k, v, q8, k8, v8t, descale, amax, signs, rows_q, rows_k, heads_kv, Nk, stream);
+  if (d == 128) return launch_prepare_d<128>(q, k, v, q8, k8, v8t, descale, amax, signs, rows_q, rows_k, heads_kv, Nk, stream);
+  if (d == 256) return launch_prepare_d<256>(q, k, v, q8, k8, v8t, descale, amax, signs, rows_q, rows_k, heads_kv, Nk, stream);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -16,6 +16,21 @@ int queries_per_wave(int d, int f32);
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
                       float c, int f32, hipStream_t stream);
 
+// Enqueue the fp8 forward kernel (operands from launch_fp8_prepare).
+hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale, void* o, float* lse,
+                          const fa_plan_t& p, int d, float c, hipStream_t stream);
+
+// True if a preparation of this shape needs a grid of 2^31 or more
+// workgroups (such shapes are rejected).
+bool fp8_prepare_too_large(int B, int Hq, int Hkv, int Nq, int Nk);
+
+// Enqueue the fp8 preparation: optional Hadamard rotation of Q and K,
+// per-tensor amax, e4m3 quantisation, V transposed (fa.h describes the
+// layouts).  amax: 3 device words of workspace.
+hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
+                              float* descale, unsigned* amax, const float* signs, int B, int Hq, int Hkv, int Nq,
+                              int Nk, int d, hipStream_t stream);
+
 }  // namespace fa
 
 #endif

@@ -90,6 +90,47 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
                      float scale, int causal, void* stream);
 
+/*
+ * FP8 preparation ("FlashAttention-3 — 闪电注意力-3", section on low
+ * precision and the reduction of quantisation error): rotate Q and K by an
+ * orthogonal matrix, quantise Q, K and V to 8-bit floating point with one
+ * scale per tensor.
+ *
+ *   q, k, v   bf16, [B][Hq][Nq][d], [B][Hkv][Nk][d], [B][Hkv][Nk][d]
+ *   signs     fp32, d values of +1 or -1 (device), or NULL: no rotation.
+ *             Rotation: x -> x diag(signs) H_d / sqrt(d) for every row of Q
+ *             and K, H_d the Sylvester Hadamard matrix (H_1 = [1],
+ *             H_2n = [[H, H], [H, -H]]); V is not rotated.  The product
+ *             Q K^T is unchanged by the rotation.
+ *   q8, k8    OCP E4M3 codes (1 byte each), same layouts as q and k
+ *   v8t       E4M3 codes of V transposed: [B][Hkv][d][Nkp], Nkp = Nk rounded
+ *             up to a multiple of 64.  Within each block of 64 keys, key
+ *             kk = 32 a + 8 g + 4 h + r (a, h in {0,1}, g, r in {0..3}) is
+ *             stored at position 32 h + 16 a + 4 g + r; keys >= Nk are zero.
+ *   descale   3 fp32 (device): s_q, s_k, s_v, with s = amax|x| / 448 over the
+ *             whole (rotated) tensor (1 for an all-zero tensor); x is
+ *             represented by s * decode(code).
+ *   amax_ws   3 uint32 of device workspace (zeroed and used inside).
+ * Codes are rounded to nearest even; |x| / s <= 448 by construction.  The
+ * scales stay on the device: nothing is synchronised.  Pointers of the code
+ * tensors and q, k, v are 16-byte aligned; descale, amax_ws, signs 4-byte.
+ */
+fa_status fa_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
+                         float* descale, unsigned* amax_ws, const float* signs,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, void* stream);
+
+/*
+ * FP8 forward pass on the output of fa_fp8_prepare: O (bf16) and LSE (fp32)
+ * of softmax(scale * Q K^T) V with Q, K, V represented by their codes and
+ * scales.  Both products run on e4m3 MFMA with fp32 accumulation; the
+ * probabilities multiply V as e4m3 values (unscaled, at most 2^8), while the
+ * row sums and the LSE use the fp32 probabilities.  Conventions (GQA,
+ * causal, errors) as for fa_fwd.
+ */
+fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale,
+                     void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                     float scale, int causal, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -69,3 +69,41 @@ def call(lib, fn="fa_fwd", **kw):
 ])
 def test_invalid_arguments_are_rejected_on_the_host(lib, fn, kw, status):
     assert call(lib, fn, **kw) == status
+
+
+FP8_GOOD = dict(q=P, k=P, v=P, q8=P, k8=P, v8t=P, descale=P, amax=P, signs=P, B=1, Hq=4, Hkv=2, Nq=10, Nk=10,
+                d=128)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(q8=None), 1), (dict(k8=None), 1),
+    (dict(v8t=None), 1), (dict(descale=None), 1), (dict(amax=None), 1),
+    (dict(B=0), 2), (dict(Nk=0), 2), (dict(Nq=-3), 2), (dict(d=96), 3), (dict(Hq=5, Hkv=2), 4),
+    (dict(q8=P + 8), 5), (dict(v8t=P + 1), 5), (dict(descale=P + 2), 5), (dict(amax=P + 1), 5),
+    (dict(signs=P + 2), 5),
+])
+def test_fp8_prepare_rejects_invalid_arguments(lib, kw, status):
+    a = dict(FP8_GOOD)
+    a.update(kw)
+    assert lib.fa_fp8_prepare(a["q"], a["k"], a["v"], a["q8"], a["k8"], a["v8t"], a["descale"], a["amax"],
+                              a["signs"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], None) == status
+
+
+FWD8_GOOD = dict(q8=P, k8=P, v8t=P, descale=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=10, Nk=10, d=128, scale=0.1,
+                 causal=0)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q8=None), 1), (dict(k8=None), 1), (dict(v8t=None), 1), (dict(descale=None), 1), (dict(o=None), 1),
+    (dict(Hkv=0), 2), (dict(d=64 + 16), 3), (dict(Hq=3, Hkv=2), 4),
+    (dict(o=P + 8), 5), (dict(lse=P + 4), 5), (dict(descale=P + 1), 5),
+    (dict(scale=0.0), 6), (dict(scale=float("nan")), 6), (dict(causal=3), 8),
+    (dict(Nk=(1 << 31) // (4 * 256)), 2),
+])
+def test_fp8_forward_rejects_invalid_arguments(lib, kw, status):
+    a = dict(FWD8_GOOD)
+    a.update(kw)
+    if "Nk" in kw:
+        a["d"] = 256
+    assert lib.fa_fwd_fp8(a["q8"], a["k8"], a["v8t"], a["descale"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Nq"], a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], None) == status
