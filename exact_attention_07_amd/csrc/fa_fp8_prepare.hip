@@ -20,9 +20,10 @@
 // Work layout: a row of d elements is handled by 8 consecutive lanes, each
 // holding d/8 consecutive elements; the transform runs its first log2(d/8)
 // butterfly stages inside each lane and the last three across the 8 lanes
-// (__shfl_xor).  Three kernels run in order on the caller's stream: zero the
-// amax words, rotate + amax (atomicMax on the float bits, all values >= 0),
-// rotate + quantise.
+// (__shfl_xor).  Four kernels run in order on the caller's stream: zero the
+// amax words; rotate + amax (a grid-stride loop, one atomicMax on the float
+// bits per workgroup, all values >= 0); rotate + quantise Q and K; quantise
+// and transpose V.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,12 +89,15 @@ __device__ __forceinline__ void rotate(float (&x)[D / 8], const float* signs, in
   for (int e = 0; e < EPL; ++e) x[e] *= inv;
 }
 
+// max over the workgroup (256 threads), then one atomic per workgroup; m >= 0
+// so the float bit pattern orders like the value
 __device__ __forceinline__ void amax_to(unsigned* word, float m) {
-  // reduce over the wave, then one atomic per wave; m >= 0 so the float bit
-  // pattern orders like the value
+  __shared__ float part[4];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(word, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(word, __float_as_uint(fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]))));
 }
 
 __device__ __forceinline__ float scale_of(unsigned amax_bits) {
@@ -112,23 +116,28 @@ __global__ void zero3_kernel(unsigned* w) {
   if (threadIdx.x < 3) w[threadIdx.x] = 0u;
 }
 
-// pass 1: amax of the rotated Q and K rows (tensor 0, 1) and of V (tensor 2)
+// pass 1: amax of the rotated Q and K rows (tensor 0, 1) and of V (tensor 2).
+// A grid-stride loop over groups of 32 rows (the loop bound is uniform over
+// the workgroup) keeps the number of workgroups, and so of atomics on the
+// three words, small.
 template <int D>
 __global__ __launch_bounds__(256) void amax_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                    const __bf16* __restrict__ v, const float* __restrict__ signs,
                                                    long long rows_q, long long rows_k, unsigned* __restrict__ amax) {
-  const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int sub = threadIdx.x & 7;
   const int tensor = blockIdx.y;  // 0: Q, 1: K, 2: V
   const long long rows = tensor == 0 ? rows_q : rows_k;
   const __bf16* base = tensor == 0 ? q : tensor == 1 ? k : v;
-  // rows past the end are zero (the shuffles of rotate() stay uniform)
-  float x[D / 8] = {};
-  if (row < rows) load_row_part<D>(base + row * D, sub, x);
-  if (tensor < 2 && signs != nullptr) rotate<D>(x, signs, sub);
   float m = 0.f;
+  for (long long r0 = (long long)blockIdx.x * 32; r0 < rows; r0 += (long long)gridDim.x * 32) {
+    const long long row = r0 + (threadIdx.x >> 3);
+    // rows past the end are zero (the shuffles of rotate() stay uniform)
+    float x[D / 8] = {};
+    if (row < rows) load_row_part<D>(base + row * D, sub, x);
+    if (tensor < 2 && signs != nullptr) rotate<D>(x, signs, sub);
 #pragma unroll
-  for (int e = 0; e < D / 8; ++e) m = fmaxf(m, fabsf(x[e]));
+    for (int e = 0; e < D / 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  }
   amax_to(&amax[tensor], m);
 }
 
@@ -226,7 +235,9 @@ static hipError_t launch_prepare_d(const void* q, const void* k, const void* v, 
   const int Nkp = (Nk + FP8_BC - 1) / FP8_BC * FP8_BC;
   hipLaunchKernelGGL(zero3_kernel, dim3(1), dim3(64), 0, stream, amax);
   const long long rmax = rows_q > rows_k ? rows_q : rows_k;
-  const dim3 g1((unsigned)((rmax + 31) / 32), 3);
+  // at most 1024 workgroups per tensor: 4 per CU
+  const long long groups = (rmax + 31) / 32;
+  const dim3 g1((unsigned)(groups < 1024 ? groups : 1024), 3);
   hipLaunchKernelGGL(amax_kernel<D>, g1, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, signs, rows_q, rows_k, amax);
   const dim3 g2((unsigned)((rmax + 31) / 32), 2);
