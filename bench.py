@@ -36,7 +36,14 @@ sys.path.insert(0, ROOT)
 METRIC = "attention fwd TFLOP/s + % of MFMA peak (bf16, causal GQA, N=8K, d=128)"
 # MI355X published dense peaks (no sparsity), TFLOP/s
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "fp8": 5000.0}
-KERNEL_SOURCES = ["exact_attention_07_amd/csrc/fa_fwd.hip"]
+# sources of the attention kernel of each dtype (the traffic summary is valid
+# only for the sources it was measured on)
+_CSRC = "exact_attention_07_amd/csrc/"
+KERNEL_SOURCES = {
+    "bf16": [_CSRC + f for f in ("fa_fwd.hip", "fa_device.h", "plan.h")],
+    "f32": [_CSRC + f for f in ("fa_fwd.hip", "fa_device.h", "plan.h")],
+    "fp8": [_CSRC + f for f in ("fa_fwd_fp8.hip", "fa_device.h", "plan.h")],
+}
 KERNEL_NAME = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel"}
 
 
@@ -44,18 +51,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(cfg: int = 3) -> str:
+def source_hash(dtype: str) -> str:
     h = hashlib.sha256()
-    extra = ["exact_attention_07_amd/csrc/fa_fp8_prepare.hip"] if cfg == 5 else []
-    for p in KERNEL_SOURCES + extra:
+    for p in KERNEL_SOURCES[dtype]:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_traffic(cfg: int):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source."""
+def load_traffic(cfg: int, dtype: str):
+    """HBM bytes per launch of the attention kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
     path = os.path.join(ROOT, "profiles", f"traffic_config{cfg}.txt")
     if not os.path.exists(path):
         return None
@@ -64,7 +70,7 @@ def load_traffic(cfg: int):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != source_hash(cfg):
+    if fields.get("kernel_source_sha256") != source_hash(dtype):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -208,7 +214,7 @@ def main():
         log(f"check on {len(rows)} rows: max|dO|={err:.2e} max|dLSE|={lerr:.2e}")
 
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(args.config)
+    traffic = load_traffic(args.config, w.dtype)
     data = "synthetic (seeded N(0,1), generated on the host, resident in HBM before timing)"
     if w.dtype == "fp8":
         data = ("synthetic (seeded N(0,1) bf16, Q and K with +-50 outliers at p=0.001; quantised to e4m3 "

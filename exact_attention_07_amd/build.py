@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_fp8_prepare.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_fwd_fp8.hip", "fa_fp8_prepare.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the device code on purpose.
@@ -33,9 +33,10 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    objs = []
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(HERE, "_build", src + ".o")
         cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
@@ -43,7 +44,10 @@ def build(verbose: bool = False) -> str:
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
-        objs.append(obj)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as pool:
+        objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
