@@ -43,30 +43,28 @@ fa_status validate(const void* q, const void* k, const void* v, const void* o, c
   return FA_OK;
 }
 
-fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int f32);
+enum { KIND_BF16 = 0, KIND_F32 = 1, KIND_FP8 = 2 };
+fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int kind);
 
 fa_status forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
                   int Nk, int d, float scale, int causal, void* stream, int f32) {
   fa_status st = validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
   if (st != FA_OK) return st;
-  const int qpw = fa::queries_per_wave(d, f32);
-  // the fp32 path is instantiated for 4-wave workgroups only
-  // bf16: up to 4 waves per workgroup (two workgroups share a CU at d <= 128)
-  const fa_plan_t p = f32 ? fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4)
-                          : fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS, 4);
+  const fa_plan_t p = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, f32 ? KIND_F32 : KIND_BF16);
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
   const float c = (float)((double)scale * LOG2E);
   hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int f32) {
-  const int qpw = fa::queries_per_wave(d, f32);
-  // the fp32 path is instantiated for 4-wave workgroups only; the bf16 and
-  // fp8 paths use up to 4 waves per workgroup (two workgroups share a CU at
-  // d <= 128)
-  return f32 ? fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4)
-             : fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS, 4);
+fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int kind) {
+  const int qpw = fa::queries_per_wave(d, kind == KIND_F32);
+  // fp32: 4-wave workgroups.  fp8: up to 4 waves (two workgroups share a CU
+  // at d <= 128).  bf16 at d = 128: up to 8 waves, one workgroup per CU, so
+  // that each K/V tile copied from L2 serves twice the query rows.
+  if (kind == KIND_F32) return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4);
+  const int max_nw = (kind == KIND_BF16 && d == 128) ? 8 : 4;
+  return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS, max_nw);
 }
 
 }  // namespace
@@ -125,7 +123,7 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const floa
     return FA_ERR_ALIGN;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
-  const fa_plan_t p = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, 0);
+  const fa_plan_t p = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, KIND_FP8);
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
   const hipError_t e =
       fa::launch_fwd_fp8(q8, k8, v8t, descale, o, lse, p, d, (float)((double)scale * LOG2E), (hipStream_t)stream);

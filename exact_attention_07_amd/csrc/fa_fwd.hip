@@ -8,24 +8,30 @@
 // Mapping onto CDNA4
 // ------------------
 // * Each wave owns 32 query rows and keeps their Q fragments in VGPRs for
-//   the whole pass; at
-//   d <= 128 a wave needs at most 256 VGPRs, so two waves share each SIMD and
-//   one wave's softmax overlaps the other's matrix products.
-// * A workgroup of NW waves (plan.h) streams K/V tiles of BC = 64 keys
-//   through LDS.  bf16 tiles are copied HBM -> LDS directly with
-//   buffer_load_dwordx4 ... lds (16 B per lane, bounds-checked by the buffer
-//   resource so rows past the end read as zero), double buffered, so the copy
-//   of tile j+1 overlaps the math on tile j (the asynchronous next-block load
-//   of "FlashAttention-3 — 闪电注意力-3", section on minimising memory
-//   operations).  LDS rows are padded so that both the row reads of K and the
-//   transposed reads of V hit distinct banks with plain "lane base +
-//   constant" addresses.
+//   the whole pass; at d <= 128 a wave needs at most 256 VGPRs, so two waves
+//   share each SIMD.
+// * A workgroup of NW waves (plan.h; up to 8 at d = 128, one workgroup per
+//   CU, so that every K/V tile fetched from L2 serves 256 query rows) streams
+//   K/V tiles of BC = 64 keys through LDS.  Tiles are copied HBM -> LDS
+//   directly with buffer_load_dwordx4 ... lds (16 B per lane, bounds-checked
+//   by the buffer resource so rows past the end read as zero), double
+//   buffered, so the copy of a tile overlaps the math on the tiles before it
+//   (the asynchronous next-block load of "FlashAttention-3 — 闪电注意力-3",
+//   section on minimising memory operations).  LDS rows are padded so that
+//   the K row reads and the transposed V reads hit distinct banks with plain
+//   "lane base + constant" addresses.
 // * Scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16:
 //   the accumulator then holds, in each lane, 16 keys of ONE query, so a row
 //   maximum is an in-lane max plus one v_permlane32_swap, and the fp32
 //   accumulator registers, rounded to bf16, are directly the B operand of
 //   O^T += V^T P^T (no LDS round trip for P).  V^T fragments come from LDS
 //   with ds_read_b64_tr_b16.
+// * Each wave software-pipelines three streams per key tile: the MFMAs of
+//   the next tile's scores, the exponentials of this tile, and the MFMAs of
+//   the previous tile's P V, one MFMA per chunk with an equal share of the
+//   softmax work, so the exponentials overlap the matrix products (the
+//   softmax / matrix-product overlap FlashAttention-3 obtains with ping-pong
+//   warpgroups, "FlashAttention-3 — 闪电注意力-3", section on asynchrony).
 // * Online softmax in log2 units (c = scale * log2 e folded into one FMA).
 //   The output is rescaled only when some row's running maximum has grown by
 //   more than TAU = 8 over the reference maximum its exponentials use
@@ -63,24 +69,23 @@ struct Cfg {
   static constexpr int DS = D / 16;    // k-steps of S^T = K Q^T
   static constexpr int DB = D / 32;    // 32-row blocks of O^T
   static constexpr int PS = BC / 16;   // k-steps of O^T += V^T P^T
-  // LDS tile: BC rows of D bf16, each row padded by PAD 16-byte slots.  The
-  // row stride RS makes both access patterns conflict-free on the 64 banks:
-  // 16 lanes reading one 16-byte chunk of 16 consecutive rows (K fragments),
-  // and 16 lanes reading a pair of adjacent chunks of 4 consecutive rows (the
-  // transposed V reads), while every address stays "lane base + constant".
+  // LDS tiles: BC rows of D bf16 (CPR 16-byte data slots), each row padded so
+  // that the fragment reads hit distinct banks of the 64 x 4-byte banks with
+  // plain "lane base + constant" addresses:
+  //  * K rows: one padding slot.  A b128 read serves 16 lanes at a time,
+  //    here one 16-byte chunk of 16 consecutive rows; a row stride of an odd
+  //    multiple of 4 banks puts them on 16 distinct groups of 4 banks.
+  //  * V rows: four padding slots.  A ds_read_b64_tr_b16 serves 32 lanes at
+  //    a time, here 64 bytes (16 banks) of each of 4 consecutive rows; a row
+  //    stride of 16 (or 48) banks modulo 64 makes the four rows disjoint.
   static constexpr int CPR = D / 8;                    // data slots per row
-  static constexpr int PAD = (D == 64) ? 1 : 3;
-  static constexpr int SPR = CPR + PAD;                // slots per LDS row
-  static constexpr int RS = SPR * 16;                  // LDS row stride, bytes
-  static constexpr int TILE = BC * RS;                 // bytes of one tile
-  static constexpr int SLOTS = BC * SPR;
-  static constexpr int INS = (SLOTS + 63) / 64;        // 64-lane copy instructions per tile
+  static constexpr int SPR_K = CPR + 1;                // slots per K row
+  static constexpr int SPR_V = CPR + 4;                // slots per V row
+  static constexpr int RSK = SPR_K * 16, RSV = SPR_V * 16;  // LDS row strides, bytes
+  static constexpr int TILE_K = BC * RSK, TILE_V = BC * RSV;  // bytes of one tile
+  static_assert((RSK / 4) % 8 == 4, "K rows: odd multiple of 4 banks");
+  static_assert((RSV / 4) % 64 == 16 || (RSV / 4) % 64 == 48, "V rows: 16 or 48 banks");
 };
-
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int SG_VALU = 0x002;
-constexpr int SG_MFMA = 0x008;
-constexpr int SG_DS_READ = 0x100;
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -125,10 +130,12 @@ __device__ __forceinline__ bf16x8 v_frag(LDS_AS const char* vlane, int ps, int d
 // byte offset of the slot's data within the tile's rows in HBM (rows of D
 // bf16, contiguous); padding slots get an offset past any buffer range, so
 // their load reads zero and writes it into the (never read) padding.
-template <int D, int NW>
+template <int D, int NW, int SPR>
 struct CopyPlan {
-  using C = Cfg<D, false>;
-  static constexpr int MI = (C::INS + NW - 1) / NW;
+  static constexpr int CPR = D / 8;
+  static constexpr int INS = BC * SPR / 64;            // 64-lane copy instructions per tile
+  static_assert(BC * SPR % 64 == 0, "whole copy instructions");
+  static constexpr int MI = (INS + NW - 1) / NW;
   static constexpr unsigned OUT_OF_RANGE = 0x7ffffff0u;
   unsigned goff[MI];
   __device__ __forceinline__ void init(int wave, int lane) {
@@ -136,8 +143,8 @@ struct CopyPlan {
     for (int i = 0; i < MI; ++i) {
       const int ins = i * NW + wave;
       const int sl = ins * 64 + lane;
-      const int r = sl / C::SPR, pp = sl % C::SPR;
-      goff[i] = (ins < C::INS && pp < C::CPR) ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
+      const int r = sl / SPR, pp = sl % SPR;
+      goff[i] = (ins < INS && pp < CPR) ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
     }
   }
   // Buffer resource over a whole [Nk][D] bf16 matrix; the hardware range
@@ -152,7 +159,7 @@ struct CopyPlan {
   __device__ __forceinline__ void issue_one(const __amdgpu_buffer_rsrc_t& rs, int soff, LDS_AS char* tile,
                                             LDS_AS char* spare, int wave, int i) const {
     const int ins = i * NW + wave;
-    LDS_AS char* dst = (C::INS % NW == 0 || ins < C::INS) ? tile + ins * 1024 : spare;
+    LDS_AS char* dst = (INS % NW == 0 || ins < INS) ? tile + ins * 1024 : spare;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], soff, 0, 0);
   }
   __device__ __forceinline__ void issue_all(const __amdgpu_buffer_rsrc_t& rs, int soff, LDS_AS char* tile,
@@ -173,13 +180,13 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
 
 // fp32 tile -> (hi, lo) bf16 tiles through registers (synchronous); rows past
 // Nk are zero.
-template <int D>
+template <int D, int SPR>
 __device__ __forceinline__ void copy_tile_f32(const float* src, int j0, int Nk, LDS_AS char* tile_hi,
                                               LDS_AS char* tile_lo) {
-  using C = Cfg<D, true>;
-  for (int sl = threadIdx.x; sl < C::SLOTS; sl += blockDim.x) {
-    const int r = sl / C::SPR, pp = sl % C::SPR;
-    if (pp >= C::CPR) continue;
+  constexpr int CPR = D / 8;
+  for (int sl = threadIdx.x; sl < BC * SPR; sl += blockDim.x) {
+    const int r = sl / SPR, pp = sl % SPR;
+    if (pp >= CPR) continue;
     bf16x8 hi = {}, lo = {};
     if (j0 + r < Nk) {
       const f32x4* g = (const f32x4*)(src + (size_t)(j0 + r) * D + pp * 8);
@@ -200,13 +207,13 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(const float* __restrict
                                                           const float* __restrict__ V, float* __restrict__ O,
                                                           float* __restrict__ LSE, fa_plan_t p, float c) {
   using C = Cfg<D, true>;
-  constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RS = C::RS;
-  __shared__ __attribute__((aligned(1024))) char smem_[4 * C::TILE];
+  constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RSK = C::RSK, RSV = C::RSV;
+  __shared__ __attribute__((aligned(1024))) char smem_[2 * C::TILE_K + 2 * C::TILE_V];
   LDS_AS char* const smem = (LDS_AS char*)smem_;
   LDS_AS char* const kt = smem;
-  LDS_AS char* const ktl = smem + C::TILE;
-  LDS_AS char* const vt = smem + 2 * C::TILE;
-  LDS_AS char* const vtl = smem + 3 * C::TILE;
+  LDS_AS char* const ktl = smem + C::TILE_K;
+  LDS_AS char* const vt = smem + 2 * C::TILE_K;
+  LDS_AS char* const vtl = smem + 2 * C::TILE_K + C::TILE_V;
 
   const fa_work_t w = fa_decode(p, blockIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -239,14 +246,14 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(const float* __restrict
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
   float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
-  const int koff_l = k_lane_off<RS>(lane);
-  const int voff_l = v_lane_off<RS>(lane);
+  const int koff_l = k_lane_off<RSK>(lane);
+  const int voff_l = v_lane_off<RSV>(lane);
 
   for (int j = 0; j < ntiles; ++j) {
     const int j0 = j * BC;
     __syncthreads();
-    copy_tile_f32<D>(K + kvoff, j0, Nk, kt, ktl);
-    copy_tile_f32<D>(V + kvoff, j0, Nk, vt, vtl);
+    copy_tile_f32<D, C::SPR_K>(K + kvoff, j0, Nk, kt, ktl);
+    copy_tile_f32<D, C::SPR_V>(V + kvoff, j0, Nk, vt, vtl);
     __syncthreads();
     if (!live || j0 > klast_w) continue;  // wave-uniform: nothing visible to this wave
 
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(const float* __restrict
     for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const int off = koff_l + kb * 32 * RS + ds * 32;
+        const int off = koff_l + kb * 32 * RSK + ds * 32;
         const bf16x8 kh = lds_b128(kt + off), kl = lds_b128(ktl + off);
         s[kb] = mfma(kh, qf[ds], s[kb]);
         s[kb] = mfma(kh, qlo[ds], s[kb]);
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(const float* __restrict
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int ps = 0; ps < PS; ++ps) {
-        const bf16x8 vh = v_frag<RS>(vt + voff_l, ps, db), vl = v_frag<RS>(vtl + voff_l, ps, db);
+        const bf16x8 vh = v_frag<RSV>(vt + voff_l, ps, db), vl = v_frag<RSV>(vtl + voff_l, ps, db);
         o[db] = mfma(vh, ph[ps], o[db]);
         o[db] = mfma(vh, pl[ps], o[db]);
         o[db] = mfma(vl, ph[ps], o[db]);
@@ -337,14 +344,7 @@ __global__ __launch_bounds__(256) void fa_fwd_f32_kernel(const float* __restrict
     LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
 }
 
-// ---------------------------------------------------------------- pipelined bf16 kernel
-// The bf16 path software-pipelines each wave: while the exponentials of
-// key tile j are computed on the VALU, the MFMAs of S^T for tile j+1 are
-// already in flight (the softmax / matrix-product overlap FlashAttention-3
-// obtains with ping-pong warpgroups, "FlashAttention-3 — 闪电注意力-3",
-// section on asynchrony).  K therefore runs one tile ahead of V in LDS:
-// iteration j reads K_{j+1} and V_j and refills the slots of K_j and V_{j-1}
-// with K_{j+2} and V_{j+1}.
+// ---------------------------------------------------------------- bf16 kernel helpers
 
 // Scores of one wave for one key tile (S^T blocks [kb][qb]).
 template <int D>
@@ -366,7 +366,7 @@ __device__ __forceinline__ void scores_full(Scores<D>& s, LDS_AS const char* kla
   for (int ds = 0; ds < C::DS; ++ds)
 #pragma unroll
     for (int kb = 0; kb < C::KB; ++kb) {
-      const bf16x8 kf = lds_b128(klane + kb * 32 * C::RS + ds * 32);
+      const bf16x8 kf = lds_b128(klane + kb * 32 * C::RSK + ds * 32);
 #pragma unroll
       for (int qb = 0; qb < C::QB; ++qb) s.v[kb][qb] = mfma(kf, qf[qb][ds], s.v[kb][qb]);
     }
@@ -389,40 +389,55 @@ __device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int q0w, int N
     }
 }
 
-// NST: slots per K and V ring in LDS.  PP (ping-pong, 8 waves): the upper
-// half of the workgroup runs its loop half an iteration behind, so on each
-// SIMD one wave is in its exponential-heavy phase while the other is in its
-// MFMA-heavy P V phase.
-template <int D, bool CAUSAL, int NW, int NST, bool PP>
+// ---------------------------------------------------------------- bf16 kernel
+// Iteration j of a wave interleaves three independent streams, one MFMA per
+// chunk: the MFMAs of S_{j+1} = K_{j+1} Q^T, the exponentials of tile j, and
+// the MFMAs of O^T += V_{j-1}^T P_{j-1}^T.  Every MFMA thus carries the same
+// share of softmax work (one score per MFMA at d = 128), rather than all of
+// it next to the S MFMAs and none next to the P V MFMAs.
+// The lazy rescale of tile j runs after P_{j-1} V_{j-1} has entered O, so O
+// and P_j always refer to the same reference maximum.
+//
+// LDS ring (two slots each): iteration j reads K_{j+1} and V_{j-1} and
+// refills the slots of K_j and V_{j-2} with K_{j+2} and V_j; every copy has
+// one iteration to land before the barrier that publishes it.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                         __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c) {
   using C = Cfg<D, false>;
-  constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RS = C::RS;
+  constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RSK = C::RSK, RSV = C::RSV;
   static_assert(C::QB == 1, "one 32-row query block per wave");
-  constexpr int NMF = DS * KB;   // MFMAs of one S^T tile
-  constexpr int NPV = DB * PS;   // MFMAs of one P V product
-  constexpr int SPS = KB * 16 / NMF;  // exponentials per S^T MFMA
-  static_assert(SPS * NMF == KB * 16, "score / MFMA interleave");
-  constexpr int KPF = PP ? 3 : 4;  // K fragment reads in flight ahead of the S^T MFMAs
-  constexpr int VPF = 3;         // V fragments in flight ahead of the P V MFMAs
-  static_assert(VPF <= NMF && KPF <= NMF, "prefetch depth");
-  // Iteration j copies K_{j+KD} and V_{j+VD}.  It reads K_{j+1} and V_j (and,
-  // in the late half of a ping-pong workgroup, V_{j-1}); a copy overwrites
-  // the slot of a tile read two barriers ago at the latest.  The copies of
-  // the last WIF iterations may still be in flight when an iteration starts.
-  static_assert(!PP || (NW == 8 && NST == 4), "ping-pong layout");
-  static_assert(NST == 2 || NST == 4, "ring size");
-  constexpr int KD = PP ? NST - 1 : NST;
-  constexpr int VD = PP ? NST - 2 : NST - 1;
-  constexpr int WIF = (KD - 1 < VD ? KD - 1 : VD) - 1;
-  constexpr int MI = CopyPlan<D, NW>::MI;
-  __shared__ __attribute__((aligned(1024))) char smem_[2 * NST * C::TILE + 1024];
-  LDS_AS char* const smem = (LDS_AS char*)smem_;
-  // LDS: K slots 0..NST-1, V slots 0..NST-1, spare block
-  auto kslot = [&](int i) { return smem + (i & (NST - 1)) * C::TILE; };
-  auto vslot = [&](int i) { return smem + (NST + (i & (NST - 1))) * C::TILE; };
-  LDS_AS char* const spare = smem + 2 * NST * C::TILE;
+  constexpr int NMF = DS * KB;        // MFMAs of one S^T tile
+  constexpr int NPV = DB * PS;        // MFMAs of one P V product
+  static_assert(NMF == NPV, "S and P V streams alternate");
+  constexpr int NSC = KB * 16;        // scores per lane per tile
+  constexpr int NCH = NMF + NPV;      // chunks of the fused phase
+  constexpr int KPF = 2, VPF = 2;     // LDS fragment reads in flight per stream
+  using CopyK = CopyPlan<D, NW, C::SPR_K>;
+  using CopyV = CopyPlan<D, NW, C::SPR_V>;
+  // Ring slot t & 1 of tile t.  Every slot is an array of its own: a copy
+  // into one slot then provably cannot alias the reads of the other, and the
+  // compiler does not wait for the copies in flight before each transposed
+  // V read (it does for reads of the same array).
+  __shared__ __attribute__((aligned(1024))) char lk0_[C::TILE_K];
+  __shared__ __attribute__((aligned(1024))) char lk1_[C::TILE_K];
+  __shared__ __attribute__((aligned(1024))) char lv0_[C::TILE_V];
+  __shared__ __attribute__((aligned(1024))) char lv1_[C::TILE_V];
+  __shared__ __attribute__((aligned(1024))) char lsp_[1024];
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto kslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lk0_ : lk1_); };
+  auto vslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lv0_ : lv1_); };
+  LDS_AS char* const spare = (LDS_AS char*)lsp_;
 
   const fa_work_t w = fa_decode(p, blockIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -440,7 +455,6 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   const size_t qoff = (size_t)(w.b * p.Hq + hq) * Nq * D;
   const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
 
-  // resident Q fragments (B operand of S^T = K Q^T): column = query, k = d
   bf16x8 qf[1][DS];
   {
     const int qrow = min(q0w + (lane & 31), Nq - 1);
@@ -453,104 +467,112 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
   float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
 
-  const int koff_l = k_lane_off<RS>(lane);
-  const int voff_l = v_lane_off<RS>(lane);
-  const __bf16* kbase = K + kvoff;
-  const __bf16* vbase = V + kvoff;
-  CopyPlan<D, NW> cp;
-  cp.init(wave, lane);
-
-  // Copy of K_t / V_t into its ring slot.  Every copy is issued, also past
-  // the workgroup's last tile (then out of range: it reads nothing and
-  // writes zeros into a slot whose tile is no longer used), so each wave has
-  // a fixed number of copies in flight and vmcnt can count them.
-  const __amdgpu_buffer_rsrc_t kres = cp.rsrc(kbase, Nk), vres = cp.rsrc(vbase, Nk);
+  const int koff_l = k_lane_off<RSK>(lane);
+  const int voff_l = v_lane_off<RSV>(lane);
+  CopyK cpk;
+  CopyV cpv;
+  cpk.init(wave, lane);
+  cpv.init(wave, lane);
+  const __amdgpu_buffer_rsrc_t kres = CopyK::rsrc(K + kvoff, Nk), vres = CopyV::rsrc(V + kvoff, Nk);
   const int kv_bytes = Nk * (D * 2);
   auto tile_off = [&](int t) { return t < nt ? t * (BC * D * 2) : kv_bytes; };
-  // (the slot offset passes through an opaque scalar move so that the
-  // destinations are formed at each copy instead of being kept in SGPRs)
-  auto opaque = [](int x) {
-    asm volatile("" : "+s"(x));
-    return x;
+  // Copy instruction i of this wave in iteration j (of parity par): K_{j+2}
+  // into K slot par, then V_j into V slot par.  The instructions are spread
+  // over the chunks of the iteration rather than issued in one burst.
+  constexpr int NCP = CopyK::MI + CopyV::MI;
+  auto copy_one = [&](int j, auto par, int i) {
+    if (i < CopyK::MI) cpk.issue_one(kres, tile_off(j + 2), kslot(par), spare, wave, i);
+    else cpv.issue_one(vres, tile_off(j), vslot(par), spare, wave, i - CopyK::MI);
   };
-  auto copy_k = [&](int t) {
-    cp.issue_all(kres, tile_off(t), smem + opaque((t & (NST - 1)) * C::TILE), spare, wave);
+  auto copy_all = [&](int j, auto par) {
+    cpk.issue_all(kres, tile_off(j + 2), kslot(par), spare, wave);
+    cpv.issue_all(vres, tile_off(j), vslot(par), spare, wave);
   };
-  auto copy_v = [&](int t) {
-    cp.issue_all(vres, tile_off(t), smem + opaque((NST + (t & (NST - 1))) * C::TILE), spare, wave);
-  };
-  // prologue: the copies iterations -KD..-1 would have made; then S_0
-#pragma unroll
-  for (int i = -(KD > VD ? KD : VD); i < 0; ++i) {
-    if (i + KD >= 0) copy_k(i + KD);
-    if (i + VD >= 0) copy_v(i + VD);
-  }
-  vm_wait<WIF * 2 * MI>();
+
+  // prologue: K_0, K_1, zeros into V slot 1, which iteration 0 reads (its
+  // P V product then adds 0 x 0); S_0
+  cpk.issue_all(kres, tile_off(0), kslot(P0{}), spare, wave);
+  cpk.issue_all(kres, tile_off(1), kslot(P1{}), spare, wave);
+  cpv.issue_all(vres, kv_bytes, vslot(P1{}), spare, wave);
+  vm_wait<0>();
   __syncthreads();
   Scores<D> sa, sb;
-  if (ntw > 0) scores_full<D>(sa, kslot(0) + koff_l, qf);
+  if (ntw > 0) scores_full<D>(sa, kslot(P0{}) + koff_l, qf);
 
-  // top of iteration j: wait for this wave's old copies, make every wave's
-  // copies visible, refill the slots read two barriers ago
-  auto top = [&](int j) {
-    vm_wait<WIF * 2 * MI>();
-    __syncthreads();
-    copy_k(j + KD);
-    copy_v(j + VD);
+  // probabilities of one tile, bf16 pairs packed per dword (B operand of P V)
+  struct Probs {
+    u32x4 v[PS];
+  };
+  Probs pa, pb;
+#pragma unroll
+  for (int ps = 0; ps < PS; ++ps) pb.v[ps] = (u32x4){0u, 0u, 0u, 0u};
+
+  // score sc = (kb, i) of s: exponential against mu, row-sum part, packed
+  // into the P dword of its pair (the odd member of a pair writes it)
+  auto score = [&](const Scores<D>& s, Probs& pf, int sc, float mu, float& part0, float& part1, float& even) {
+    const int skb = sc / 16, si = sc % 16;
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s.v[skb][0][si], c, -mu));
+    if (sc & 1) {
+      part1 += pv;
+      pf.v[skb * 2 + si / 8][(si % 8) / 2] = pack_bf16(even, pv);
+    } else {
+      part0 += pv;
+      even = pv;
+    }
   };
 
-  // Softmax phase of tile j: the scores of tile j are in s; the scores of
-  // tile j+1 are produced into sn (K_{j+1} is in LDS), interleaved with the
-  // exponentials P_j = 2^(S_j c - m_ref) into pf.
-  auto softmax_phase = [&](int j, Scores<D>& s, Scores<D>& sn, bf16x8 (&pf)[PS], bf16x8 (&vbuf)[VPF]) {
+  // the exponentials of tile j (scores in s, probabilities into pf), the
+  // MFMAs of S_{j+1} (into sn) and of O += V_{j-1} P_{j-1} (pprev).  At
+  // j = ntw (the wave's last P V product) tile j lies past every key the
+  // wave's queries see, so the mask turns all its scores into -inf and its
+  // exponentials contribute nothing.
+  // (par = j & 1: K_{j+1} and V_{j-1} are read from the slots 1 - par.)
+  auto fused = [&](int j, auto par, Scores<D>& s, Scores<D>& sn, Probs& pf, const Probs& pprev) {
+    using other = std::integral_constant<int, 1 - decltype(par)::value>;
     const int j0 = j * BC;
-    LDS_AS const char* knext = kslot(j + 1) + koff_l;
-    LDS_AS const char* vlane = vslot(j) + voff_l;
-    // the first K fragments of S_{j+1} load while the mask is applied
-    bf16x8 kbuf[KPF];
+    LDS_AS const char* knext = kslot(other{}) + koff_l;
+    LDS_AS const char* vprev = vslot(other{}) + voff_l;
+    bf16x8 kbuf[KPF], vbuf[VPF];
 #pragma unroll
-    for (int t = 0; t < KPF; ++t) kbuf[t] = lds_b128(knext + (t % KB) * 32 * RS + (t / KB) * 32);
-
+    for (int t = 0; t < KPF; ++t) kbuf[t] = lds_b128(knext + (t % KB) * 32 * RSK + (t / KB) * 32);
+#pragma unroll
+    for (int t = 0; t < VPF; ++t) vbuf[t] = v_frag<RSV>(vprev, t / DB, t % DB);
     if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q0w, Nq, Nk, lane);
 
-    // Chunk t issues MFMA t of S_{j+1}, the LDS read of the K fragment KPF
-    // chunks ahead, and SPS exponentials taken against the current reference
-    // maximum m_ref (fast path); sched_barrier fences keep the chunks in
-    // this order.  S_{j+1} is computed unconditionally (on a wave's last tile
-    // the K slot holds stale data and the result is discarded), so the whole
-    // phase is one branch-free block.  The last chunks also start the V
-    // fragment reads of P V.
     float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-    float part0 = 0.f, part1 = 0.f;
+    float part0 = 0.f, part1 = 0.f, even = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sn.v[kb][0] = (f32x16){};
 #pragma unroll
-    for (int t = 0; t < NMF; ++t) {
-      const int ds = t / KB, kb = t % KB;
-      sn.v[kb][0] = mfma(kbuf[t % KPF], qf[0][ds], sn.v[kb][0]);
-      if (t + KPF < NMF) kbuf[t % KPF] = lds_b128(knext + ((t + KPF) % KB) * 32 * RS + ((t + KPF) / KB) * 32);
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int m = ch / 2;
+      if (ch % 2 == 0) {
+        // S_{j+1}: MFMA m, reading the K fragment KPF MFMAs ahead
+        const int ds = m / KB, kb = m % KB;
+        sn.v[kb][0] = mfma(kbuf[m % KPF], qf[0][ds], sn.v[kb][0]);
+        if (m + KPF < NMF) kbuf[m % KPF] = lds_b128(knext + ((m + KPF) % KB) * 32 * RSK + ((m + KPF) / KB) * 32);
+      } else {
+        // O += V_{j-1} P_{j-1}: MFMA m (k-step m / DB, d-block m % DB)
+        const int ps = m / DB, db = m % DB;
+        o[db] = mfma(vbuf[m % VPF], __builtin_bit_cast(bf16x8, pprev.v[ps]), o[db]);
+        if (m + VPF < NPV) vbuf[m % VPF] = v_frag<RSV>(vprev, (m + VPF) / DB, (m + VPF) % DB);
+      }
+      // scores [ch * NSC / NCH, (ch + 1) * NSC / NCH)
 #pragma unroll
-      for (int u = 0; u < SPS; ++u) {
-        const int sc = t * SPS + u;  // score index [kb][i]
-        const int skb = sc / 16, si = sc % 16;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s.v[skb][0][si], c, -mu));
-        if (sc & 1) part1 += pv;
-        else part0 += pv;
-        pf[skb * 2 + si / 8][si % 8] = (__bf16)pv;
-      }
-      if (!PP && t >= NMF - VPF) {
-        const int tv = t - (NMF - VPF);
-        vbuf[tv] = v_frag<RS>(vlane, tv / DB, tv % DB);
-      }
+      for (int sc = ch * NSC / NCH; sc < (ch + 1) * NSC / NCH; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      // copy instructions [ch * NCP / NCH, (ch + 1) * NCP / NCH): all NCP of them
+#pragma unroll
+      for (int i = ch * NCP / NCH; i < (ch + 1) * NCP / NCH; ++i) copy_one(j, par, i);
       __builtin_amdgcn_sched_barrier(0);
     }
     float part = part0 + part1;
 
     // slow path: if some probability may exceed 2^TAU (a lane's partial row
-    // sum does), or a row has no reference yet, form the row maximum,
-    // rescale O and l when it grew by more than TAU, and redo the
-    // exponentials.  Otherwise every probability is at most 2^TAU and the
-    // reference maximum stands, exactly as the max-first rule would decide.
+    // sum does), or a row has no reference yet, form the row maximum, rescale
+    // O (which already holds P_{j-1} V_{j-1}) and l when it grew by more than
+    // TAU, and redo the exponentials.  Otherwise every probability is at most
+    // 2^TAU and the reference maximum stands, exactly as the max-first rule
+    // would decide.
     if (__ballot(!(part <= TAU_EXP2) || m_ref == NEG_INF)) {
       float mx = NEG_INF;
 #pragma unroll
@@ -566,71 +588,34 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         m_ref = m_run;
       }
       mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-      part = 0.f;
+      part0 = part1 = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s.v[kb][0][i], c, -mu));
-          part += pv;
-          pf[kb * 2 + i / 8][i % 8] = (__bf16)pv;
-        }
+      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      part = part0 + part1;
     }
     lsum += part;
   };
 
-  // P V phase of tile j: O^T += V_j^T P_j^T.  MFMA t uses k-step t/DB and
-  // d-block t%DB (the accumulators rotate); the V fragment is read VPF MFMAs
-  // ahead (the first VPF are already in vbuf unless `fresh`).
-  auto pv_phase = [&](int j, const bf16x8 (&pf)[PS], bf16x8 (&vbuf)[VPF], bool fresh) {
-    LDS_AS const char* vlane = vslot(j) + voff_l;
-    if (fresh) {
-#pragma unroll
-      for (int t = 0; t < VPF; ++t) vbuf[t] = v_frag<RS>(vlane, t / DB, t % DB);
-    }
-#pragma unroll
-    for (int t = 0; t < NPV; ++t) {
-      const int ps = t / DB, db = t % DB;
-      o[db] = mfma(vbuf[t % VPF], pf[ps], o[db]);
-      if (t + VPF < NPV) vbuf[t % VPF] = v_frag<RS>(vlane, (t + VPF) / DB, (t + VPF) % DB);
-      __builtin_amdgcn_sched_barrier(0);
+  // one code path for every iteration a wave takes part in (j <= ntw);
+  // waves past their last tile only keep the barriers and copies going
+  auto iteration = [&](int j, auto par, Scores<D>& s, Scores<D>& sn, Probs& pf, Probs& pprev) {
+    vm_wait<0>();
+    __syncthreads();
+    if (j <= ntw && ntw > 0) {
+      fused(j, par, s, sn, pf, pprev);
+    } else {
+      copy_all(j, par);
     }
   };
-
-  const bool late = PP && wave >= NW / 2;  // wave-uniform
-  if (!late) {
-    // two score buffers alternate (unrolled by two): no copies between tiles
-    for (int j = 0; j < nt; j += 2) {
-      top(j);
-      if (j < ntw) {
-        bf16x8 pf[PS], vbuf[VPF];
-        softmax_phase(j, sa, sb, pf, vbuf);
-        pv_phase(j, pf, vbuf, PP);
-      }
-      if (j + 1 < nt) {
-        top(j + 1);
-        if (j + 1 < ntw) {
-          bf16x8 pf[PS], vbuf[VPF];
-          softmax_phase(j + 1, sb, sa, pf, vbuf);
-          pv_phase(j + 1, pf, vbuf, PP);
-        }
-      }
-    }
-  } else {
-    // late half: P V of the previous tile first, then the softmax phase
-    bf16x8 pf[PS], vbuf[VPF];
-    for (int j = 0; j < nt; j += 2) {
-      top(j);
-      if (j >= 1 && j - 1 < ntw) pv_phase(j - 1, pf, vbuf, true);
-      if (j < ntw) softmax_phase(j, sa, sb, pf, vbuf);
-      if (j + 1 < nt) {
-        top(j + 1);
-        if (j < ntw) pv_phase(j, pf, vbuf, true);
-        if (j + 1 < ntw) softmax_phase(j + 1, sb, sa, pf, vbuf);
-      }
-    }
-    if (nt >= 1 && nt - 1 < ntw) pv_phase(nt - 1, pf, vbuf, true);
+  // nt + 1 iterations (the last one only adds P_{nt-1} V_{nt-1}); score and
+  // probability buffers alternate (unrolled by two)
+  for (int j = 0; j <= nt; j += 2) {
+    iteration(j, P0{}, sa, sb, pa, pb);
+    if (j + 1 <= nt) iteration(j + 1, P1{}, sb, sa, pb, pa);
   }
+  // the last copies (zeros past the final tile) land before the workgroup's
+  // LDS can pass to another workgroup
+  vm_wait<0>();
 
   // ---- epilogue: O / l, LSE = ln2 * (m_ref + log2 l)
   if (!live) return;
@@ -660,20 +645,18 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   template __global__ void fa_fwd_f32_kernel<DD, CC>(const float* __restrict__, const float* __restrict__,       \
                                                      const float* __restrict__, float* __restrict__,             \
                                                      float* __restrict__, fa_plan_t, float);
-#define FA_INST_BF16(DD, CC, NN, SS, PP)                                                                    \
-  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN, SS, PP>(                                           \
-      const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, __bf16* __restrict__, \
-      float* __restrict__, fa_plan_t, float);
 #define FA_F32_VARIANTS(X) X(64, false) X(64, true) X(128, false) X(128, true) X(256, false) X(256, true)
-// (head dim, causal, waves per workgroup, ring slots, ping-pong)
-#define FA_BF16_VARIANTS(X)                                                                                \
-  X(64, false, 1, 2, false) X(64, false, 2, 2, false) X(64, false, 4, 2, false)                             \
-  X(64, true, 1, 2, false) X(64, true, 2, 2, false) X(64, true, 4, 2, false)                                \
-  X(128, false, 1, 2, false) X(128, false, 2, 2, false) X(128, false, 4, 2, false) X(128, false, 8, 4, true) \
-  X(128, true, 1, 2, false) X(128, true, 2, 2, false) X(128, true, 4, 2, false) X(128, true, 8, 4, true)    \
-  X(256, false, 1, 2, false) X(256, false, 2, 2, false) X(256, false, 4, 2, false)                          \
-  X(256, true, 1, 2, false) X(256, true, 2, 2, false) X(256, true, 4, 2, false)
 FA_F32_VARIANTS(FA_INST_F32)
+#define FA_INST_BF16(DD, CC, NN)                                                                          \
+  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN>(const __bf16* __restrict__, const __bf16* __restrict__, \
+                                                          const __bf16* __restrict__, __bf16* __restrict__,     \
+                                                          float* __restrict__, fa_plan_t, float);
+// (head dim, causal, waves per workgroup)
+#define FA_BF16_VARIANTS(X)                                                                                \
+  X(64, false, 1) X(64, false, 2) X(64, false, 4) X(64, true, 1) X(64, true, 2) X(64, true, 4)              \
+  X(128, false, 1) X(128, false, 2) X(128, false, 4) X(128, false, 8)                                       \
+  X(128, true, 1) X(128, true, 2) X(128, true, 4) X(128, true, 8)                                           \
+  X(256, false, 1) X(256, false, 2) X(256, false, 4) X(256, true, 1) X(256, true, 2) X(256, true, 4)
 FA_BF16_VARIANTS(FA_INST_BF16)
 
 int queries_per_wave(int, int) { return 32; }
@@ -686,9 +669,9 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                        (const float*)k, (const float*)v, (float*)o, lse, p, c);                        \
     return hipGetLastError();                                                                           \
   }
-#define FA_CASE_BF16(DD, CC, NN, SS, PP)                                                                  \
+#define FA_CASE_BF16(DD, CC, NN)                                                                       \
   if (!f32 && d == DD && (p.causal != 0) == CC && p.nw == NN) {                                         \
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN, SS, PP>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream, \
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream,      \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c);   \
     return hipGetLastError();                                                                           \
   }

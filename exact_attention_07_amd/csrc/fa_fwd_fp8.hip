@@ -259,6 +259,9 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
     if (j + 1 < nt) step(j + 1, sb, sa);
   }
   (void)vslot;
+  // the last copies (zeros past the final tile) land before the workgroup's
+  // LDS can pass to another workgroup
+  vm_wait<0>();
 
   if (!live) return;
   const float lt = xhalf_sum(lsum);

@@ -148,3 +148,35 @@ def test_status_errors_raise(api):
     with pytest.raises(api.FaError) as e:
         api.fa_fwd(q, q, q, torch.empty_like(q), None, 0.1, False)
     assert e.value.status == 3        # head dimension 96
+
+
+# ---------------------------------------------------------------- large grids (eight-wave workgroups at d = 128)
+def _edge_rows(w, rng, n):
+    """Rows at the ends of query blocks, tails and random positions."""
+    rows = []
+    for i in (0, 31, 32, 63, 64, 127, 128, w.Nq // 2, w.Nq - 64, w.Nq - 2, w.Nq - 1):
+        if 0 <= i < w.Nq:
+            rows.append((int(rng.integers(w.B)), int(rng.integers(w.Hq)), i))
+    while len(rows) < n:
+        rows.append((int(rng.integers(w.B)), int(rng.integers(w.Hq)), int(rng.integers(w.Nq))))
+    return rows
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk", [(1999, 1999), (2000, 2500), (2047, 1100)])
+def test_large_grid_ragged(api, nq, nk, causal):
+    # >= 1024 workgroups of 8 waves: the launch configuration of the long-context workloads
+    w = gen.workload(2, 64, 16, nq, nk, 128, causal=causal)
+    x = gen.make_inputs(w, (nq, nk, int(causal)))
+    print(f"case: {w.name}", flush=True)
+    o, lse = _run(api, w, x)
+    rows = _edge_rows(w, np.random.default_rng(nq + nk), 48)
+    q, k, v = (to_f64(x[t], w.dtype) for t in "qkv")
+    o_ref, lse_ref = attention_rows_fp64(q, k, v, w.softmax_scale, w.causal, rows)
+    got_o = np.stack([o[b, h, i] for b, h, i in rows])
+    got_l = np.array([lse[b, h, i] for b, h, i in rows])
+    compare(got_o, got_l, o_ref, lse_ref, what=w.name)
+    assert np.isfinite(o).all()
+    if causal and nq > nk:
+        # queries that see no key (i + nk - nq < 0): O = 0, LSE = -inf
+        assert (o[:, :, : nq - nk] == 0).all() and np.isneginf(lse[:, :, : nq - nk]).all()
