@@ -15,6 +15,11 @@ Sources (the pages these functions restate):
     aligned, key j visible to query i iff j <= i + (Nk - Nq).
   * "FlashAttention-4震撼发布" (FlashAttention-2 list): MQA and GQA; query head h
     reads key/value head h // (Hq // Hkv).
+  * "FlashAttention (SV)", section "Online-beräkning av Softmax": softmax
+    statistics of separate key blocks combine exactly, given each block's
+    maximum and sum of exponentials.  attention_keys_fp64 and merge_fp64 use
+    this for attention split over key ranges (each part keeps its own
+    normalised output and log-sum-exp).
 
 Layouts: q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d]; outputs o [B, Hq, Nq, d]
 (v may have its own last dimension, which o then has)
@@ -179,3 +184,47 @@ def online_fp64(q, k, v, scale: float, causal: bool, bc: int, tau: float, group:
             o[b, h][live] = acc[live] / l[live][:, None]
             lse[b, h][live] = (m_ref[live] + np.log2(l[live])) / LOG2E
     return o, lse, (events, decisions)
+
+
+def attention_keys_fp64(q, k, v, scale: float, causal: bool, k0: int, k1: int):
+    """The definition over the keys [k0, k1) only, each key visible to a query
+    exactly when it is in the full problem: o [B, Hq, Nq, d] normalised by the
+    part's own sum, lse [B, Hq, Nq] of the part; a row that sees none of these
+    keys gets o = 0 and lse = -inf."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, HQ, NQ, _ = q.shape
+    _, HKV, NK, _ = k.shape
+    if not 0 <= k0 <= k1 <= NK:
+        raise ValueError("key range out of bounds")
+    o = np.zeros((B, HQ, NQ, v.shape[-1]), dtype=np.float64)
+    lse = np.full((B, HQ, NQ), -np.inf, dtype=np.float64)
+    vis = _visible(NQ, NK, causal)[:, k0:k1]
+    for b in range(B):
+        for h in range(HQ):
+            hk = kv_head_of(h, HQ, HKV)
+            s = scale * (q[b, h] @ k[b, hk, k0:k1].T)
+            p, m, l = _softmax_rows(s, vis)
+            live = l > 0
+            o[b, h][live] = (p[live] @ v[b, hk, k0:k1]) / l[live][:, None]
+            lse[b, h][live] = m[live] + np.log(l[live])
+    return o, lse
+
+
+def merge_fp64(o_parts, lse_parts):
+    """Combine attention over disjoint key sets: parts o_s (normalised by their
+    own sums) and lse_s, stacked on axis 0.  With L = ln sum_s exp(lse_s):
+    o = sum_s exp(lse_s - L) o_s and lse = L; rows where every part is -inf get
+    o = 0 and lse = -inf."""
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    w = np.exp(lse_parts - m_safe[None])          # -inf parts weigh 0
+    tot = w.sum(axis=0)
+    live = tot > 0
+    lse = np.where(live, m_safe + np.log(np.where(live, tot, 1.0)), -np.inf)
+    o = np.einsum("s...,s...d->...d", w, o_parts)
+    o = np.where(live[..., None], o / np.where(live, tot, 1.0)[..., None], 0.0)
+    return o, lse

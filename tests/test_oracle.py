@@ -13,7 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import attention_fp64, attention_rows_fp64, online_fp64, formats, fp8
+from oracle import attention_fp64, attention_keys_fp64, attention_rows_fp64, merge_fp64, online_fp64, formats, fp8
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
 
@@ -339,3 +339,52 @@ def test_prepare_layouts_and_product():
     approx = qd[0, 0] @ kd[0, 0].T
     assert np.abs(approx - exact).max() < 0.25 * np.abs(exact).max()
     assert np.abs(vd - v).max() <= np.abs(v).max() / 16
+
+
+# ---------------------------------------------------------------- attention split over key ranges
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk,cuts", [(7, 19, (0, 5, 6, 19)), (12, 12, (0, 4, 8, 12)), (20, 9, (0, 3, 9)),
+                                        (1, 33, (0, 11, 22, 33)), (5, 40, (0, 40))])
+def test_merge_of_key_ranges_equals_full_attention(causal, nq, nk, cuts):
+    rng = np.random.default_rng(nq * 100 + nk)
+    q = rng.standard_normal((2, 4, nq, 8)) * 2
+    k = rng.standard_normal((2, 2, nk, 8))
+    v = rng.standard_normal((2, 2, nk, 5))
+    o, lse = attention_fp64(q, k, v, 0.4, causal)
+    parts = [attention_keys_fp64(q, k, v, 0.4, causal, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    om, lm = merge_fp64([p[0] for p in parts], [p[1] for p in parts])
+    np.testing.assert_array_equal(np.isneginf(lm), np.isneginf(lse))
+    fin = np.isfinite(lse)
+    np.testing.assert_allclose(lm[fin], lse[fin], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(om, o, rtol=0, atol=1e-12)
+    # the merge does not depend on the order of the parts
+    om2, lm2 = merge_fp64([p[0] for p in parts[::-1]], [p[1] for p in parts[::-1]])
+    np.testing.assert_allclose(om2, om, atol=1e-13)
+    np.testing.assert_array_equal(np.isneginf(lm2), np.isneginf(lm))
+
+
+def test_merge_closed_forms():
+    o1 = np.array([[1.0, 2.0]]); o2 = np.array([[3.0, -2.0]])
+    # equal weights: the mean, lse + ln 2
+    o, l = merge_fp64([o1, o2], [np.array([0.5]), np.array([0.5])])
+    np.testing.assert_allclose(o, [[2.0, 0.0]], atol=1e-15)
+    np.testing.assert_allclose(l, [0.5 + math.log(2.0)], atol=1e-15)
+    # weights e^1 : e^0
+    o, l = merge_fp64([o1, o2], [np.array([1.0]), np.array([0.0])])
+    w = math.e / (math.e + 1.0)
+    np.testing.assert_allclose(o, w * o1 + (1 - w) * o2, atol=1e-15)
+    np.testing.assert_allclose(l, [math.log(math.e + 1.0)], atol=1e-15)
+    # a part that saw no key does not count; all empty -> 0, -inf
+    o, l = merge_fp64([o1, np.zeros_like(o1)], [np.array([0.25]), np.array([-np.inf])])
+    np.testing.assert_allclose(o, o1, atol=1e-15)
+    np.testing.assert_allclose(l, [0.25], atol=1e-15)
+    o, l = merge_fp64([np.zeros_like(o1)] * 3, [np.array([-np.inf])] * 3)
+    assert (o == 0).all() and np.isneginf(l).all()
+
+
+def test_key_range_single_key_is_its_value_row():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 4, 6)); k = rng.standard_normal((1, 1, 10, 6)); v = rng.standard_normal((1, 1, 10, 6))
+    o, l = attention_keys_fp64(q, k, v, 0.3, False, 7, 8)
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0, 7], (4, 6)), atol=1e-15)
+    np.testing.assert_allclose(l[0, 0], 0.3 * (q[0, 0] @ k[0, 0, 7]), atol=1e-14)
