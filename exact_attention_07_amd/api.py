@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_GQA_RATIO",
-             5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_HIP", 8: "FA_ERR_FLAG"}
+             5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_HIP", 8: "FA_ERR_FLAG", 9: "FA_ERR_WORKSPACE"}
 
 _lib = None
 
@@ -44,6 +44,10 @@ def lib() -> ctypes.CDLL:
     L.fa_fp8_prepare.restype = ctypes.c_int
     L.fa_fwd_fp8.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp]
     L.fa_fwd_fp8.restype = ctypes.c_int
+    L.fa_fwd_splitkv.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, vp, ctypes.c_size_t, vp]
+    L.fa_fwd_splitkv.restype = ctypes.c_int
+    L.fa_fwd_splitkv_workspace_size.argtypes = [i] * 8
+    L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_abi_version.argtypes = []
@@ -191,3 +195,40 @@ def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None, sig
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
     fa_fwd_fp8(q8, k8, v8t, descale, o, lse, scale, causal, stream)
     return o, lse, {"q8": q8, "k8": k8, "v8t": v8t, "descale": descale}
+
+
+def splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal: bool, nsplit: int = 0) -> int:
+    """Bytes of workspace fa_fwd_splitkv needs for these arguments (0: none)."""
+    return int(lib().fa_fwd_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), nsplit))
+
+
+def fa_fwd_splitkv(q, k, v, o, lse, scale: float, causal: bool, nsplit: int = 0, workspace=None, stream=None) -> None:
+    """bf16 forward pass with the keys split into ranges (partials merged on the GPU)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v, o, lse)
+    for t in (q, k, v, o):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("fa_fwd_splitkv takes bfloat16 q, k, v, o")
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d, float(scale),
+                                int(bool(causal)), int(nsplit), _ptr(workspace), nbytes, _stream(stream)),
+           "fa_fwd_splitkv")
+
+
+def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None, nsplit: int = 0, stream=None):
+    """Allocate o, lse and the workspace, run fa_fwd_splitkv, return (o, lse)."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    nbytes = splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal, nsplit)
+    ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=q.device) if nbytes else None
+    fa_fwd_splitkv(q, k, v, o, lse, scale, causal, nsplit, ws, stream)
+    return o, lse

@@ -53,7 +53,7 @@ fa_status forward(const void* q, const void* k, const void* v, void* o, float* l
   const fa_plan_t p = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, f32 ? KIND_F32 : KIND_BF16);
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
   const float c = (float)((double)scale * LOG2E);
-  hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, (hipStream_t)stream);
+  hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, nullptr, nullptr, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -65,6 +65,38 @@ fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, in
   if (kind == KIND_F32) return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4);
   const int max_nw = (kind == KIND_BF16 && d == 128) ? 8 : 4;
   return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS, max_nw);
+}
+
+// Key-split plan of the bf16 path.  Few query rows (Nq <= 32): one workgroup
+// holds all query heads of a GQA group (up to the wave limit), so each K/V
+// tile is read once for all of them.  Then the keys are split into ranges
+// until the grid has MIN_WORKGROUPS workgroups (nsplit_req = 0), or into
+// nsplit_req ranges of equal tile counts (the last may be shorter; fewer
+// ranges result when nsplit_req does not divide the tiles evenly).
+fa_plan_t plan_splitkv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int nsplit_req) {
+  const int qpw = fa::queries_per_wave(d, 0);
+  fa_plan_t base;
+  if (Nq <= qpw) {
+    const int max_nw = d == 128 ? 8 : 4;
+    int nw = 1;
+    while (nw * 2 <= max_nw && (Hq / Hkv) % (nw * 2) == 0) nw *= 2;
+    base = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, nw);
+  } else {
+    base = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, KIND_BF16);
+  }
+  const long long tiles = ((long long)Nk + 63) / 64;
+  long long want = nsplit_req;
+  if (want == 0) want = base.nwg >= MIN_WORKGROUPS ? 1 : (MIN_WORKGROUPS + base.nwg - 1) / base.nwg;
+  if (want > tiles) want = tiles;
+  if (want <= 1) return base;
+  const int tps = (int)((tiles + want - 1) / want);
+  return fa_split_plan(base, tps, 64);
+}
+
+size_t splitkv_workspace_bytes(const fa_plan_t& p, int d) {
+  if (p.nsplit <= 1) return 0;
+  const size_t rows = (size_t)p.B * p.Hq * p.Nq;
+  return (size_t)p.nsplit * rows * (size_t)(d + 1) * sizeof(float);
 }
 
 }  // namespace
@@ -84,6 +116,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_SCALE: return "scale must be finite and > 0";
     case FA_ERR_HIP: return "HIP launch failed";
     case FA_ERR_FLAG: return "causal must be 0 or 1";
+    case FA_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
   }
   return "unknown status";
 }
@@ -127,6 +160,35 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const floa
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
   const hipError_t e =
       fa::launch_fwd_fp8(q8, k8, v8t, descale, o, lse, p, d, (float)((double)scale * LOG2E), (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int nsplit) {
+  if (validate_shape(B, Hq, Hkv, Nq, Nk, d) != FA_OK || nsplit < 0 || (causal != 0 && causal != 1)) return 0;
+  return splitkv_workspace_bytes(plan_splitkv(B, Hq, Hkv, Nq, Nk, d, causal, nsplit), d);
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv,
+                         int Nq, int Nk, int d, float scale, int causal, int nsplit, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  fa_status st = validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (nsplit < 0) return FA_ERR_SHAPE;
+  const fa_plan_t p = plan_splitkv(B, Hq, Hkv, Nq, Nk, d, causal, nsplit);
+  if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const float c = (float)((double)scale * LOG2E);
+  if (p.nsplit <= 1) {
+    const hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, 0, nullptr, nullptr, (hipStream_t)stream);
+    return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  const size_t need = splitkv_workspace_bytes(p, d);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  const long long rows = (long long)B * Hq * Nq;
+  if (rows > 0x7fffffffLL) return FA_ERR_SHAPE;
+  float* ows = (float*)workspace;
+  float* lws = ows + (size_t)p.nsplit * rows * d;
+  hipError_t e = fa::launch_fwd(q, k, v, nullptr, nullptr, p, d, c, 0, ows, lws, (hipStream_t)stream);
+  if (e == hipSuccess) e = fa::launch_merge(ows, lws, o, lse, p.nsplit, rows, d, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -375,14 +375,15 @@ __device__ __forceinline__ void scores_full(Scores<D>& s, LDS_AS const char* kla
 // Mask keys past the visible range of each query (tiles that cross the
 // causal diagonal or the end of the keys only).
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int q0w, int Nq, int Nk, int lane) {
+__device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int q0w, int Nq, int Nk, int kend, int lane) {
   using C = Cfg<D, false>;
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
       const int query = q0w + qb * 32 + (lane & 31);
-      const int kmax = (CAUSAL ? min(Nk - 1, query + Nk - Nq) : Nk - 1) - j0 - kb * 32 - (lane >> 5) * 4;
+      const int klim = min(kend, CAUSAL ? min(Nk, query + Nk - Nq + 1) : Nk);  // keys < klim are visible
+      const int kmax = klim - 1 - j0 - kb * 32 - (lane >> 5) * 4;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
         if ((i >> 2) * 8 + (i & 3) > kmax) s.v[kb][qb][i] = NEG_INF;
@@ -412,7 +413,8 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                        __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c) {
+                        __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c,
+                        float* __restrict__ OWS, float* __restrict__ LWS) {
   using C = Cfg<D, false>;
   constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RSK = C::RSK, RSV = C::RSV;
   static_assert(C::QB == 1, "one 32-row query block per wave");
@@ -445,12 +447,17 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   const int q0w = w.qpos0 + (wave / p.hw) * 32;
   const int Nq = p.Nq, Nk = p.Nk;
   const int nt = fa_num_kv_tiles(p, w.qpos0, BC);
+  // key tiles [t0, t1) of this workgroup's range (all of them without a split)
+  int t0, t1;
+  fa_split_tiles(p, w.split, nt, t0, t1);
+  const int kend = t1 * BC;  // keys past the range are masked like invisible ones
 
   const bool live = q0w < Nq;
   const int qlast_w = min(Nq - 1, q0w + 31);
   const int klast_w = CAUSAL ? min(Nk - 1, qlast_w + Nk - Nq) : Nk - 1;
-  const int kfull_w = CAUSAL ? min(Nk - 1, q0w + Nk - Nq) : Nk - 1;
-  const int ntw = (live && klast_w >= 0) ? min(nt, klast_w / BC + 1) : 0;  // tiles this wave computes
+  const int kfull_w = min(kend - 1, CAUSAL ? min(Nk - 1, q0w + Nk - Nq) : Nk - 1);
+  // tiles of the range this wave computes (t0 .. t0 + ntw - 1)
+  const int ntw = (live && klast_w >= 0) ? max(0, min(t1, klast_w / BC + 1) - t0) : 0;
 
   const size_t qoff = (size_t)(w.b * p.Hq + hq) * Nq * D;
   const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
@@ -475,7 +482,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   cpv.init(wave, lane);
   const __amdgpu_buffer_rsrc_t kres = CopyK::rsrc(K + kvoff, Nk), vres = CopyV::rsrc(V + kvoff, Nk);
   const int kv_bytes = Nk * (D * 2);
-  auto tile_off = [&](int t) { return t < nt ? t * (BC * D * 2) : kv_bytes; };
+  auto tile_off = [&](int t) { return t < t1 ? t * (BC * D * 2) : kv_bytes; };
   // Copy instruction i of this wave in iteration j (of parity par): K_{j+2}
   // into K slot par, then V_j into V slot par.  The instructions are spread
   // over the chunks of the iteration rather than issued in one burst.
@@ -489,10 +496,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     cpv.issue_all(vres, tile_off(j), vslot(par), spare, wave);
   };
 
-  // prologue: K_0, K_1, zeros into V slot 1, which iteration 0 reads (its
-  // P V product then adds 0 x 0); S_0
-  cpk.issue_all(kres, tile_off(0), kslot(P0{}), spare, wave);
-  cpk.issue_all(kres, tile_off(1), kslot(P1{}), spare, wave);
+  // prologue: K_{t0}, K_{t0+1}, zeros into V slot 1, which iteration 0 reads
+  // (its P V product then adds 0 x 0); S_{t0}
+  cpk.issue_all(kres, tile_off(t0), kslot(P0{}), spare, wave);
+  cpk.issue_all(kres, tile_off(t0 + 1), kslot(P1{}), spare, wave);
   cpv.issue_all(vres, kv_bytes, vslot(P1{}), spare, wave);
   vm_wait<0>();
   __syncthreads();
@@ -523,9 +530,9 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
   // the exponentials of tile j (scores in s, probabilities into pf), the
   // MFMAs of S_{j+1} (into sn) and of O += V_{j-1} P_{j-1} (pprev).  At
-  // j = ntw (the wave's last P V product) tile j lies past every key the
-  // wave's queries see, so the mask turns all its scores into -inf and its
-  // exponentials contribute nothing.
+  // j = t0 + ntw (the wave's last P V product) tile j lies past every key
+  // the wave's queries see in this range, so the mask turns all its scores
+  // into -inf and its exponentials contribute nothing.
   // (par = j & 1: K_{j+1} and V_{j-1} are read from the slots 1 - par.)
   auto fused = [&](int j, auto par, Scores<D>& s, Scores<D>& sn, Probs& pf, const Probs& pprev) {
     using other = std::integral_constant<int, 1 - decltype(par)::value>;
@@ -537,7 +544,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     for (int t = 0; t < KPF; ++t) kbuf[t] = lds_b128(knext + (t % KB) * 32 * RSK + (t / KB) * 32);
 #pragma unroll
     for (int t = 0; t < VPF; ++t) vbuf[t] = v_frag<RSV>(vprev, t / DB, t % DB);
-    if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q0w, Nq, Nk, lane);
+    if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q0w, Nq, Nk, kend, lane);
 
     float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
     float part0 = 0.f, part1 = 0.f, even = 0.f;
@@ -598,31 +605,50 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
   // one code path for every iteration a wave takes part in (j <= ntw);
   // waves past their last tile only keep the barriers and copies going
-  auto iteration = [&](int j, auto par, Scores<D>& s, Scores<D>& sn, Probs& pf, Probs& pprev) {
+  // iteration i of the range handles tile j = t0 + i
+  auto iteration = [&](int i, auto par, Scores<D>& s, Scores<D>& sn, Probs& pf, Probs& pprev) {
+    const int j = t0 + i;
     vm_wait<0>();
     __syncthreads();
-    if (j <= ntw && ntw > 0) {
+    if (i <= ntw && ntw > 0) {
       fused(j, par, s, sn, pf, pprev);
     } else {
       copy_all(j, par);
     }
   };
-  // nt + 1 iterations (the last one only adds P_{nt-1} V_{nt-1}); score and
-  // probability buffers alternate (unrolled by two)
-  for (int j = 0; j <= nt; j += 2) {
-    iteration(j, P0{}, sa, sb, pa, pb);
-    if (j + 1 <= nt) iteration(j + 1, P1{}, sb, sa, pb, pa);
+  // t1 - t0 + 1 iterations (the last one only adds P V of the range's last
+  // tile); score and probability buffers alternate (unrolled by two)
+  const int n = t1 - t0;
+  for (int i = 0; i <= n; i += 2) {
+    iteration(i, P0{}, sa, sb, pa, pb);
+    if (i + 1 <= n) iteration(i + 1, P1{}, sb, sa, pb, pa);
   }
   // the last copies (zeros past the final tile) land before the workgroup's
   // LDS can pass to another workgroup
   vm_wait<0>();
 
-  // ---- epilogue: O / l, LSE = ln2 * (m_ref + log2 l)
+  // ---- epilogue: O / l, LSE = ln2 * (m_ref + log2 l); with a key split, the
+  // range's partial result (fp32) goes to the workspace for the merge
   if (!live) return;
   const float lt = xhalf_sum(lsum);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   const int query = q0w + (lane & 31);
   if (query >= Nq) return;
+  const float lse_row = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
+  if (p.nsplit > 1) {
+    const size_t row = ((size_t)w.split * p.B * p.Hq + (size_t)w.b * p.Hq + hq) * Nq + query;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        f32x4 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[e] = o[db][i4 * 4 + e] * inv;
+        *(f32x4*)(OWS + row * D + db * 32 + i4 * 8 + (lane >> 5) * 4) = r;
+      }
+    if (lane < 32) LWS[row] = lse_row;
+    return;
+  }
   const size_t orow = qoff + (size_t)query * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -634,8 +660,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       for (int e = 0; e < 4; ++e) r[e] = (__bf16)(o[db][i4 * 4 + e] * inv);
       *(bf16x4*)(O + orow + d0) = r;
     }
-  if (LSE != nullptr && lane < 32)
-    LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
+  if (LSE != nullptr && lane < 32) LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lse_row;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -650,7 +675,8 @@ FA_F32_VARIANTS(FA_INST_F32)
 #define FA_INST_BF16(DD, CC, NN)                                                                          \
   template __global__ void fa_fwd_bf16_kernel<DD, CC, NN>(const __bf16* __restrict__, const __bf16* __restrict__, \
                                                           const __bf16* __restrict__, __bf16* __restrict__,     \
-                                                          float* __restrict__, fa_plan_t, float);
+                                                          float* __restrict__, fa_plan_t, float, float* __restrict__, \
+                                                          float* __restrict__);
 // (head dim, causal, waves per workgroup)
 #define FA_BF16_VARIANTS(X)                                                                                \
   X(64, false, 1) X(64, false, 2) X(64, false, 4) X(64, true, 1) X(64, true, 2) X(64, true, 4)              \
@@ -659,10 +685,54 @@ FA_F32_VARIANTS(FA_INST_F32)
   X(256, false, 1) X(256, false, 2) X(256, false, 4) X(256, true, 1) X(256, true, 2) X(256, true, 4)
 FA_BF16_VARIANTS(FA_INST_BF16)
 
+// ---------------------------------------------------------------- merge of key ranges
+// One wave per output row (b, h, i): with L = ln sum_s exp(lse_s),
+// O = sum_s exp(lse_s - L) O_s and LSE = L ("FlashAttention (SV)", section
+// "Online-beräkning av Softmax": block statistics combine exactly).  Ranges
+// that saw no key (lse_s = -inf) weigh nothing; rows with none get O = 0 and
+// LSE = -inf.  Lane t handles columns t*D/64 .. +D/64.
+template <int D>
+__global__ __launch_bounds__(64) void fa_merge_kernel(const float* __restrict__ OWS, const float* __restrict__ LWS,
+                                                      __bf16* __restrict__ O, float* __restrict__ LSE, int nsplit,
+                                                      long long rows) {
+  constexpr int EPL = D / 64;
+  const long long row = blockIdx.x;
+  const int lane = threadIdx.x;
+  float m = NEG_INF;
+  for (int sp = 0; sp < nsplit; ++sp) m = fmaxf(m, LWS[sp * rows + row]);
+  float acc[EPL] = {};
+  float tot = 0.f;
+  if (m != NEG_INF) {
+    for (int sp = 0; sp < nsplit; ++sp) {
+      const float l = LWS[sp * rows + row];
+      const float wgt = __builtin_amdgcn_exp2f((l - m) * 1.4426950408889634f);  // exp(-inf) = 0
+      tot += wgt;
+      const float* src = OWS + ((size_t)sp * rows + row) * D + lane * EPL;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(wgt, src[e], acc[e]);
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) O[row * D + lane * EPL + e] = (__bf16)(acc[e] * inv);
+  if (LSE != nullptr && lane == 0) LSE[row] = tot > 0.f ? m + logf(tot) : NEG_INF;
+}
+
+hipError_t launch_merge(const float* ows, const float* lws, void* o, float* lse, int nsplit, long long rows, int d,
+                        hipStream_t stream) {
+  if (rows < 1 || rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)rows);
+  if (d == 64) hipLaunchKernelGGL(fa_merge_kernel<64>, grid, dim3(64), 0, stream, ows, lws, (__bf16*)o, lse, nsplit, rows);
+  else if (d == 128) hipLaunchKernelGGL(fa_merge_kernel<128>, grid, dim3(64), 0, stream, ows, lws, (__bf16*)o, lse, nsplit, rows);
+  else if (d == 256) hipLaunchKernelGGL(fa_merge_kernel<256>, grid, dim3(64), 0, stream, ows, lws, (__bf16*)o, lse, nsplit, rows);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 int queries_per_wave(int, int) { return 32; }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
-                      float c, int f32, hipStream_t stream) {
+                      float c, int f32, float* ows, float* lws, hipStream_t stream) {
 #define FA_CASE_F32(DD, CC)                                                                               \
   if (f32 && d == DD && (p.causal != 0) == CC) {                                                        \
     hipLaunchKernelGGL((fa_fwd_f32_kernel<DD, CC>), dim3((unsigned)p.nwg), dim3(256), 0, stream, (const float*)q, \
@@ -672,9 +742,10 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
 #define FA_CASE_BF16(DD, CC, NN)                                                                       \
   if (!f32 && d == DD && (p.causal != 0) == CC && p.nw == NN) {                                         \
     hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream,      \
-                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c);   \
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c, ows, lws); \
     return hipGetLastError();                                                                           \
   }
+  if (f32 && p.nsplit > 1) return hipErrorInvalidValue;  // the fp32 kernel has no key split
   FA_F32_VARIANTS(FA_CASE_F32)
   FA_BF16_VARIANTS(FA_CASE_BF16)
 #undef FA_CASE_F32

@@ -12,9 +12,16 @@ namespace fa {
 int queries_per_wave(int d, int f32);
 
 // Enqueue the forward kernel.  c = scale * log2(e).  f32 selects fp32
-// operands (split into bf16 hi/lo parts inside the kernel).
+// operands (split into bf16 hi/lo parts inside the kernel).  With a key
+// split (p.nsplit > 1, bf16 only) the kernel writes the partial results of
+// every range to ows ([nsplit][B][Hq][Nq][d] fp32) and lws ([nsplit][B][Hq][Nq]).
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
-                      float c, int f32, hipStream_t stream);
+                      float c, int f32, float* ows, float* lws, hipStream_t stream);
+
+// Enqueue the merge of nsplit partial results of rows = B*Hq*Nq rows into o
+// (bf16) and lse (fp32, may be NULL).
+hipError_t launch_merge(const float* ows, const float* lws, void* o, float* lse, int nsplit, long long rows, int d,
+                        hipStream_t stream);
 
 // Enqueue the fp8 forward kernel (operands from launch_fp8_prepare).
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale, void* o, float* lse,

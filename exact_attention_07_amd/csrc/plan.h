@@ -19,7 +19,13 @@
 //   * the hardware hands workgroup ids round-robin to the 8 XCDs of an
 //     MI355X, each with its own L2.  When the count divides by 8 the id is
 //     remapped so that XCD x runs the x-th contiguous eighth of that order,
-//     which keeps the workgroups that read one K/V head on one L2.
+//     which keeps the workgroups that read one K/V head on one L2;
+//   * optionally the keys are split into `nsplit` ranges of `tps` tiles
+//     (for grids too small to fill the chip, e.g. decoding with few query
+//     rows): each workgroup then covers one range and writes a partial
+//     result that a merge combines ("FlashAttention (SV)", section
+//     "Online-beräkning av Softmax": block statistics combine exactly).  The
+//     ranges of one query block are consecutive in the order.
 #ifndef FA_PLAN_H
 #define FA_PLAN_H
 
@@ -40,6 +46,8 @@ struct fa_plan_t {
   int nqb;    // query blocks per head: ceil(Nq / pos)
   int nhg;    // head subsets per GQA group: G / hw
   int xcd;    // 1 if workgroup ids are remapped XCD-contiguously
+  int nsplit; // key ranges (1: no split)
+  int tps;    // key tiles per range (nsplit > 1)
   long long nwg;  // workgroups in the grid
 };
 
@@ -60,7 +68,22 @@ FA_HD inline fa_plan_t fa_make_plan(int B, int Hq, int Hkv, int Nq, int Nk, int 
   p.pos = qpw * nw / p.hw;
   p.nqb = (Nq + p.pos - 1) / p.pos;
   p.nhg = p.G / p.hw;
+  p.nsplit = 1;
+  p.tps = 0;
   p.nwg = (long long)B * Hkv * p.nhg * p.nqb;
+  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  return p;
+}
+
+// Split the keys of plan p into ranges of tps tiles of bc keys (nsplit =
+// ceil(tiles / tps) ranges; tps >= 1).
+FA_HD inline fa_plan_t fa_split_plan(fa_plan_t p, int tps, int bc) {
+  const int tiles = (p.Nk + bc - 1) / bc;
+  if (tps < 1) tps = 1;
+  if (tps > tiles) tps = tiles;
+  p.tps = tps;
+  p.nsplit = (tiles + tps - 1) / tps;
+  p.nwg = (long long)p.B * p.Hkv * p.nhg * p.nqb * p.nsplit;
   p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
   return p;
 }
@@ -79,16 +102,19 @@ FA_HD inline fa_plan_t fa_choose_plan(int B, int Hq, int Hkv, int Nq, int Nk, in
 
 struct fa_work_t {
   int b, hkv, hq0, qpos0;  // batch, kv head, first query head, first query position
+  int split;               // key range (0 without a split)
 };
 
 // Workgroup hardware id -> its work.  A bijection of [0, nwg) onto the
 // (group, query block) pairs.
 FA_HD inline fa_work_t fa_decode(const fa_plan_t& p, long long id) {
   long long L = p.xcd ? (id % 8) * (p.nwg / 8) + id / 8 : id;
+  fa_work_t w;
+  w.split = (int)(L % p.nsplit);
+  L /= p.nsplit;
   long long g = L / p.nqb;
   int qi = (int)(L % p.nqb);
   if (p.causal) qi = p.nqb - 1 - qi;
-  fa_work_t w;
   int hg = (int)(g % p.nhg);
   g /= p.nhg;
   w.hkv = (int)(g % p.Hkv);
@@ -109,6 +135,20 @@ FA_HD inline int fa_num_kv_tiles(const fa_plan_t& p, int qpos0, int bc) {
     if (k < klast) klast = k;
   }
   return klast < 0 ? 0 : klast / bc + 1;
+}
+
+// Key tiles [t0, t1) of the workgroup's range, given its tile count nt
+// (fa_num_kv_tiles); empty (t0 >= t1) when the range lies past every key
+// the workgroup sees.
+FA_HD inline void fa_split_tiles(const fa_plan_t& p, int split, int nt, int& t0, int& t1) {
+  if (p.nsplit <= 1) {
+    t0 = 0;
+    t1 = nt;
+    return;
+  }
+  t0 = split * p.tps;
+  t1 = t0 + p.tps < nt ? t0 + p.tps : nt;
+  if (t0 > t1) t0 = t1;
 }
 
 #endif  // FA_PLAN_H

@@ -47,6 +47,8 @@
 #ifndef FA_H
 #define FA_H
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -60,7 +62,8 @@ typedef enum fa_status {
   FA_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
   FA_ERR_SCALE = 6,      /* scale not finite or not > 0 */
   FA_ERR_HIP = 7,        /* the HIP runtime refused the launch */
-  FA_ERR_FLAG = 8        /* causal not 0 or 1 */
+  FA_ERR_FLAG = 8,       /* causal not 0 or 1 */
+  FA_ERR_WORKSPACE = 9   /* workspace missing, too small or not 16-byte aligned */
 } fa_status;
 
 /* Version of this interface; bumped on any incompatible change. */
@@ -89,6 +92,35 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
                      float scale, int causal, void* stream);
+
+/*
+ * bfloat16 forward pass with the keys split into ranges, for grids too small
+ * to fill the GPU (decoding with a few query rows over a long context, small
+ * batches).  Each workgroup computes the attention of its rows over one key
+ * range and writes that part's output (normalised by the part's own sum)
+ * and log-sum-exp; a second kernel combines the parts exactly:
+ *     LSE = ln sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s
+ * ("FlashAttention (SV)", section "Online-beräkning av Softmax": the
+ * statistics of separate blocks combine exactly).  Inputs, outputs and
+ * conventions as for fa_fwd; the result equals fa_fwd's up to rounding.
+ *
+ *   nsplit     number of key ranges; 0 lets the library choose (enough
+ *              workgroups to fill the GPU).  The ranges hold equal numbers
+ *              of 64-key tiles (the last may be shorter), so the number used
+ *              can be below the one asked for; 1 (or a choice of 1) runs
+ *              fa_fwd's kernel and needs no workspace.
+ *   workspace  device memory of at least fa_fwd_splitkv_workspace_size(...)
+ *              bytes for the same arguments, 16-byte aligned, owned by the
+ *              caller and not shared with a call in flight; holds the parts
+ *              as float32 O [nsplit][B][Hq][Nq][d] followed by float32 LSE
+ *              [nsplit][B][Hq][Nq].  May be NULL when the size is 0.
+ * Errors: those of fa_fwd; FA_ERR_SHAPE for nsplit < 0 (or too many rows);
+ * FA_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ */
+size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int nsplit);
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                         int nsplit, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * FP8 preparation ("FlashAttention-3 — 闪电注意力-3", section on low

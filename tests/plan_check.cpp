@@ -51,7 +51,55 @@ static void check_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int q
   }
 }
 
+// Split plans: every (b, query head, query row, key tile) visible to the row
+// is covered by exactly one (workgroup, tile in its range).
+static void check_split(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int nw, int tps) {
+  fa_plan_t p = fa_split_plan(fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, 32, nw), tps, 64);
+  const int tiles = (Nk + 63) / 64;
+  CHECK(p.nsplit >= 1 && p.tps >= 1 && (long long)p.nsplit * p.tps >= tiles && (long long)(p.nsplit - 1) * p.tps < tiles);
+  std::vector<int> cover((size_t)B * Hq * Nq * tiles, 0);
+  std::set<std::tuple<int, int, int, int>> seen;
+  for (long long id = 0; id < p.nwg; ++id) {
+    fa_work_t w = fa_decode(p, id);
+    CHECK(w.split >= 0 && w.split < p.nsplit);
+    CHECK(seen.insert({w.b, w.hq0, w.qpos0, w.split}).second);
+    int nt = fa_num_kv_tiles(p, w.qpos0, 64), t0, t1;
+    fa_split_tiles(p, w.split, nt, t0, t1);
+    CHECK(0 <= t0 && t0 <= t1 && t1 <= nt);
+    for (int wave = 0; wave < nw; ++wave) {
+      int hq = w.hq0 + wave % p.hw;
+      int q0 = w.qpos0 + (wave / p.hw) * 32;
+      for (int i = q0; i < q0 + 32 && i < Nq; ++i) {
+        int klast = causal ? (i + Nk - Nq < Nk - 1 ? i + Nk - Nq : Nk - 1) : Nk - 1;
+        for (int t = t0; t < t1; ++t)
+          if (t * 64 <= klast) cover[(((size_t)w.b * Hq + hq) * Nq + i) * tiles + t]++;
+      }
+    }
+  }
+  CHECK((long long)seen.size() == p.nwg);
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < Hq; ++h)
+      for (int i = 0; i < Nq; ++i) {
+        int klast = causal ? (i + Nk - Nq < Nk - 1 ? i + Nk - Nq : Nk - 1) : Nk - 1;
+        for (int t = 0; t < tiles; ++t)
+          CHECK(cover[(((size_t)b * Hq + h) * Nq + i) * tiles + t] == (klast >= 0 && t * 64 <= klast ? 1 : 0));
+      }
+  // the ranges of one query block are consecutive in the logical order
+  if (!p.xcd && p.nsplit > 1) {
+    fa_work_t a = fa_decode(p, 0), b = fa_decode(p, 1);
+    CHECK(a.split == 0 && b.split == 1 && a.qpos0 == b.qpos0 && a.hq0 == b.hq0);
+  }
+}
+
 int main() {
+  for (int causal = 0; causal < 2; ++causal)
+    for (int tps : {1, 2, 3, 7, 100}) {
+      check_split(2, 8, 2, 1, 1000, causal, 4, tps);    // decoding: one query, GQA 4
+      check_split(1, 4, 4, 3, 513, causal, 1, tps);     // three queries
+      check_split(1, 6, 2, 70, 300, causal, 2, tps);    // several query blocks
+      check_split(1, 2, 2, 150, 40, causal, 1, tps);    // Nq > Nk
+    }
+
   for (int causal = 0; causal < 2; ++causal)
     for (int nw : {1, 2, 4, 8})
       for (int qpw : {32, 64}) {

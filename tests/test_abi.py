@@ -107,3 +107,43 @@ def test_fp8_forward_rejects_invalid_arguments(lib, kw, status):
         a["d"] = 256
     assert lib.fa_fwd_fp8(a["q8"], a["k8"], a["v8t"], a["descale"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
                           a["Nq"], a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], None) == status
+
+
+SPLIT_GOOD = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128, scale=0.1, causal=0, nsplit=0,
+                  ws=P, wsb=1 << 30)
+
+
+def call_split(lib, **kw):
+    a = dict(SPLIT_GOOD)
+    a.update(kw)
+    return lib.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                              a["d"], ctypes.c_float(a["scale"]), a["causal"], a["nsplit"], a["ws"],
+                              ctypes.c_size_t(a["wsb"]), None)
+
+
+def test_splitkv_workspace_size(lib):
+    f = lib.fa_fwd_splitkv_workspace_size
+    f.restype = ctypes.c_size_t
+    # decoding: one query of 8 heads over 4096 keys needs a split; its parts are [nsplit][1][8][1] rows of d + 1 floats
+    n = f(1, 8, 2, 1, 4096, 128, 0, 0)
+    assert n > 0 and n % ((128 + 1) * 4 * 8) == 0
+    nsplit = n // ((128 + 1) * 4 * 8)
+    assert 2 <= nsplit <= 64
+    # an explicit split count: 4 ranges of 16 tiles
+    assert f(1, 8, 2, 1, 4096, 128, 0, 4) == 4 * 8 * 129 * 4
+    # a split count that does not divide the 64 tiles: ranges of 22 tiles, 3 of them
+    assert f(1, 8, 2, 1, 4096, 128, 0, 3) == 3 * 8 * 129 * 4
+    # no split needed or asked: no workspace
+    assert f(2, 32, 8, 8192, 8192, 128, 1, 0) == 0
+    assert f(1, 8, 2, 1, 4096, 128, 0, 1) == 0
+    # invalid arguments: 0
+    assert f(1, 8, 3, 1, 4096, 128, 0, 0) == 0 and f(1, 8, 2, 1, 4096, 96, 0, 0) == 0 and f(1, 8, 2, 1, 4096, 128, 0, -1) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(B=0), 2), (dict(d=80), 3), (dict(Hq=7), 4), (dict(k=P + 4), 5),
+    (dict(scale=float("inf")), 6), (dict(causal=5), 8), (dict(nsplit=-1), 2),
+    (dict(ws=None), 9), (dict(wsb=100), 9), (dict(ws=P + 8), 9),
+])
+def test_splitkv_rejects_invalid_arguments(lib, kw, status):
+    assert call_split(lib, **kw) == status
