@@ -18,6 +18,12 @@ on the stream the kernels run on.  Prints one JSON line on stdout
             source (null when the source changed since the counters were taken)
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
             sample of the same workload (whole heads), as a reported baseline
+
+--config decode measures the key-split path (fa_fwd_splitkv: parts over key
+ranges merged on the GPU) on a GQA decoding step, B=8 sequences, Hq=32,
+Hkv=8, one query each over Nk=32768 keys, d=128.  That path is bound by HBM
+bandwidth, so its line reports algorithmic bytes per second (Q, K, V, O, LSE
+once) against the 8 TB/s of HBM3E; the step includes the merge kernel.
 """
 from __future__ import annotations
 
@@ -112,7 +118,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--config", default="3", help="standing workload 1..5, or decode")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="compare sampled rows with the oracle (stderr)")
@@ -128,7 +134,9 @@ def main():
     import torch
     from exact_attention_07_amd import api, gen
 
-    w, x = gen.make_config(args.config)
+    cfg = args.config if args.config == "decode" else int(args.config)
+    args.config = cfg
+    w, x = gen.make_config(cfg)
     log(f"workload: {w.name}")
     dev = torch.device("cuda:0")
 
@@ -141,7 +149,17 @@ def main():
     o = torch.empty(q.shape, dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16, device=dev)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
-    if w.dtype == "fp8":
+    decode = cfg == "decode"
+    if decode:
+        ws_bytes = api.splitkv_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal, 0)
+        ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+
+        def prepare():
+            pass
+
+        def attend():
+            api.fa_fwd_splitkv(q, k, v, o, lse, w.softmax_scale, w.causal, 0, ws, stream)
+    elif w.dtype == "fp8":
         signs = torch.from_numpy(x["signs"]).to(dev)
         q8 = torch.empty(q.shape, dtype=torch.uint8, device=dev)
         k8 = torch.empty(k.shape, dtype=torch.uint8, device=dev)
@@ -212,6 +230,34 @@ def main():
         err = max(float(np.abs(oo[b, h, i] - o_ref[r]).max()) for r, (b, h, i) in enumerate(rows))
         lerr = max(abs(float(ll[b, h, i]) - l_ref[r]) for r, (b, h, i) in enumerate(rows))
         log(f"check on {len(rows)} rows: max|dO|={err:.2e} max|dLSE|={lerr:.2e}")
+
+    if decode:
+        # the same step without the split, for comparison (stderr)
+        for _ in range(3):
+            api.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+        a, b = event(), event()
+        a.record(stream)
+        for _ in range(args.steps):
+            api.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        log(f"without the key split (fa_fwd): {a.elapsed_time(b) / args.steps:.4f} ms/step")
+        nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        log(f"key split: {ws_bytes / 4 / (w.B * w.Hq * w.Nq * (w.d + 1)):.0f} ranges, {gbs:.0f} GB/s")
+        line = {
+            "metric": "attention decode step HBM GB/s (bf16, GQA, Nq=1, Nk=32K, d=128)",
+            "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic (seeded N(0,1), resident in HBM before timing)",
+            "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                       "causal": w.causal, "path": "fa_fwd_splitkv (attention kernel over key ranges + merge)"},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbs / 8000.0, 4), "traffic": None, "step_ms": round(ms, 5),
+                         "tflops": round(tflops, 2)},
+        }
+        print(json.dumps(line), flush=True)
+        return
 
     peak = PEAK_TFLOPS[w.dtype]
     traffic = load_traffic(args.config, w.dtype)

@@ -117,10 +117,17 @@ def make_inputs(w: Workload, seed_key=(0,)) -> dict:
     return out
 
 
-def make_config(cfg: int, seed: int | None = None) -> tuple[Workload, dict]:
-    """Inputs of standing workload cfg (1..5); seed None reproduces the standing draw."""
-    w = CONFIGS[cfg]
-    key = (cfg,) if seed is None else (cfg, seed)
+# A decoding step of a GQA model over a long context (one new query per
+# sequence): the workload of the key-split path.  Tensor ids as above, seed
+# key (6,).
+DECODE = Workload("GQA decode B8 Hq32 Hkv8 Nq1 Nk32768 d128 bf16", 8, 32, 8, 1, 32768, 128, "bf16", True)
+
+
+def make_config(cfg, seed: int | None = None) -> tuple[Workload, dict]:
+    """Inputs of standing workload cfg (1..5, or "decode"); seed None reproduces the standing draw."""
+    w = DECODE if cfg == "decode" else CONFIGS[cfg]
+    cid = 6 if cfg == "decode" else cfg
+    key = (cid,) if seed is None else (cid, seed)
     return w, make_inputs(w, key)
 
 
