@@ -228,3 +228,41 @@ def merge_fp64(o_parts, lse_parts):
     o = np.einsum("s...,s...d->...d", w, o_parts)
     o = np.where(live[..., None], o / np.where(live, tot, 1.0)[..., None], 0.0)
     return o, lse
+
+
+def attention_backward_fp64(q, k, v, do, scale: float, causal: bool):
+    """Gradients of the definition for an upstream gradient do = dL/dO.
+
+    With P = softmax(S) (rows normalised, masked entries 0), O = P V:
+      dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D) with D_i = sum_j P_ij dP_ij
+      (= sum_c dO_ic O_ic),  dQ = scale dS K,  dK = scale dS^T Q.
+    GQA: the gradients of a key/value head sum over its query heads.  The
+    pages print no backward algorithm; these are the derivatives of the
+    definition they give ("FlashAttention (SV)", section "Problematik med
+    standard-attention"), written out.  Returns (dq, dk, dv) in fp64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, HQ, NQ, _ = q.shape
+    _, HKV, NK, _ = k.shape
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    vis = _visible(NQ, NK, causal)
+    for b in range(B):
+        for h in range(HQ):
+            hk = kv_head_of(h, HQ, HKV)
+            s = scale * (q[b, h] @ k[b, hk].T)
+            p, m, l = _softmax_rows(s, vis)
+            live = l > 0
+            pn = np.zeros_like(p)
+            pn[live] = p[live] / l[live][:, None]
+            dv[b, hk] += pn.T @ do[b, h]
+            dp = do[b, h] @ v[b, hk].T
+            dd = (pn * dp).sum(axis=1, keepdims=True)
+            ds = pn * (dp - dd)
+            dq[b, h] = scale * (ds @ k[b, hk])
+            dk[b, hk] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv

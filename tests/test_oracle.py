@@ -13,7 +13,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import attention_fp64, attention_keys_fp64, attention_rows_fp64, merge_fp64, online_fp64, formats, fp8
+from oracle import (attention_backward_fp64, attention_fp64, attention_keys_fp64, attention_rows_fp64, merge_fp64,
+                    online_fp64, formats, fp8)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
 
@@ -388,3 +389,68 @@ def test_key_range_single_key_is_its_value_row():
     o, l = attention_keys_fp64(q, k, v, 0.3, False, 7, 8)
     np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0, 7], (4, 6)), atol=1e-15)
     np.testing.assert_allclose(l[0, 0], 0.3 * (q[0, 0] @ k[0, 0, 7]), atol=1e-14)
+
+
+# ---------------------------------------------------------------- gradients
+def _loss(q, k, v, do, scale, causal):
+    o, _ = attention_fp64(q, k, v, scale, causal)
+    return float((o * do).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", [(1, 2, 1, 5, 7, 4), (2, 4, 2, 6, 6, 3), (1, 3, 3, 7, 4, 5)],
+                         ids=["mha", "gqa", "nq_gt_nk"])
+def test_backward_matches_finite_differences(shape, causal):
+    B, HQ, HKV, NQ, NK, D = shape
+    rng = np.random.default_rng(sum(shape) + 7 * causal)
+    q = rng.standard_normal((B, HQ, NQ, D))
+    k = rng.standard_normal((B, HKV, NK, D))
+    v = rng.standard_normal((B, HKV, NK, D))
+    do = rng.standard_normal((B, HQ, NQ, D))
+    scale = 0.7
+    dq, dk, dv = attention_backward_fp64(q, k, v, do, scale, causal)
+    eps = 1e-6
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = x.copy(); xp[idx] += eps
+            xm = x.copy(); xm[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], do, scale, causal)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], do, scale, causal)
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g, num, rtol=0, atol=1e-7, err_msg=f"d{name}")
+
+
+def test_backward_single_key_and_delta_identity():
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 2, 5, 4)); k = rng.standard_normal((1, 1, 1, 4)); v = rng.standard_normal((1, 1, 1, 4))
+    do = rng.standard_normal((1, 2, 5, 4))
+    dq, dk, dv = attention_backward_fp64(q, k, v, do, 0.5, False)
+    # one key: P = 1 everywhere, so the scores do not matter and dV is the sum of dO over all rows and heads
+    np.testing.assert_allclose(dq, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dk, 0.0, atol=1e-15)
+    np.testing.assert_allclose(dv[0, 0, 0], do.sum(axis=(0, 1, 2)), atol=1e-13)
+    # D_i = sum_j P_ij dP_ij = sum_c dO_ic O_ic (used by the kernels): rows of dS sum to zero
+    q = rng.standard_normal((1, 1, 6, 3)); k = rng.standard_normal((1, 1, 9, 3)); v = rng.standard_normal((1, 1, 9, 3))
+    do = rng.standard_normal((1, 1, 6, 3))
+    dq, dk, dv = attention_backward_fp64(q, k, v, do, 0.9, True)
+    o, _ = attention_fp64(q, k, v, 0.9, True)
+    p_list = attention_fp64(q, k, v, 0.9, True, return_p=True)[2]
+    dp = do[0, 0] @ v[0, 0].T
+    np.testing.assert_allclose((p_list[0] * dp).sum(axis=1), (do[0, 0] * o[0, 0]).sum(axis=1), atol=1e-13)
+
+
+def test_backward_gqa_equals_mha_with_repeated_kv_heads():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 4, 6, 3)); k = rng.standard_normal((2, 2, 8, 3)); v = rng.standard_normal((2, 2, 8, 3))
+    do = rng.standard_normal((2, 4, 6, 3))
+    dq, dk, dv = attention_backward_fp64(q, k, v, do, 0.6, True)
+    dq2, dk2, dv2 = attention_backward_fp64(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), do, 0.6, True)
+    np.testing.assert_allclose(dq, dq2, atol=1e-13)
+    np.testing.assert_allclose(dk, dk2.reshape(2, 2, 2, 8, 3).sum(axis=2), atol=1e-13)
+    np.testing.assert_allclose(dv, dv2.reshape(2, 2, 2, 8, 3).sum(axis=2), atol=1e-13)
