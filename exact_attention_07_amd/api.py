@@ -48,6 +48,10 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_splitkv.restype = ctypes.c_int
     L.fa_fwd_splitkv_workspace_size.argtypes = [i] * 8
     L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
+    L.fa_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
+    L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_workspace_size.argtypes = [i] * 7
+    L.fa_bwd_workspace_size.restype = ctypes.c_size_t
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_abi_version.argtypes = []
@@ -232,3 +236,48 @@ def attention_splitkv(q, k, v, causal: bool = False, scale: float | None = None,
     ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=q.device) if nbytes else None
     fa_fwd_splitkv(q, k, v, o, lse, scale, causal, nsplit, ws, stream)
     return o, lse
+
+
+def bwd_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal: bool) -> int:
+    """Bytes of workspace fa_bwd needs (0 for arguments it would reject)."""
+    return int(lib().fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(bool(causal))))
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None) -> None:
+    """bf16 backward pass: gradients into caller-allocated dq (q's shape), dk, dv (k's shape)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v, o, lse)
+    for t in (q, k, v, o, do, dq, dk, dv):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("fa_bwd takes bfloat16 q, k, v, o, do, dq, dk, dv")
+    if lse is None or lse.dtype != torch.float32:
+        raise TypeError("lse must be a float32 tensor")
+    if tuple(do.shape) != tuple(q.shape) or tuple(dq.shape) != tuple(q.shape):
+        raise ValueError("do and dq must have q's shape")
+    if tuple(dk.shape) != tuple(k.shape) or tuple(dv.shape) != tuple(k.shape):
+        raise ValueError("dk and dv must have k's shape")
+    for t in (do, dq, dk, dv):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous GPU tensors")
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous GPU tensor")
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+                        B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _ptr(workspace), nbytes,
+                        _stream(stream)), "fa_bwd")
+
+
+def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None):
+    """Allocate the gradients and the workspace, run fa_bwd, return (dq, dk, dv).
+
+    o and lse are fa_fwd's outputs for the same q, k, v, causal and scale."""
+    import torch
+    B, Hq, Nq, d = q.shape
+    _, Hkv, Nk, _ = k.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    nbytes = bwd_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal)
+    ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=q.device)
+    fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
+    return dq, dk, dv

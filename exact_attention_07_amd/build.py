@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_fwd_fp8.hip", "fa_fp8_prepare.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_fp8_prepare.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the device code on purpose.
@@ -46,7 +46,7 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as pool:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 5)) as pool:
         objs = list(pool.map(compile_one, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]

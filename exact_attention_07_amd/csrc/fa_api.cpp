@@ -99,6 +99,27 @@ size_t splitkv_workspace_bytes(const fa_plan_t& p, int d) {
   return (size_t)p.nsplit * rows * (size_t)(d + 1) * sizeof(float);
 }
 
+// Backward plans.  dQ: the forward kernel's plan (32 query rows per wave,
+// up to bwd_dq_max_waves waves).  dK/dV: key blocks of up to
+// bwd_dkdv_max_waves waves (a workgroup of that size fills a CU on its
+// own), fewer while the grid would have under MIN_KV_WORKGROUPS workgroups.
+constexpr long long MIN_KV_WORKGROUPS = 512;
+
+fa_plan_t plan_bwd_dq(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+  return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, 32, MIN_WORKGROUPS, fa::bwd_dq_max_waves(d));
+}
+
+fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+  const int kpw = fa::bwd_keys_per_wave(d);
+  for (int nw = fa::bwd_dkdv_max_waves(d); nw > 1; nw >>= 1) {
+    const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
+    if (p.nwg >= MIN_KV_WORKGROUPS) return p;
+  }
+  return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, 1);
+}
+
+size_t bwd_workspace_bytes(int B, int Hq, int Nq) { return (size_t)B * Hq * Nq * 2 * sizeof(float); }
+
 }  // namespace
 
 extern "C" {
@@ -189,6 +210,34 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
   float* lws = ows + (size_t)p.nsplit * rows * d;
   hipError_t e = fa::launch_fwd(q, k, v, nullptr, nullptr, p, d, c, 0, ows, lws, (hipStream_t)stream);
   if (e == hipSuccess) e = fa::launch_merge(ows, lws, o, lse, p.nsplit, rows, d, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+  if (validate_shape(B, Hq, Hkv, Nq, Nk, d) != FA_OK || (causal != 0 && causal != 1)) return 0;
+  return bwd_workspace_bytes(B, Hq, Nq);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+  const fa_status st = validate_shape(B, Hq, Hkv, Nq, Nk, d);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_ALIGN;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  if (causal != 0 && causal != 1) return FA_ERR_FLAG;
+  // one query head's rows (the range of a buffer resource) fit in 31 bits
+  if (((double)Nq + 64.0) * d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
+  const size_t need = bwd_workspace_bytes(B, Hq, Nq);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  const fa_plan_t pq = plan_bwd_dq(B, Hq, Hkv, Nq, Nk, d, causal);
+  const fa_kvplan_t pk = plan_bwd_dkdv(B, Hq, Hkv, Nq, Nk, d, causal);
+  if (pq.nwg > 0x7fffffffLL || pk.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const hipError_t e = fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, pq, pk, d,
+                                      (float)((double)scale * LOG2E), scale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

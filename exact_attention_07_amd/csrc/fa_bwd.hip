@@ -1,0 +1,481 @@
+// fa_bwd.hip -- backward pass of exact attention for gfx950 (MI355X):
+// gradients dQ, dK, dV for an upstream gradient dO, recomputing the
+// probabilities from Q, K and the saved log-sum-exp instead of storing them.
+//
+// The pages report training speed-ups ("FlashAttention-4震撼发布",
+// FlashAttention-2 list; "FlashAttention (SV)", section "Prestanda och
+// fördelar") but print no backward algorithm.  What is computed is the
+// derivative of the definition ("FlashAttention (SV)", section
+// "Problematik med standard-attention"), with P = softmax(scale Q K^T):
+//
+//     dV = P^T dO          dP = dO V^T          D_i = sum_c dO_ic O_ic
+//     dS = P o (dP - D)    dQ = scale dS K      dK  = scale dS^T Q
+//
+// and P_ij = 2^(scale log2(e) q_i.k_j - LSE_i log2(e)) is rebuilt tile by
+// tile from the forward pass's LSE, the same tiling that keeps the N x N
+// matrices out of memory in the forward pass ("FlashAttention (SV)",
+// sections "Tiling och blockbearbetning" and "Sammanslagning av
+// operationer").  D_i = sum_j P_ij dP_ij equals the row dot product of dO and
+// O, so it needs no pass over the keys.
+//
+// Two kernels, no atomics:
+// * fa_bwd_dq_kernel: the forward kernel's shape.  A wave owns 32 query rows
+//   of one head (Q and dO fragments in VGPRs), streams the K/V tiles of its
+//   key/value head through LDS and accumulates dQ^T += K^T dS^T.  Its
+//   prologue also forms D_i and LSE_i log2(e) of its rows and stores them
+//   (8 bytes per row) for the second kernel.
+// * fa_bwd_dkdv_kernel: the transposed shape.  A wave owns 64 keys of one
+//   key/value head (K and V fragments in VGPRs, dK^T and dV^T accumulators)
+//   and streams the query tiles of every query head of its GQA group through
+//   LDS: S = Q K^T, dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS.  The
+//   sum over the group's query heads stays inside the wave, so dK and dV are
+//   written once, without atomics.
+// Per 64 x 64 block of (queries, keys) the two kernels run 7 matrix products
+// where 5 would do (S and dP are formed in both); in exchange nothing is
+// accumulated across workgroups, which on an 8-XCD chip (one L2 per XCD)
+// would need device-scope atomics on dQ from every key block.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_frag.h"
+#include "fa_kernels.h"
+#include "plan.h"
+
+namespace fa {
+
+constexpr float LOG2E_F = 1.44269504088896341f;
+
+template <int D>
+struct BwdCfg {
+  static constexpr int DS = D / 16;  // k-steps over the head dimension
+  static constexpr int DB = D / 32;  // 32-row blocks of a D-row accumulator
+  static constexpr int KB = BC / 32; // 32-row blocks of a 64-row tile
+  static constexpr int PS = BC / 16; // k-steps over a 64-row tile
+  static constexpr int CPR = D / 8;  // 16-byte data slots per row
+  // LDS row strides.  Tiles read both as row fragments (b128, 16 rows per
+  // 16 lanes) and as transposed fragments (ds_read_b64_tr_b16, 4 rows per 32
+  // lanes) need an odd number of 16-byte slots per row for the first and
+  // rows about 16 banks apart for the second; CPR + 3 slots (CPR + 1 at
+  // d = 64) satisfies the first exactly and the second up to a few shared
+  // banks.  Tiles read only as row fragments take CPR + 1.
+  static constexpr int SPR_X = CPR + (D == 64 ? 1 : 3);
+  static constexpr int SPR_R = CPR + 1;
+  static constexpr int RSX = SPR_X * 16, RSR = SPR_R * 16;
+  static constexpr int TILE_X = BC * RSX, TILE_R = BC * RSR;
+  static_assert((RSX / 4) % 8 == 4 && (RSR / 4) % 8 == 4, "row fragments: odd multiple of 4 banks");
+};
+
+using P0 = std::integral_constant<int, 0>;
+using P1 = std::integral_constant<int, 1>;
+
+// ---------------------------------------------------------------- dQ (and D, LSE log2 e)
+// Wave state: Q and dO rows as B operands (lane: query row lane % 32, 8
+// consecutive columns per k-step), dQ^T accumulators (d x 32).  Per key tile:
+//   S^T  = K Q^T   (A = K rows from LDS)       dP^T = V dO^T (A = V rows)
+//   P^T  = 2^(S^T c - L2), dS^T = P^T o (dP^T - D), packed to bf16 in place
+//   dQ^T += K^T dS^T (A = K^T, transposed LDS reads in the row order of the
+//   S^T accumulator)
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                      const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+                      float* __restrict__ LD, __bf16* __restrict__ dQ, fa_plan_t p, float c, float scale) {
+  using C = BwdCfg<D>;
+  constexpr int DS = C::DS, DB = C::DB, KB = C::KB, PS = C::PS, RSX = C::RSX, RSR = C::RSR;
+  using CopyK = CopyPlan<D, NW, C::SPR_X>;
+  using CopyV = CopyPlan<D, NW, C::SPR_R>;
+  __shared__ __attribute__((aligned(1024))) char lk0_[C::TILE_X];
+  __shared__ __attribute__((aligned(1024))) char lk1_[C::TILE_X];
+  __shared__ __attribute__((aligned(1024))) char lv0_[C::TILE_R];
+  __shared__ __attribute__((aligned(1024))) char lv1_[C::TILE_R];
+  __shared__ __attribute__((aligned(1024))) char lsp_[1024];
+  auto kslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lk0_ : lk1_); };
+  auto vslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lv0_ : lv1_); };
+  LDS_AS char* const spare = (LDS_AS char*)lsp_;
+
+  const fa_work_t w = fa_decode(p, blockIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hq = w.hq0 + wave % p.hw;
+  const int q0w = w.qpos0 + (wave / p.hw) * 32;
+  const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq;
+  const int nt = fa_num_kv_tiles(p, w.qpos0, BC);
+  const bool live = q0w < Nq;
+  const int qlast_w = min(Nq - 1, q0w + 31);
+  const int klast_w = CAUSAL ? min(Nk - 1, qlast_w + off) : Nk - 1;
+  const int kfull_w = CAUSAL ? min(Nk - 1, q0w + off) : Nk - 1;
+  const int ntw = (live && klast_w >= 0) ? klast_w / BC + 1 : 0;  // tiles this wave computes
+
+  const size_t rowbase = (size_t)(w.b * p.Hq + hq) * Nq;
+  const size_t qoff = rowbase * D;
+  const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
+  const int query = q0w + (lane & 31);
+  const int qrow = min(query, Nq - 1);
+
+  // Q, dO fragments; D = rowsum(dO o O) from the same loads of O
+  bf16x8 qf[DS], dof[DS];
+  float L2, Drow;
+  {
+    float dsum = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const size_t e0 = qoff + (size_t)qrow * D + ds * 16 + (lane >> 5) * 8;
+      qf[ds] = *(const bf16x8*)(Q + e0);
+      dof[ds] = *(const bf16x8*)(dO + e0);
+      const bf16x8 of = *(const bf16x8*)(O + e0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dsum = __builtin_fmaf((float)dof[ds][e], (float)of[e], dsum);
+    }
+    Drow = xhalf_sum(dsum);
+    const float lse = LSE[rowbase + qrow];
+    // a row that sees no key (LSE = -inf) has every score masked; 0 keeps
+    // 2^(-inf - L2) = 0 free of NaN
+    L2 = lse == NEG_INF ? 0.f : lse * LOG2E_F;
+    if (live && lane < 32 && query < Nq) {
+      LD[(rowbase + query) * 2] = L2;
+      LD[(rowbase + query) * 2 + 1] = Drow;
+    }
+  }
+
+  f32x16 dq[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) dq[db] = (f32x16){};
+
+  const int koff_l = k_lane_off<RSX>(lane), voff_l = k_lane_off<RSR>(lane), toff_l = v_lane_off<RSX>(lane);
+  CopyK cpk;
+  CopyV cpv;
+  cpk.init(wave, lane);
+  cpv.init(wave, lane);
+  const __amdgpu_buffer_rsrc_t kres = CopyK::rsrc(K + kvoff, Nk), vres = CopyV::rsrc(V + kvoff, Nk);
+  auto issue = [&](int j, auto par) {
+    cpk.issue_all(kres, j * (BC * D * 2), kslot(par), spare, wave);
+    cpv.issue_all(vres, j * (BC * D * 2), vslot(par), spare, wave);
+  };
+
+  auto compute = [&](int j, auto par) {
+    LDS_AS const char* kt = kslot(par);
+    LDS_AS const char* vt = vslot(par);
+    const int j0 = j * BC;
+    f32x16 st[KB], dpt[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) st[kb] = dpt[kb] = (f32x16){};
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        st[kb] = mfma(lds_b128(kt + koff_l + kb * 32 * RSX + ds * 32), qf[ds], st[kb]);
+        dpt[kb] = mfma(lds_b128(vt + voff_l + kb * 32 * RSR + ds * 32), dof[ds], dpt[kb]);
+      }
+    if (j0 + BC - 1 > kfull_w) {
+      // keys past the row's last visible one (and past Nk) get P = 0
+      const int klim = CAUSAL ? min(Nk, query + off + 1) : Nk;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int kmax = klim - 1 - j0 - kb * 32 - (lane >> 5) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if ((i >> 2) * 8 + (i & 3) > kmax) st[kb][i] = NEG_INF;
+      }
+    }
+    u32x4 dsp[PS];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i], c, -L2));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][i + 1], c, -L2));
+        dsp[kb * 2 + i / 8][(i % 8) / 2] = pack_bf16(p0 * (dpt[kb][i] - Drow), p1 * (dpt[kb][i + 1] - Drow));
+      }
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+        dq[db] = mfma(v_frag<RSX>(kt + toff_l, ps, db), __builtin_bit_cast(bf16x8, dsp[ps]), dq[db]);
+  };
+
+  // double-buffered key tiles: iteration j waits for tile j, then starts the
+  // copy of tile j + 1 into the slot tile j - 1 used
+  auto iteration = [&](int j, auto par) {
+    using other = std::integral_constant<int, 1 - decltype(par)::value>;
+    vm_wait<0>();
+    __syncthreads();
+    if (j + 1 < nt) issue(j + 1, other{});
+    if (j < ntw) compute(j, par);
+  };
+  if (nt > 0) issue(0, P0{});
+  for (int j = 0; j < nt; j += 2) {
+    iteration(j, P0{});
+    if (j + 1 < nt) iteration(j + 1, P1{});
+  }
+  vm_wait<0>();
+
+  if (!live || query >= Nq) return;
+  const size_t orow = qoff + (size_t)query * D;
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      bf16x4 r;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) r[e] = (__bf16)(dq[db][i4 * 4 + e] * scale);
+      *(bf16x4*)(dQ + orow + db * 32 + i4 * 8 + (lane >> 5) * 4) = r;
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+// Wave state: K and V rows of KBW blocks of 32 keys as B operands (lane: key
+// lane % 32, 8 consecutive columns per k-step); dK^T, dV^T accumulators
+// (d x 32 per key block).  Per query tile (64 rows of one query head, staged
+// in LDS with their L2 = LSE log2(e) and D values), per 32-row half:
+//   S  = Q K^T   (A = Q rows from LDS)         dP = dO V^T  (A = dO rows)
+//   P  = 2^(S c - L2), dS = P o (dP - D), packed to bf16 in place
+//   dV^T += dO^T P,  dK^T += Q^T dS  (A = dO^T, Q^T: transposed LDS reads in
+//   the row order of the S accumulator)
+// The query tiles are visited last tile first, head-minor: all workgroups of
+// one key/value head then read the same query tiles at about the same time,
+// from L2.
+template <int D, bool CAUSAL, int NW, int KBW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1)))
+void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                        const __bf16* __restrict__ dO, const float* __restrict__ LD, __bf16* __restrict__ dK,
+                        __bf16* __restrict__ dV, fa_kvplan_t p, float c, float scale) {
+  using C = BwdCfg<D>;
+  constexpr int DS = C::DS, DB = C::DB, RSX = C::RSX;
+  constexpr int KPW = 32 * KBW;
+  using CopyQ = CopyPlan<D, NW, C::SPR_X>;
+  __shared__ __attribute__((aligned(1024))) char lq0_[C::TILE_X];
+  __shared__ __attribute__((aligned(1024))) char lq1_[C::TILE_X];
+  __shared__ __attribute__((aligned(1024))) char lo0_[C::TILE_X];
+  __shared__ __attribute__((aligned(1024))) char lo1_[C::TILE_X];
+  __shared__ __attribute__((aligned(1024))) char ll0_[1024];
+  __shared__ __attribute__((aligned(1024))) char ll1_[1024];
+  __shared__ __attribute__((aligned(1024))) char lsp_[1024];
+  auto qslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lq0_ : lq1_); };
+  auto oslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lo0_ : lo1_); };
+  auto lslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? ll0_ : ll1_); };
+  LDS_AS char* const spare = (LDS_AS char*)lsp_;
+
+  const fa_kvwork_t w = fa_kv_decode(p, blockIdx.x);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int h = lane >> 5;
+  const int k0w = w.k0 + wave * KPW;
+  const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq, G = p.G;
+  const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
+  const bool has_keys = k0w < Nk;
+
+  bf16x8 kf[KBW][DS], vf[KBW][DS];
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb) {
+    const int key = k0w + kb * 32 + (lane & 31);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) {
+      const size_t e0 = kvoff + (size_t)key * D + ds * 16 + h * 8;
+      kf[kb][ds] = key < Nk ? *(const bf16x8*)(K + e0) : (bf16x8){};
+      vf[kb][ds] = key < Nk ? *(const bf16x8*)(V + e0) : (bf16x8){};
+    }
+  }
+  f32x16 dk[KBW][DB], dv[KBW][DB];
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb)
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dk[kb][db] = dv[kb][db] = (f32x16){};
+
+  int first, ntq;
+  fa_kv_query_tiles(p, w.k0, BC, first, ntq);
+  const int total = (ntq - first) * G;  // iterations: tile ntq - 1 - it / G of head it % G
+
+  const int qoff_l = k_lane_off<RSX>(lane), toff_l = v_lane_off<RSX>(lane);
+  CopyQ cp;
+  cp.init(wave, lane);
+  auto issue = [&](int it, auto par) {
+    const int t = ntq - 1 - it / G, hq = w.hkv * G + it % G;
+    const size_t rb = (size_t)(w.b * p.Hq + hq) * Nq;
+    const __amdgpu_buffer_rsrc_t rq = CopyQ::rsrc(Q + rb * D, Nq), ro = CopyQ::rsrc(dO + rb * D, Nq);
+    cp.issue_all(rq, t * (BC * D * 2), qslot(par), spare, wave);
+    cp.issue_all(ro, t * (BC * D * 2), oslot(par), spare, wave);
+    if (wave == 0) {
+      // (L2, D) of the tile's 64 rows: 512 bytes from lanes 0 .. 31 (lanes
+      // 32 .. 63 fill the unused second half of the 1 KB slot)
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc((void*)(LD + rb * 2), (short)0, Nq * 8, 0x00020000);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (LDS_AS void*)lslot(par), 16, lane * 16, t * (BC * 8), 0, 0);
+    }
+  };
+
+  auto compute = [&](int it, auto par) {
+    LDS_AS const char* qt = qslot(par);
+    LDS_AS const char* ot = oslot(par);
+    LDS_AS const char* lt = lslot(par);
+    const int q0 = (ntq - 1 - it / G) * BC;
+    // the two 32-row halves one after the other (overlapping them would need
+    // a second set of score registers)
+#pragma unroll 1
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qb0 = q0 + qb * 32;
+      // wave-uniform skips: rows past Nq, or no row of the half sees the
+      // wave's first key
+      if (qb0 >= Nq || (CAUSAL && qb0 + 31 + off < k0w)) continue;
+      LDS_AS const char* qh = qt + qb * 32 * RSX;
+      LDS_AS const char* oh = ot + qb * 32 * RSX;
+      f32x16 s[KBW], dp[KBW];
+#pragma unroll
+      for (int kb = 0; kb < KBW; ++kb) s[kb] = dp[kb] = (f32x16){};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds) {
+        const bf16x8 a = lds_b128(qh + qoff_l + ds * 32);
+        const bf16x8 b = lds_b128(oh + qoff_l + ds * 32);
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          s[kb] = mfma(a, kf[kb][ds], s[kb]);
+          dp[kb] = mfma(b, vf[kb][ds], dp[kb]);
+        }
+      }
+      // causal: some row of the half misses one of the wave's keys
+      const bool need_mask = CAUSAL && k0w + KPW - 1 > qb0 + off;
+      u32x4 pp[KBW][2], dsp[KBW][2];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // (L2, D) of the lane's rows qb*32 + 8g + 4h + r, r = 0 .. 3
+        LDS_AS const f32x4* src = (LDS_AS const f32x4*)(lt + (qb * 32 + 8 * g + 4 * h) * 8);
+        const f32x4 la = src[0], lb = src[1];
+        const float l2v[4] = {la[0], la[2], lb[0], lb[2]}, ddv[4] = {la[1], la[3], lb[1], lb[3]};
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          const int key = k0w + kb * 32 + (lane & 31);
+#pragma unroll
+          for (int r = 0; r < 4; r += 2) {
+            float pr[2], dsv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              float sv = s[kb][4 * g + r + u];
+              if (need_mask && key > qb0 + 8 * g + 4 * h + r + u + off) sv = NEG_INF;
+              pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -l2v[r + u]));
+              dsv[u] = pr[u] * (dp[kb][4 * g + r + u] - ddv[r + u]);
+            }
+            pp[kb][g / 2][2 * (g % 2) + r / 2] = pack_bf16(pr[0], pr[1]);
+            dsp[kb][g / 2][2 * (g % 2) + r / 2] = pack_bf16(dsv[0], dsv[1]);
+          }
+        }
+      }
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = v_frag<RSX>(oh + toff_l, ps, db);
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) dv[kb][db] = mfma(a, __builtin_bit_cast(bf16x8, pp[kb][ps]), dv[kb][db]);
+        }
+#pragma unroll
+      for (int ps = 0; ps < 2; ++ps)
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          const bf16x8 a = v_frag<RSX>(qh + toff_l, ps, db);
+#pragma unroll
+          for (int kb = 0; kb < KBW; ++kb) dk[kb][db] = mfma(a, __builtin_bit_cast(bf16x8, dsp[kb][ps]), dk[kb][db]);
+        }
+    }
+  };
+
+  auto iteration = [&](int it, auto par) {
+    using other = std::integral_constant<int, 1 - decltype(par)::value>;
+    vm_wait<0>();
+    __syncthreads();
+    if (it + 1 < total) issue(it + 1, other{});
+    if (has_keys) {
+      const int q0 = (ntq - 1 - it / G) * BC;
+      if (!CAUSAL || q0 + BC - 1 + off >= k0w) compute(it, par);
+    }
+  };
+  if (total > 0) issue(0, P0{});
+  for (int it = 0; it < total; it += 2) {
+    iteration(it, P0{});
+    if (it + 1 < total) iteration(it + 1, P1{});
+  }
+  vm_wait<0>();
+
+#pragma unroll
+  for (int kb = 0; kb < KBW; ++kb) {
+    const int key = k0w + kb * 32 + (lane & 31);
+    if (key >= Nk) continue;
+    const size_t krow = kvoff + (size_t)key * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d0 = db * 32 + i4 * 8 + h * 4;
+        bf16x4 rk, rv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          rk[e] = (__bf16)(dk[kb][db][i4 * 4 + e] * scale);
+          rv[e] = (__bf16)dv[kb][db][i4 * 4 + e];
+        }
+        *(bf16x4*)(dK + krow + d0) = rk;
+        *(bf16x4*)(dV + krow + d0) = rv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- launchers
+#define FA_INST_DQ(DD, CC, NN)                                                                                  \
+  template __global__ void fa_bwd_dq_kernel<DD, CC, NN>(                                                       \
+      const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, \
+      const __bf16* __restrict__, const float* __restrict__, float* __restrict__, __bf16* __restrict__, fa_plan_t,  \
+      float, float);
+// (head dim, causal, waves per workgroup)
+#define FA_DQ_VARIANTS(X)                                                                                    \
+  X(64, false, 1) X(64, false, 2) X(64, false, 4) X(64, false, 8) X(64, true, 1) X(64, true, 2)                \
+  X(64, true, 4) X(64, true, 8) X(128, false, 1) X(128, false, 2) X(128, false, 4) X(128, false, 8)            \
+  X(128, true, 1) X(128, true, 2) X(128, true, 4) X(128, true, 8) X(256, false, 1) X(256, false, 2)            \
+  X(256, false, 4) X(256, true, 1) X(256, true, 2) X(256, true, 4)
+FA_DQ_VARIANTS(FA_INST_DQ)
+
+#define FA_INST_DKDV(DD, CC, NN, KK)                                                                           \
+  template __global__ void fa_bwd_dkdv_kernel<DD, CC, NN, KK>(                                                \
+      const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, \
+      const float* __restrict__, __bf16* __restrict__, __bf16* __restrict__, fa_kvplan_t, float, float);
+// (head dim, causal, waves per workgroup, 32-key blocks per wave)
+#define FA_DKDV_VARIANTS(X)                                                                                  \
+  X(64, false, 1, 2) X(64, false, 2, 2) X(64, false, 4, 2) X(64, true, 1, 2) X(64, true, 2, 2)                 \
+  X(64, true, 4, 2) X(128, false, 1, 1) X(128, false, 2, 1) X(128, false, 4, 1) X(128, false, 8, 1)            \
+  X(128, true, 1, 1) X(128, true, 2, 1) X(128, true, 4, 1) X(128, true, 8, 1) X(256, false, 1, 1)              \
+  X(256, false, 2, 1) X(256, true, 1, 1) X(256, true, 2, 1)
+FA_DKDV_VARIANTS(FA_INST_DKDV)
+
+int bwd_keys_per_wave(int d) { return d == 64 ? 64 : 32; }
+
+int bwd_dkdv_max_waves(int d) { return d == 64 ? 4 : d == 128 ? 8 : 2; }
+
+int bwd_dq_max_waves(int d) { return d == 256 ? 4 : 8; }
+
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* ld, const fa_plan_t& pq, const fa_kvplan_t& pk, int d,
+                      float c, float scale, hipStream_t stream) {
+  bool done = false;
+#define FA_CASE_DQ(DD, CC, NN)                                                                             \
+  if (!done && d == DD && (pq.causal != 0) == CC && pq.nw == NN) {                                          \
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DD, CC, NN>), dim3((unsigned)pq.nwg), dim3(64 * NN), 0, stream,       \
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o,                  \
+                       (const __bf16*)dout, lse, ld, (__bf16*)dq, pq, c, scale);                              \
+    done = true;                                                                                            \
+  }
+  FA_DQ_VARIANTS(FA_CASE_DQ)
+#undef FA_CASE_DQ
+  if (!done) return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  done = false;
+#define FA_CASE_DKDV(DD, CC, NN, KK)                                                                        \
+  if (!done && d == DD && (pk.causal != 0) == CC && pk.nw == NN && pk.kpw == 32 * KK) {                     \
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DD, CC, NN, KK>), dim3((unsigned)pk.nwg), dim3(64 * NN), 0, stream, \
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld,          \
+                       (__bf16*)dk, (__bf16*)dv, pk, c, scale);                                               \
+    done = true;                                                                                            \
+  }
+  FA_DKDV_VARIANTS(FA_CASE_DKDV)
+#undef FA_CASE_DKDV
+  if (!done) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace fa

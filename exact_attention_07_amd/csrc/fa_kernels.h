@@ -38,6 +38,19 @@ hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, void*
                               float* descale, unsigned* amax, const float* signs, int B, int Hq, int Hkv, int Nq,
                               int Nk, int d, hipStream_t stream);
 
+// Backward pass: keys per wave and most waves per workgroup of the dK/dV
+// kernel, most waves per workgroup of the dQ kernel, for head dimension d.
+int bwd_keys_per_wave(int d);
+int bwd_dkdv_max_waves(int d);
+int bwd_dq_max_waves(int d);
+
+// Enqueue the backward pass: the dQ kernel (plan pq; it also writes the
+// per-row (LSE log2 e, rowsum(dO o O)) pairs into ld, [B][Hq][Nq][2] fp32),
+// then the dK/dV kernel (plan pk), which reads them.  c = scale * log2(e).
+hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      void* dq, void* dk, void* dv, float* ld, const fa_plan_t& pq, const fa_kvplan_t& pk, int d,
+                      float c, float scale, hipStream_t stream);
+
 }  // namespace fa
 
 #endif

@@ -151,4 +151,69 @@ FA_HD inline void fa_split_tiles(const fa_plan_t& p, int split, int nt, int& t0,
   if (t0 > t1) t0 = t1;
 }
 
+// ---------------------------------------------------------------- backward: key blocks
+// The dK/dV kernel of the backward pass owns keys instead of queries: a
+// wave keeps `kpw` consecutive keys of one key/value head (their K and V
+// rows and their dK, dV accumulators) and streams the query rows of every
+// query head of the GQA group past them, so that dK and dV, which sum over
+// all those query heads, are each written by exactly one wave.  A workgroup
+// holds `nw` waves over consecutive keys (`kpb` = kpw * nw keys), which
+// share every query tile staged in LDS.  Workgroups are numbered
+// group-major (group = batch, kv head) with the key blocks of a group
+// consecutive, first key block first: with causal masking the first keys
+// are seen by the most query rows, so the heaviest workgroups start first.
+// The same XCD remap as above keeps the workgroups of one head on one L2.
+struct fa_kvplan_t {
+  int B, Hq, Hkv, Nq, Nk;
+  int causal;
+  int G;     // Hq / Hkv
+  int kpw;   // keys per wave
+  int nw;    // waves per workgroup
+  int kpb;   // keys per workgroup
+  int nkb;   // key blocks per key/value head: ceil(Nk / kpb)
+  int xcd;
+  long long nwg;
+};
+
+FA_HD inline fa_kvplan_t fa_make_kvplan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int kpw, int nw) {
+  fa_kvplan_t p;
+  p.B = B; p.Hq = Hq; p.Hkv = Hkv; p.Nq = Nq; p.Nk = Nk; p.causal = causal;
+  p.G = Hq / Hkv;
+  p.kpw = kpw;
+  p.nw = nw;
+  p.kpb = kpw * nw;
+  p.nkb = (Nk + p.kpb - 1) / p.kpb;
+  p.nwg = (long long)B * Hkv * p.nkb;
+  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  return p;
+}
+
+struct fa_kvwork_t {
+  int b, hkv, k0;  // batch, kv head, first key of the workgroup
+};
+
+// Workgroup hardware id -> its key block; a bijection of [0, nwg) onto the
+// (group, key block) pairs.
+FA_HD inline fa_kvwork_t fa_kv_decode(const fa_kvplan_t& p, long long id) {
+  const long long L = p.xcd ? (id % 8) * (p.nwg / 8) + id / 8 : id;
+  fa_kvwork_t w;
+  const long long g = L / p.nkb;
+  w.k0 = (int)(L % p.nkb) * p.kpb;
+  w.hkv = (int)(g % p.Hkv);
+  w.b = (int)(g / p.Hkv);
+  return w;
+}
+
+// Query tiles of `bq` rows a key block starting at key k0 must visit: tiles
+// [first, ntq).  Causal: query i sees key j iff j <= i + Nk - Nq, so rows
+// below k0 - (Nk - Nq) see none of the block's keys.
+FA_HD inline void fa_kv_query_tiles(const fa_kvplan_t& p, int k0, int bq, int& first, int& ntq) {
+  ntq = (p.Nq + bq - 1) / bq;
+  first = 0;
+  if (p.causal) {
+    const long long r = (long long)k0 - ((long long)p.Nk - p.Nq);
+    if (r > 0) first = r >= p.Nq ? ntq : (int)(r / bq);
+  }
+}
+
 #endif  // FA_PLAN_H

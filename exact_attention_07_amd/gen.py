@@ -6,7 +6,8 @@ the fp64 oracle consume what it returns.
 
 Every tensor comes from its own numpy Generator seeded with
 SeedSequence([config_or_seed, tensor_id]); tensor ids: Q=0, K=1, V=2,
-outlier channels=3, Q outliers=4, K outliers=5, Hadamard signs=6.  Values are
+outlier channels=3, Q outliers=4, K outliers=5, Hadamard signs=6, the
+upstream gradient dO of the backward pass=7.  Values are
 standard normal fp32, rounded to bf16 (nearest, ties to even) unless the
 tensor dtype is fp32.
 
@@ -27,7 +28,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-TID_Q, TID_K, TID_V, TID_CHANNELS, TID_QOUT, TID_KOUT, TID_SIGNS = range(7)
+TID_Q, TID_K, TID_V, TID_CHANNELS, TID_QOUT, TID_KOUT, TID_SIGNS, TID_DO = range(8)
 
 
 @dataclass(frozen=True)
@@ -115,6 +116,12 @@ def make_inputs(w: Workload, seed_key=(0,)) -> dict:
     else:
         out.update(q=f32_to_bf16_bits(q), k=f32_to_bf16_bits(k), v=f32_to_bf16_bits(v))
     return out
+
+
+def make_dout(w: Workload, seed_key=(0,)) -> np.ndarray:
+    """Upstream gradient dL/dO for the backward pass: standard normal, q's
+    shape, as bf16 bit patterns (uint16)."""
+    return f32_to_bf16_bits(_normal(seed_key, TID_DO, (w.B, w.Hq, w.Nq, w.d)))
 
 
 # A decoding step of a GQA model over a long context (one new query per

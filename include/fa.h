@@ -1,5 +1,5 @@
 /*
- * fa.h -- C ABI of libfa.so, a fused exact-attention forward pass for AMD
+ * fa.h -- C ABI of libfa.so, fused exact-attention forward and backward passes for AMD
  * Instinct MI355X (gfx950).
  *
  * What is computed (the definition on "FlashAttention (SV)", section
@@ -162,6 +162,45 @@ fa_status fa_fp8_prepare(const void* q, const void* k, const void* v, void* q8, 
 fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale,
                      void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                      float scale, int causal, void* stream);
+
+/*
+ * Backward pass (bfloat16): the gradients of L with respect to Q, K and V for
+ * an upstream gradient dout = dL/dO of fa_fwd's output.  The pages report
+ * the method's training speed-ups ("FlashAttention-4震撼发布",
+ * FlashAttention-2 list; "FlashAttention (SV)", section "Prestanda och
+ * fördelar") but print no backward algorithm; what is computed is the
+ * derivative of the definition above, with P = softmax(scale Q K^T):
+ *
+ *     dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,
+ *     dS = P o (dP - D),   dQ = scale dS K,   dK = scale dS^T Q,
+ *
+ * per (b, query head); with GQA the gradients of a key/value head are summed
+ * over the query heads that read it.  P is recomputed tile by tile from q, k
+ * and the forward pass's lse (none of the N x N matrices reaches memory).
+ *
+ *   q, k, v    the forward pass's inputs (bf16, layouts as for fa_fwd)
+ *   o, lse     its outputs: O (bf16) and the natural-log LSE (fp32), as
+ *              fa_fwd wrote them for the same q, k, v, scale and causal
+ *   dout       dL/dO, bf16, q's layout
+ *   dq         out: dL/dQ, bf16, q's layout
+ *   dk, dv     out: dL/dK, dL/dV, bf16, k's layout (every element written)
+ *   workspace  device memory of at least fa_bwd_workspace_size(...) bytes
+ *              (8 bytes per query row: B * Hq * Nq * 8), 16-byte aligned,
+ *              owned by the caller and not shared with a call in flight.
+ *              It holds the per-row pair (LSE log2(e), D) between the two
+ *              kernels; its contents on entry do not matter.
+ * Products run on bf16 MFMA with fp32 accumulation; P and dS multiply in
+ * bf16; the gradients are rounded to bf16 (nearest even).  D is formed from
+ * the bf16 O.  Rows that see no key (LSE = -inf) contribute nothing.
+ * Errors: those of fa_fwd (every pointer except the workspace required);
+ * FA_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ * fa_bwd_workspace_size returns 0 for arguments fa_bwd would reject.
+ */
+size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal);
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv,
+                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -91,7 +91,44 @@ static void check_split(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int 
   }
 }
 
+// Backward key-block plans: every (b, kv head, key) is owned by exactly one
+// wave, and every query row that sees one of a workgroup's keys lies in the
+// query tiles the workgroup visits.
+static void check_kvplan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int kpw, int nw) {
+  fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
+  CHECK(p.kpb == kpw * nw && (long long)p.nkb * p.kpb >= Nk && (long long)(p.nkb - 1) * p.kpb < Nk);
+  std::vector<int> cover((size_t)B * Hkv * Nk, 0);
+  std::set<std::tuple<int, int, int>> seen;
+  for (long long id = 0; id < p.nwg; ++id) {
+    fa_kvwork_t w = fa_kv_decode(p, id);
+    CHECK(w.b >= 0 && w.b < B && w.hkv >= 0 && w.hkv < Hkv && w.k0 >= 0 && w.k0 < Nk && w.k0 % p.kpb == 0);
+    CHECK(seen.insert({w.b, w.hkv, w.k0}).second);
+    for (int j = w.k0; j < w.k0 + p.kpb && j < Nk; ++j) cover[((size_t)w.b * Hkv + w.hkv) * Nk + j]++;
+    int first, ntq;
+    fa_kv_query_tiles(p, w.k0, 64, first, ntq);
+    CHECK(ntq == (Nq + 63) / 64 && 0 <= first && first <= ntq);
+    for (int i = 0; i < Nq; ++i) {
+      bool sees = !causal || w.k0 <= i + Nk - Nq;  // the block's first key is its most visible one
+      if (sees) CHECK(i / 64 >= first);
+    }
+    if (first > 0) CHECK(causal && (first * 64 - 1) + Nk - Nq < w.k0);  // the skipped rows see none of the keys
+  }
+  CHECK((long long)seen.size() == p.nwg);
+  for (int c : cover) CHECK(c == 1);
+  if (!p.xcd && p.nkb > 1) CHECK(fa_kv_decode(p, 0).k0 == 0 && fa_kv_decode(p, 1).k0 == p.kpb);
+}
+
 int main() {
+  for (int causal = 0; causal < 2; ++causal)
+    for (int nw : {1, 2, 4})
+      for (int kpw : {32, 64}) {
+        check_kvplan(2, 32, 8, 8192, 8192, causal, kpw, nw);
+        check_kvplan(1, 6, 2, 257, 300, causal, kpw, nw);
+        check_kvplan(2, 4, 1, 1000, 70, causal, kpw, nw);
+        check_kvplan(1, 2, 2, 150, 40, causal, kpw, nw);
+        check_kvplan(1, 3, 3, 40, 150, causal, kpw, nw);
+        check_kvplan(3, 5, 5, 1, 100, causal, kpw, nw);
+      }
   for (int causal = 0; causal < 2; ++causal)
     for (int tps : {1, 2, 3, 7, 100}) {
       check_split(2, 8, 2, 1, 1000, causal, 4, tps);    // decoding: one query, GQA 4

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.fa_abi_version() == 1
-    for s in range(9):
+    for s in range(10):
         assert len(lib.fa_status_string(s)) > 0
     assert lib.fa_status_string(123) == b"unknown status"
 
@@ -147,3 +147,36 @@ def test_splitkv_workspace_size(lib):
 ])
 def test_splitkv_rejects_invalid_arguments(lib, kw, status):
     assert call_split(lib, **kw) == status
+
+
+BWD_GOOD = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, B=1, Hq=4, Hkv=2, Nq=100, Nk=300, d=128,
+                scale=0.1, causal=1, ws=P, wsb=1 << 30)
+
+
+def call_bwd(lib, **kw):
+    a = dict(BWD_GOOD)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["Hq"],
+                      a["Hkv"], a["Nq"], a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], a["ws"],
+                      ctypes.c_size_t(a["wsb"]), None)
+
+
+def test_bwd_workspace_size(lib):
+    f = lib.fa_bwd_workspace_size
+    f.restype = ctypes.c_size_t
+    # one (LSE log2 e, D) pair of floats per query row
+    assert f(1, 4, 2, 100, 300, 128, 1) == 4 * 100 * 8
+    assert f(2, 32, 8, 8192, 8192, 128, 1) == 2 * 32 * 8192 * 8
+    assert f(1, 4, 3, 100, 300, 128, 1) == 0 and f(1, 4, 2, 100, 300, 96, 0) == 0 and f(1, 4, 2, 0, 300, 128, 0) == 0
+    assert f(1, 4, 2, 100, 300, 128, 2) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(do=None), 1), (dict(lse=None), 1), (dict(dq=None), 1),
+    (dict(dk=None), 1), (dict(dv=None), 1), (dict(B=0), 2), (dict(Nq=0), 2), (dict(d=80), 3), (dict(Hq=7), 4),
+    (dict(dk=P + 4), 5), (dict(lse=P + 4), 5), (dict(scale=0.0), 6), (dict(scale=float("nan")), 6),
+    (dict(causal=2), 8), (dict(ws=None), 9), (dict(wsb=4 * 100 * 8 - 1), 9), (dict(ws=P + 8), 9),
+    (dict(Nq=(1 << 31) // (4 * 256), d=256), 2),
+])
+def test_bwd_rejects_invalid_arguments(lib, kw, status):
+    assert call_bwd(lib, **kw) == status

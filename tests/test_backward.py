@@ -1,0 +1,194 @@
+"""GPU parity of fa_bwd (dQ, dK, dV) against the fp64 oracle's gradients.
+
+The HIP path runs fa_fwd (O, LSE) and then fa_bwd on seeded bf16 inputs;
+the oracle differentiates the definition in fp64 on the same bf16 values
+(attention_backward_fp64).  Shapes cover MHA, GQA and MQA, causal and not,
+head dimensions 64, 128 and 256, ragged query and key counts spanning
+several tiles, rows that see no key (causal with Nq > Nk), a single query
+row, and a GQA head group at the full long-context size.
+
+Tolerance (bf16 arithmetic, unit roundoff u = 2^-9): P and dS enter their
+products rounded to bf16 (relative error u per term), D is formed from the
+bf16 O (error u |dO||O| per row), and each gradient is rounded to bf16
+(u relative).  The products are accumulated in fp32.  With random-sign terms
+these errors add in quadrature, so the root-mean-square error of a gradient
+stays a small multiple of u times its root-mean-square value, and the largest
+error a small multiple of u times its largest magnitude:
+    rms|g - g_ref| <= 2^-7 rms|g_ref|,   max|g - g_ref| <= 2^-6 max|g_ref|
+(4u and 8u; measured: rms 1.1u - 1.4u, max at most 3u on these shapes).
+Sharper softmax rows (large scores) weaken this for dQ and dK: dS = P (dP - D)
+then cancels, and the rounding of O to bf16 inside D stops being small
+against it.  The case with outlier channels measures that effect and takes
+twice the bounds (there the exact gradient with D formed from bf16(O) alone
+is 3.5u from the true one in rms for dQ).
+"""
+import math
+
+import numpy as np
+import pytest
+
+from exact_attention_07_amd import gen
+from oracle import attention_backward_fp64
+from tests.gpu_util import out_to_f64, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+RMS_REL = 2.0 ** -7
+MAX_REL = 2.0 ** -6
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from exact_attention_07_amd import api as a
+    a.lib()
+    return a
+
+
+def compare_grad(g, ref, what, rms_rel=RMS_REL, max_rel=MAX_REL):
+    assert g.shape == ref.shape, (g.shape, ref.shape)
+    assert np.isfinite(g).all(), f"{what}: non-finite gradient"
+    err = np.abs(g - ref)
+    rms_ref = math.sqrt(float(np.mean(ref * ref)))
+    max_ref = float(np.abs(ref).max())
+    rms_err = math.sqrt(float(np.mean(err * err)))
+    print(f"  {what}: rms err / rms ref = {rms_err / max(rms_ref, 1e-300):.2e}, "
+          f"max err / max ref = {err.max() / max(max_ref, 1e-300):.2e}", flush=True)
+    if max_ref == 0.0:
+        assert err.max() == 0.0, f"{what}: nonzero gradient where the reference is 0"
+        return
+    assert rms_err <= rms_rel * rms_ref, f"{what}: rms err {rms_err:.3e} > {rms_rel} x rms ref {rms_ref:.3e}"
+    assert err.max() <= max_rel * max_ref, f"{what}: max err {err.max():.3e} > {max_rel} x max ref {max_ref:.3e}"
+
+
+def run_backward(api, w, x, do_bits):
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    do = to_device(do_bits, "bf16")
+    o, lse = api.attention(q, k, v, causal=w.causal, scale=w.softmax_scale)
+    dq, dk, dv = api.attention_backward(q, k, v, o, lse, do, causal=w.causal, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    return out_to_f64(dq), out_to_f64(dk), out_to_f64(dv)
+
+
+def check(api, w, seed, rms_rel=RMS_REL, max_rel=MAX_REL):
+    x = gen.make_inputs(w, seed)
+    do_bits = gen.make_dout(w, seed)
+    print(f"case: backward {w.name}", flush=True)
+    dq, dk, dv = run_backward(api, w, x, do_bits)
+    qf, kf, vf = (to_f64(x[t], "bf16") for t in "qkv")
+    rq, rk, rv = attention_backward_fp64(qf, kf, vf, to_f64(do_bits, "bf16"), w.softmax_scale, w.causal)
+    compare_grad(dq, rq, f"{w.name} dQ", rms_rel, max_rel)
+    compare_grad(dk, rk, f"{w.name} dK", rms_rel, max_rel)
+    compare_grad(dv, rv, f"{w.name} dV", rms_rel, max_rel)
+
+
+CASES = [
+    # B, Hq, Hkv, Nq, Nk, d
+    (1, 2, 2, 64, 64, 128),       # one tile each way
+    (1, 4, 2, 300, 300, 128),     # GQA 2, ragged, several tiles
+    (2, 8, 2, 257, 200, 128),     # GQA 4, Nq > Nk
+    (1, 4, 1, 150, 333, 128),     # MQA, Nq < Nk
+    (1, 3, 3, 129, 700, 64),      # d = 64
+    (2, 4, 2, 190, 190, 64),      # d = 64, GQA
+    (1, 2, 1, 100, 260, 256),     # d = 256, MQA
+    (1, 2, 2, 1, 500, 128),       # a single query row
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(map(str, c)))
+def test_backward_matches_the_oracle(api, case, causal):
+    B, Hq, Hkv, Nq, Nk, d = case
+    w = gen.workload(B, Hq, Hkv, Nq, Nk, d, causal=causal)
+    check(api, w, (sum(case), int(causal), 21))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_single_key(api, causal):
+    """One key: every visible row's softmax is the constant 1, so dQ and dK
+    are exactly 0 and dV is the sum of dO over the rows that see the key.
+    The kernels reach the zeros as dP - D with D formed from the bf16 O (here
+    O = V exactly, D accumulated in a different order than dP), so dQ and dK
+    carry rounding noise bounded by scale |dP - D| max|K| <= scale * d * 2^-24
+    max_i sum_c |dO_ic V_c| max|K| per element (fp32 accumulation of d
+    exact products); dV is checked like the other cases."""
+    w = gen.workload(1, 2, 2, 500, 1, 64, causal=causal)
+    x = gen.make_inputs(w, (25, int(causal)))
+    do_bits = gen.make_dout(w, (25, int(causal)))
+    dq, dk, dv = run_backward(api, w, x, do_bits)
+    qf, kf, vf = (to_f64(x[t], "bf16") for t in "qkv")
+    dof = to_f64(do_bits, "bf16")
+    rq, rk, rv = attention_backward_fp64(qf, kf, vf, dof, w.softmax_scale, causal)
+    assert (rq == 0).all() and (rk == 0).all()
+    bound = w.softmax_scale * 64 * 2.0 ** -24 * np.abs(dof * vf).sum(axis=-1).max() * np.abs(kf).max()
+    assert np.abs(dq).max() <= bound, (np.abs(dq).max(), bound)
+    # dK sums dS Q over the rows: at most 500 rows of such noise times max|Q| / max|K|
+    assert np.abs(dk).max() <= 500 * bound * np.abs(qf).max() / np.abs(kf).max()
+    compare_grad(dv, rv, "dV")
+
+
+def test_backward_outlier_channels(api):
+    # a few feature channels of Q and K eight times larger (sharper softmax
+    # rows): twice the bounds, for the reason given at the top
+    w = gen.workload(1, 4, 2, 256, 256, 256, causal=False, outlier_channel_frac=0.02)
+    check(api, w, (22,), 2 * RMS_REL, 2 * MAX_REL)
+
+
+def test_backward_rows_without_keys_get_zero_dq(api):
+    # causal with Nq > Nk: the first Nq - Nk rows see no key; their dQ is 0 and
+    # they add nothing to dK, dV
+    w = gen.workload(1, 2, 1, 130, 40, 128, causal=True)
+    x = gen.make_inputs(w, (23,))
+    do_bits = gen.make_dout(w, (23,))
+    dq, dk, dv = run_backward(api, w, x, do_bits)
+    assert (dq[:, :, : 130 - 40] == 0).all()
+    qf, kf, vf = (to_f64(x[t], "bf16") for t in "qkv")
+    rq, rk, rv = attention_backward_fp64(qf, kf, vf, to_f64(do_bits, "bf16"), w.softmax_scale, True)
+    compare_grad(dk, rk, "dK")
+    compare_grad(dv, rv, "dV")
+
+
+def test_backward_full_size_head_group(api):
+    """The long-context GQA shape (B2 Hq32 Hkv8 N8192 d128, causal) in the
+    launch configuration of the full problem; the oracle checks one head group
+    (batch 1, key/value head 5 and its 4 query heads), sliced from the same
+    inputs."""
+    w, x = gen.make_config(3)
+    do_bits = gen.make_dout(w, (3,))
+    print(f"case: backward full size {w.name}", flush=True)
+    dq, dk, dv = run_backward(api, w, x, do_bits)
+    b, hk, G = 1, 5, w.Hq // w.Hkv
+    hs = slice(hk * G, hk * G + G)
+    qf = to_f64(x["q"][b:b + 1, hs], "bf16")
+    kf = to_f64(x["k"][b:b + 1, hk:hk + 1], "bf16")
+    vf = to_f64(x["v"][b:b + 1, hk:hk + 1], "bf16")
+    dof = to_f64(do_bits[b:b + 1, hs], "bf16")
+    rq, rk, rv = attention_backward_fp64(qf, kf, vf, dof, w.softmax_scale, True)
+    compare_grad(dq[b:b + 1, hs], rq, "full dQ")
+    compare_grad(dk[b:b + 1, hk:hk + 1], rk, "full dK")
+    compare_grad(dv[b:b + 1, hk:hk + 1], rv, "full dV")
+
+
+def test_backward_agrees_with_torch_autograd_on_the_cpu(api):
+    """A second reference for the same quantity: autograd of the plain fp64
+    attention formula on the CPU (the products of the definition), on one
+    small GQA case."""
+    w = gen.workload(1, 4, 2, 96, 130, 64, causal=True)
+    x = gen.make_inputs(w, (24,))
+    do_bits = gen.make_dout(w, (24,))
+    dq, dk, dv = run_backward(api, w, x, do_bits)
+    q, k, v = (torch.from_numpy(to_f64(x[t], "bf16")).requires_grad_() for t in "qkv")
+    do = torch.from_numpy(to_f64(do_bits, "bf16"))
+    kr, vr = k.repeat_interleave(2, dim=1), v.repeat_interleave(2, dim=1)
+    s = (q @ kr.transpose(-1, -2)) * w.softmax_scale
+    i = torch.arange(96)[:, None]
+    j = torch.arange(130)[None, :]
+    s = s.masked_fill(j > i + (130 - 96), float("-inf"))
+    o = torch.softmax(s, dim=-1) @ vr
+    o.backward(do)
+    compare_grad(dq, q.grad.numpy(), "autograd dQ")
+    compare_grad(dk, k.grad.numpy(), "autograd dK")
+    compare_grad(dv, v.grad.numpy(), "autograd dV")
