@@ -19,6 +19,14 @@ on the stream the kernels run on.  Prints one JSON line on stdout
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
             sample of the same workload (whole heads), as a reported baseline
 
+--config backward measures the backward pass (fa_bwd_dq then fa_bwd_dkdv:
+dQ, dK, dV for a seeded upstream gradient dO, probabilities recomputed from
+the saved LSE) on the same causal GQA workload, O and LSE from one fa_fwd
+before timing.  value = 10*B*Hq*Nq*Nk*d (halved when causal) per step, the
+five matrix products of the gradient; the roofline is the dK/dV kernel with
+its four of them (S, dP, dV, dK) against its own launch time.  The dQ kernel
+recomputes S and dP, so only its dQ product counts as algorithmic work.
+
 --config decode measures the key-split path (fa_fwd_splitkv: parts over key
 ranges merged on the GPU) on a GQA decoding step, B=8 sequences, Hq=32,
 Hkv=8, one query each over Nk=32768 keys, d=128.  That path is bound by HBM
@@ -46,11 +54,13 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "fp8": 5000.0}
 # only for the sources it was measured on)
 _CSRC = "exact_attention_07_amd/csrc/"
 KERNEL_SOURCES = {
-    "bf16": [_CSRC + f for f in ("fa_fwd.hip", "fa_device.h", "plan.h")],
-    "f32": [_CSRC + f for f in ("fa_fwd.hip", "fa_device.h", "plan.h")],
+    "bf16": [_CSRC + f for f in ("fa_fwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
+    "f32": [_CSRC + f for f in ("fa_fwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
     "fp8": [_CSRC + f for f in ("fa_fwd_fp8.hip", "fa_device.h", "plan.h")],
+    "bwd": [_CSRC + f for f in ("fa_bwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
 }
-KERNEL_NAME = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel"}
+KERNEL_NAME = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel",
+               "bwd": "fa_bwd_dkdv_kernel"}
 
 
 def log(*a):
@@ -65,10 +75,11 @@ def source_hash(dtype: str) -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(cfg: int, dtype: str):
-    """HBM bytes per launch of the attention kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_config{cfg}.txt")
+def load_traffic(tag: str, dtype: str):
+    """HBM bytes per launch of the measured kernel from the committed
+    rocprofv3 counter summary profiles/traffic_<tag>.txt, if it was taken on
+    the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -113,12 +124,142 @@ def cpu_baseline(w, x, budget_s: float):
                       f"(S and P materialised), {t_total:.1f} s"}
 
 
+def cpu_baseline_backward(w, x, dout, budget_s: float):
+    """Time the fp64 gradient oracle on whole (b, h) heads until budget_s elapsed."""
+    from oracle import attention_backward_fp64
+    from oracle.formats import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        threads = os.cpu_count() or 1
+    g = w.Hq // w.Hkv
+    done, flops, t_total = 0, 0.0, 0.0
+    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for b, h in heads:
+        q = bf16_bits_to_f64(x["q"][b:b + 1, h:h + 1])
+        k = bf16_bits_to_f64(x["k"][b:b + 1, h // g:h // g + 1])
+        v = bf16_bits_to_f64(x["v"][b:b + 1, h // g:h // g + 1])
+        do = bf16_bits_to_f64(dout[b:b + 1, h:h + 1])
+        t0 = time.perf_counter()
+        attention_backward_fp64(q, k, v, do, w.softmax_scale, w.causal)
+        t_total += time.perf_counter() - t0
+        done += 1
+        f = 10.0 * w.Nq * w.Nk * w.d
+        flops += f / 2 if w.causal else f
+        if t_total >= budget_s:
+            break
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, fp64 gradient oracle "
+                      f"(P, dP, dS materialised), {t_total:.1f} s"}
+
+
+def bench_backward(args, torch, api, gen):
+    w, x = gen.make_config(3)
+    dout = gen.make_dout(w, (3,))
+    log(f"workload: backward of {w.name}")
+    dev = torch.device("cuda:0")
+
+    def dev_tensor(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = (dev_tensor(a) for a in (x["q"], x["k"], x["v"], dout))
+    stream = torch.cuda.current_stream()
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    api.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(api.bwd_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal) // 4, dtype=torch.float32,
+                     device=dev)
+
+    def stage_dq():
+        api.fa_bwd_dq(q, k, v, o, lse, do, dq, w.softmax_scale, w.causal, ws, stream)
+
+    def stage_dkdv():
+        api.fa_bwd_dkdv(q, k, v, o, lse, do, dk, dv, w.softmax_scale, w.causal, ws, stream)
+
+    for _ in range(args.warmup):
+        stage_dq()
+        stage_dkdv()
+    torch.cuda.synchronize()
+
+    def event():
+        return torch.cuda.Event(enable_timing=True)
+
+    marks = [(event(), event(), event()) for _ in range(args.steps)]
+    e0, e1 = event(), event()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for a, m, b in marks:
+        a.record(stream)
+        stage_dq()
+        m.record(stream)
+        stage_dkdv()
+        b.record(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    dq_ms = sum(a.elapsed_time(m) for a, m, _ in marks) / args.steps
+    dkdv_ms = sum(m.elapsed_time(b) for _, m, b in marks) / args.steps
+    fwd_flops = w.flops()                 # one product pair of the forward pass = 2 products
+    flops = 2.5 * fwd_flops               # S, dP, dV, dK, dQ
+    tflops = flops / (ms * 1e-3) / 1e12
+    dkdv_tflops = 2.0 * fwd_flops / (dkdv_ms * 1e-3) / 1e12   # S, dP, dV, dK
+    dq_exec_tflops = 1.5 * fwd_flops / (dq_ms * 1e-3) / 1e12  # S, dP, dQ as executed
+    log(f"{args.steps} steps: {ms:.4f} ms/step (events), {wall / args.steps * 1e3:.4f} ms/step (wall), "
+        f"{tflops:.1f} TFLOP/s; dQ kernel {dq_ms:.4f} ms ({dq_exec_tflops:.1f} TFLOP/s executed), "
+        f"dK/dV kernel {dkdv_ms:.4f} ms ({dkdv_tflops:.1f} TFLOP/s)")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy calibration: 1 GiB device copy done")
+
+    if args.check:
+        # one query row of dQ against the oracle's gradient of one head (stderr only)
+        from oracle import attention_backward_fp64
+        from oracle.formats import bf16_bits_to_f64
+        b_, h_ = w.B - 1, w.Hq - 1
+        g = w.Hq // w.Hkv
+        rq, rk, rv = attention_backward_fp64(bf16_bits_to_f64(x["q"][b_:b_ + 1, h_:h_ + 1]),
+                                             bf16_bits_to_f64(x["k"][b_:b_ + 1, h_ // g:h_ // g + 1]),
+                                             bf16_bits_to_f64(x["v"][b_:b_ + 1, h_ // g:h_ // g + 1]),
+                                             bf16_bits_to_f64(dout[b_:b_ + 1, h_:h_ + 1]), w.softmax_scale, w.causal)
+        got = dq[b_, h_].float().cpu().numpy()
+        err = np.abs(got - rq[0, 0])
+        log(f"check dQ of head ({b_},{h_}): rms err / rms ref = "
+            f"{np.sqrt((err ** 2).mean()) / np.sqrt((rq ** 2).mean()):.2e}")
+
+    traffic = load_traffic("backward", "bwd")
+    line = {
+        "metric": "attention bwd TFLOP/s + % of MFMA peak (bf16, causal GQA, N=8K, d=128)",
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) Q, K, V, dO; O and LSE from fa_fwd; resident in HBM before timing)",
+        "config": {"workload": "backward of " + w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
+                   "d": w.d, "causal": w.causal, "kernel": KERNEL_NAME["bwd"],
+                   "steps_in_a_step": "fa_bwd_dq (dQ, D, LSE log2 e) + fa_bwd_dkdv (dK, dV)"},
+        "roofline": {"bound": "mfma", "achieved": round(dkdv_tflops, 2), "peak": PEAK_TFLOPS["bf16"],
+                     "unit": "TFLOP/s", "frac": round(dkdv_tflops / PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
+                     "kernel_ms": round(dkdv_ms, 5)},
+        "dq_kernel": {"ms": round(dq_ms, 5), "executed_tflops": round(dq_exec_tflops, 2),
+                      "algorithmic_tflops": round(0.5 * fwd_flops / (dq_ms * 1e-3) / 1e12, 2)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_backward(w, x, dout, args.cpu_budget)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="3", help="standing workload 1..5, or decode")
+    ap.add_argument("--config", default="3", help="standing workload 1..5, decode or backward")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="compare sampled rows with the oracle (stderr)")
@@ -134,6 +275,9 @@ def main():
     import torch
     from exact_attention_07_amd import api, gen
 
+    if args.config == "backward":
+        bench_backward(args, torch, api, gen)
+        return
     cfg = args.config if args.config == "decode" else int(args.config)
     args.config = cfg
     w, x = gen.make_config(cfg)
@@ -260,7 +404,7 @@ def main():
         return
 
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(args.config, w.dtype)
+    traffic = load_traffic(f"config{args.config}", w.dtype)
     data = "synthetic (seeded N(0,1), generated on the host, resident in HBM before timing)"
     if w.dtype == "fp8":
         data = ("synthetic (seeded N(0,1) bf16, Q and K with +-50 outliers at p=0.001; quantised to e4m3 "

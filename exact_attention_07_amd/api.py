@@ -50,6 +50,10 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
     L.fa_bwd.restype = ctypes.c_int
+    L.fa_bwd_dq.argtypes = [vp] * 7 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
+    L.fa_bwd_dq.restype = ctypes.c_int
+    L.fa_bwd_dkdv.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
+    L.fa_bwd_dkdv.restype = ctypes.c_int
     L.fa_bwd_workspace_size.argtypes = [i] * 7
     L.fa_bwd_workspace_size.restype = ctypes.c_size_t
     L.fa_status_string.argtypes = [ctypes.c_int]
@@ -243,8 +247,7 @@ def bwd_workspace_size(B, Hq, Hkv, Nq, Nk, d, causal: bool) -> int:
     return int(lib().fa_bwd_workspace_size(B, Hq, Hkv, Nq, Nk, d, int(bool(causal))))
 
 
-def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None) -> None:
-    """bf16 backward pass: gradients into caller-allocated dq (q's shape), dk, dv (k's shape)."""
+def _bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace):
     import torch
     B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v, o, lse)
     for t in (q, k, v, o, do, dq, dk, dv):
@@ -262,9 +265,28 @@ def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspac
     if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
         raise ValueError("workspace must be a contiguous GPU tensor")
     nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return (B, Hq, Hkv, Nq, Nk, d), nbytes
+
+
+def fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale: float, causal: bool, workspace, stream=None) -> None:
+    """bf16 backward pass: gradients into caller-allocated dq (q's shape), dk, dv (k's shape)."""
+    dims, nbytes = _bwd_args(q, k, v, o, lse, do, dq, dk, dv, workspace)
     _check(lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
-                        B, Hq, Hkv, Nq, Nk, d, float(scale), int(bool(causal)), _ptr(workspace), nbytes,
-                        _stream(stream)), "fa_bwd")
+                        *dims, float(scale), int(bool(causal)), _ptr(workspace), nbytes, _stream(stream)), "fa_bwd")
+
+
+def fa_bwd_dq(q, k, v, o, lse, do, dq, scale: float, causal: bool, workspace, stream=None) -> None:
+    """First stage of fa_bwd: dq, and the per-row (LSE log2 e, D) pairs into the workspace."""
+    dims, nbytes = _bwd_args(q, k, v, o, lse, do, dq, k, v, workspace)
+    _check(lib().fa_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), *dims, float(scale),
+                           int(bool(causal)), _ptr(workspace), nbytes, _stream(stream)), "fa_bwd_dq")
+
+
+def fa_bwd_dkdv(q, k, v, o, lse, do, dk, dv, scale: float, causal: bool, workspace, stream=None) -> None:
+    """Second stage of fa_bwd: dk and dv from the workspace fa_bwd_dq filled (o, lse: shape checks only)."""
+    dims, nbytes = _bwd_args(q, k, v, o, lse, do, q, dk, dv, workspace)
+    _check(lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv), *dims, float(scale),
+                             int(bool(causal)), _ptr(workspace), nbytes, _stream(stream)), "fa_bwd_dkdv")
 
 
 def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float | None = None, stream=None):

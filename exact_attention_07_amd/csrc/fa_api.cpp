@@ -218,27 +218,78 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int 
   return bwd_workspace_bytes(B, Hq, Nq);
 }
 
-fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                 void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                 void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL;
+namespace {
+
+// Checks shared by the backward entry points (o and lse may be absent for
+// the dK/dV stage, dq/dk/dv for the stage that does not write them).
+fa_status validate_bwd(const void* const* ptrs, int nptrs, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale,
+                       int causal, const void* workspace, size_t workspace_bytes) {
+  for (int i = 0; i < nptrs; ++i)
+    if (!ptrs[i]) return FA_ERR_NULL;
   const fa_status st = validate_shape(B, Hq, Hkv, Nq, Nk, d);
   if (st != FA_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(lse) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
-    return FA_ERR_ALIGN;
+  for (int i = 0; i < nptrs; ++i)
+    if (!aligned16(ptrs[i])) return FA_ERR_ALIGN;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
   // one query head's rows (the range of a buffer resource) fit in 31 bits
   if (((double)Nq + 64.0) * d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
-  const size_t need = bwd_workspace_bytes(B, Hq, Nq);
-  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace)) return FA_ERR_WORKSPACE;
+  if (workspace == nullptr || workspace_bytes < bwd_workspace_bytes(B, Hq, Nq) || !aligned16(workspace))
+    return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+fa_status bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq};
+  const fa_status st = validate_bwd(ptrs, 7, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
   const fa_plan_t pq = plan_bwd_dq(B, Hq, Hkv, Nq, Nk, d, causal);
-  const fa_kvplan_t pk = plan_bwd_dkdv(B, Hq, Hkv, Nq, Nk, d, causal);
-  if (pq.nwg > 0x7fffffffLL || pk.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
-  const hipError_t e = fa::launch_bwd(q, k, v, o, dout, lse, dq, dk, dv, (float*)workspace, pq, pk, d,
-                                      (float)((double)scale * LOG2E), scale, (hipStream_t)stream);
+  if (pq.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const hipError_t e = fa::launch_bwd_dq(q, k, v, o, dout, lse, dq, (float*)workspace, pq, d,
+                                         (float)((double)scale * LOG2E), scale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B, int Hq,
+                   int Hkv, int Nq, int Nk, int d, float scale, int causal, const void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  const void* ptrs[] = {q, k, v, dout, dk, dv};
+  const fa_status st = validate_bwd(ptrs, 6, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa_kvplan_t pk = plan_bwd_dkdv(B, Hq, Hkv, Nq, Nk, d, causal);
+  if (pk.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
+  const hipError_t e = fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, (const float*)workspace, pk, d,
+                                           (float)((double)scale * LOG2E), scale, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    void* dq, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return bwd_dq(q, k, v, o, dout, lse, dq, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B,
+                      int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, const void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return bwd_dkdv(q, k, v, dout, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes, stream);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                 void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  // both stages are validated before either is enqueued
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  const fa_status st = validate_bwd(ptrs, 9, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes);
+  if (st != FA_OK) return st;
+  const fa_status s1 = bwd_dq(q, k, v, o, dout, lse, dq, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace,
+                              workspace_bytes, stream);
+  if (s1 != FA_OK) return s1;
+  return bwd_dkdv(q, k, v, dout, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

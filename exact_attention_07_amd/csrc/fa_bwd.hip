@@ -448,34 +448,33 @@ int bwd_dkdv_max_waves(int d) { return d == 64 ? 4 : d == 128 ? 8 : 2; }
 
 int bwd_dq_max_waves(int d) { return d == 256 ? 4 : 8; }
 
-hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                      void* dq, void* dk, void* dv, float* ld, const fa_plan_t& pq, const fa_kvplan_t& pk, int d,
-                      float c, float scale, hipStream_t stream) {
-  bool done = false;
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, float* ld, const fa_plan_t& pq, int d, float c, float scale,
+                         hipStream_t stream) {
 #define FA_CASE_DQ(DD, CC, NN)                                                                             \
-  if (!done && d == DD && (pq.causal != 0) == CC && pq.nw == NN) {                                          \
+  if (d == DD && (pq.causal != 0) == CC && pq.nw == NN) {                                                   \
     hipLaunchKernelGGL((fa_bwd_dq_kernel<DD, CC, NN>), dim3((unsigned)pq.nwg), dim3(64 * NN), 0, stream,       \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o,                  \
                        (const __bf16*)dout, lse, ld, (__bf16*)dq, pq, c, scale);                              \
-    done = true;                                                                                            \
+    return hipGetLastError();                                                                               \
   }
   FA_DQ_VARIANTS(FA_CASE_DQ)
 #undef FA_CASE_DQ
-  if (!done) return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  done = false;
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                           const float* ld, const fa_kvplan_t& pk, int d, float c, float scale, hipStream_t stream) {
 #define FA_CASE_DKDV(DD, CC, NN, KK)                                                                        \
-  if (!done && d == DD && (pk.causal != 0) == CC && pk.nw == NN && pk.kpw == 32 * KK) {                     \
+  if (d == DD && (pk.causal != 0) == CC && pk.nw == NN && pk.kpw == 32 * KK) {                              \
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DD, CC, NN, KK>), dim3((unsigned)pk.nwg), dim3(64 * NN), 0, stream, \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld,          \
                        (__bf16*)dk, (__bf16*)dv, pk, c, scale);                                               \
-    done = true;                                                                                            \
+    return hipGetLastError();                                                                               \
   }
   FA_DKDV_VARIANTS(FA_CASE_DKDV)
 #undef FA_CASE_DKDV
-  if (!done) return hipErrorInvalidValue;
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -44,12 +44,17 @@ int bwd_keys_per_wave(int d);
 int bwd_dkdv_max_waves(int d);
 int bwd_dq_max_waves(int d);
 
-// Enqueue the backward pass: the dQ kernel (plan pq; it also writes the
-// per-row (LSE log2 e, rowsum(dO o O)) pairs into ld, [B][Hq][Nq][2] fp32),
-// then the dK/dV kernel (plan pk), which reads them.  c = scale * log2(e).
-hipError_t launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
-                      void* dq, void* dk, void* dv, float* ld, const fa_plan_t& pq, const fa_kvplan_t& pk, int d,
-                      float c, float scale, hipStream_t stream);
+// Enqueue the dQ kernel of the backward pass (plan pq).  It also writes the
+// per-row pairs (LSE log2 e, rowsum(dO o O)) into ld, [B][Hq][Nq][2] fp32.
+// c = scale * log2(e).
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                         const float* lse, void* dq, float* ld, const fa_plan_t& pq, int d, float c, float scale,
+                         hipStream_t stream);
+
+// Enqueue the dK/dV kernel of the backward pass (plan pk); reads the pairs
+// launch_bwd_dq wrote into ld.
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                           const float* ld, const fa_kvplan_t& pk, int d, float c, float scale, hipStream_t stream);
 
 }  // namespace fa
 

@@ -193,14 +193,29 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const floa
  * bf16; the gradients are rounded to bf16 (nearest even).  D is formed from
  * the bf16 O.  Rows that see no key (LSE = -inf) contribute nothing.
  * Errors: those of fa_fwd (every pointer except the workspace required);
- * FA_ERR_WORKSPACE for a missing, small or misaligned workspace.
+ * FA_ERR_WORKSPACE for a missing, small or misaligned workspace.  fa_bwd
+ * checks every argument before it enqueues anything.
  * fa_bwd_workspace_size returns 0 for arguments fa_bwd would reject.
+ *
+ * fa_bwd runs two kernels in stream order, also available on their own:
+ *   fa_bwd_dq    dq, plus the per-row pairs (LSE log2(e), D) into the
+ *                workspace ([B][Hq][Nq][2] float32);
+ *   fa_bwd_dkdv  dk and dv; reads those pairs, so it must follow an
+ *                fa_bwd_dq with the same arguments and workspace (on the same
+ *                stream, or after it has completed).
+ * fa_bwd(...) is fa_bwd_dq(...) followed by fa_bwd_dkdv(...).
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal);
 fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                  const float* lse, void* dq, void* dk, void* dv,
                  int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                  void* workspace, size_t workspace_bytes, void* stream);
+fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* dq, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                    float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
+fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
+                      int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                      const void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -180,3 +180,27 @@ def test_bwd_workspace_size(lib):
 ])
 def test_bwd_rejects_invalid_arguments(lib, kw, status):
     assert call_bwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(o=None), 1), (dict(lse=None), 1), (dict(dq=None), 1), (dict(dq=P + 2), 5),
+    (dict(d=96), 3), (dict(ws=None), 9), (dict(wsb=8), 9), (dict(causal=-1), 8),
+])
+def test_bwd_dq_rejects_invalid_arguments(lib, kw, status):
+    a = dict(BWD_GOOD)
+    a.update(kw)
+    assert lib.fa_bwd_dq(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["B"], a["Hq"], a["Hkv"],
+                         a["Nq"], a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], a["ws"],
+                         ctypes.c_size_t(a["wsb"]), None) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), 1), (dict(do=None), 1), (dict(dk=None), 1), (dict(dv=None), 1), (dict(dv=P + 8), 5),
+    (dict(Hkv=3), 4), (dict(ws=None), 9), (dict(ws=P + 4), 9), (dict(scale=-1.0), 6),
+])
+def test_bwd_dkdv_rejects_invalid_arguments(lib, kw, status):
+    a = dict(BWD_GOOD)
+    a.update(kw)
+    assert lib.fa_bwd_dkdv(a["q"], a["k"], a["v"], a["do"], a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                           a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], a["ws"],
+                           ctypes.c_size_t(a["wsb"]), None) == status

@@ -192,3 +192,26 @@ def test_backward_agrees_with_torch_autograd_on_the_cpu(api):
     compare_grad(dq, q.grad.numpy(), "autograd dQ")
     compare_grad(dk, k.grad.numpy(), "autograd dK")
     compare_grad(dv, v.grad.numpy(), "autograd dV")
+
+
+def test_backward_stages_equal_the_whole(api):
+    """fa_bwd_dq followed by fa_bwd_dkdv writes exactly what fa_bwd writes."""
+    w = gen.workload(2, 8, 2, 200, 333, 128, causal=True)
+    x = gen.make_inputs(w, (26,))
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    do = to_device(gen.make_dout(w, (26,)), "bf16")
+    o, lse = api.attention(q, k, v, causal=True)
+    dq1, dk1, dv1 = api.attention_backward(q, k, v, o, lse, do, causal=True)
+    nbytes = api.bwd_workspace_size(2, 8, 2, 200, 333, 128, True)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    dq2, dk2, dv2 = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    api.fa_bwd_dq(q, k, v, o, lse, do, dq2, w.softmax_scale, True, ws)
+    api.fa_bwd_dkdv(q, k, v, o, lse, do, dk2, dv2, w.softmax_scale, True, ws)
+    torch.cuda.synchronize()
+    for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # the workspace holds (LSE log2 e, D) per row
+    pairs = ws.view(2, 8, 200, 2).cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(pairs[..., 0], lse.cpu().numpy() * math.log2(math.e), rtol=1e-6)
+    d_ref = (do.float() * o.float()).sum(-1).cpu().numpy()
+    np.testing.assert_allclose(pairs[..., 1], d_ref, rtol=1e-4, atol=1e-4)
