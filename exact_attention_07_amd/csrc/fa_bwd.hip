@@ -55,12 +55,10 @@ struct BwdCfg {
   static constexpr int KB = BC / 32; // 32-row blocks of a 64-row tile
   static constexpr int PS = BC / 16; // k-steps over a 64-row tile
   static constexpr int CPR = D / 8;  // 16-byte data slots per row
-  // LDS row strides.  Tiles read both as row fragments (b128, 16 rows per
-  // 16 lanes) and as transposed fragments (ds_read_b64_tr_b16, 4 rows per 32
-  // lanes) need an odd number of 16-byte slots per row for the first and
-  // rows about 16 banks apart for the second; CPR + 3 slots (CPR + 1 at
-  // d = 64) satisfies the first exactly and the second up to a few shared
-  // banks.  Tiles read only as row fragments take CPR + 1.
+  // LDS row strides: an odd number of 16-byte slots per row.  Tiles read
+  // both as row fragments and transposed (K in the dQ kernel, Q and dO in
+  // the dK/dV kernel) also store their rows in perm16 order (fa_frag.h),
+  // which makes both kinds of read free of bank conflicts.
   static constexpr int SPR_X = CPR + (D == 64 ? 1 : 3);
   static constexpr int SPR_R = CPR + 1;
   static constexpr int RSX = SPR_X * 16, RSR = SPR_R * 16;
@@ -85,7 +83,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
                       float* __restrict__ LD, __bf16* __restrict__ dQ, fa_plan_t p, float c, float scale) {
   using C = BwdCfg<D>;
   constexpr int DS = C::DS, DB = C::DB, KB = C::KB, PS = C::PS, RSX = C::RSX, RSR = C::RSR;
-  using CopyK = CopyPlan<D, NW, C::SPR_X>;
+  using CopyK = CopyPlan<D, NW, C::SPR_X, true>;
   using CopyV = CopyPlan<D, NW, C::SPR_R>;
   __shared__ __attribute__((aligned(1024))) char lk0_[C::TILE_X];
   __shared__ __attribute__((aligned(1024))) char lk1_[C::TILE_X];
@@ -143,7 +141,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
 #pragma unroll
   for (int db = 0; db < DB; ++db) dq[db] = (f32x16){};
 
-  const int koff_l = k_lane_off<RSX>(lane), voff_l = k_lane_off<RSR>(lane), toff_l = v_lane_off<RSX>(lane);
+  const int koff_l = k_lane_off_p<RSX>(lane), voff_l = k_lane_off<RSR>(lane), toff_l = v_lane_off_p<RSX>(lane);
   CopyK cpk;
   CopyV cpv;
   cpk.init(wave, lane);
@@ -192,7 +190,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
     for (int ps = 0; ps < PS; ++ps)
 #pragma unroll
       for (int db = 0; db < DB; ++db)
-        dq[db] = mfma(v_frag<RSX>(kt + toff_l, ps, db), __builtin_bit_cast(bf16x8, dsp[ps]), dq[db]);
+        dq[db] = mfma(v_frag_p<RSX>(kt + toff_l, ps, db), __builtin_bit_cast(bf16x8, dsp[ps]), dq[db]);
   };
 
   // double-buffered key tiles: iteration j waits for tile j, then starts the
@@ -244,11 +242,19 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   using C = BwdCfg<D>;
   constexpr int DS = C::DS, DB = C::DB, RSX = C::RSX;
   constexpr int KPW = 32 * KBW;
-  using CopyQ = CopyPlan<D, NW, C::SPR_X>;
+  using CopyQ = CopyPlan<D, NW, C::SPR_X, true>;
   __shared__ __attribute__((aligned(1024))) char lq0_[C::TILE_X];
   __shared__ __attribute__((aligned(1024))) char lq1_[C::TILE_X];
   __shared__ __attribute__((aligned(1024))) char lo0_[C::TILE_X];
   __shared__ __attribute__((aligned(1024))) char lo1_[C::TILE_X];
+  // d = 128: the V rows of the workgroup's keys are staged in LDS once (whole
+  // tiles of 64 rows) and the V fragments of dP = dO V^T are read from there,
+  // which leaves the registers they would take to the compiler for loads in
+  // flight.  At d = 256 there is no LDS room; at d = 64 no register pressure.
+  constexpr bool VLDS = (D == 128);
+  constexpr int RSR = C::RSR;
+  constexpr int VT = (NW * KPW + BC - 1) / BC;  // tiles of V rows
+  __shared__ __attribute__((aligned(1024))) char lvr_[VLDS ? VT * C::TILE_R : 16];
   __shared__ __attribute__((aligned(1024))) char ll0_[1024];
   __shared__ __attribute__((aligned(1024))) char ll1_[1024];
   __shared__ __attribute__((aligned(1024))) char lsp_[1024];
@@ -265,7 +271,7 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
   const bool has_keys = k0w < Nk;
 
-  bf16x8 kf[KBW][DS], vf[KBW][DS];
+  bf16x8 kf[KBW][DS], vf[VLDS ? 1 : KBW][VLDS ? 1 : DS];
 #pragma unroll
   for (int kb = 0; kb < KBW; ++kb) {
     const int key = k0w + kb * 32 + (lane & 31);
@@ -273,9 +279,21 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     for (int ds = 0; ds < DS; ++ds) {
       const size_t e0 = kvoff + (size_t)key * D + ds * 16 + h * 8;
       kf[kb][ds] = key < Nk ? *(const bf16x8*)(K + e0) : (bf16x8){};
-      vf[kb][ds] = key < Nk ? *(const bf16x8*)(V + e0) : (bf16x8){};
+      if constexpr (!VLDS) vf[kb][ds] = key < Nk ? *(const bf16x8*)(V + e0) : (bf16x8){};
     }
   }
+  if constexpr (VLDS) {
+    // copied like the query tiles (rows past Nk read as zero); they land
+    // before the barrier of the first iteration
+    using CopyV = CopyPlan<D, NW, C::SPR_R>;
+    CopyV cv;
+    cv.init(wave, lane);
+    const __amdgpu_buffer_rsrc_t vres = CopyV::rsrc(V + kvoff, Nk);
+#pragma unroll
+    for (int t = 0; t < VT; ++t)
+      cv.issue_all(vres, (w.k0 + t * BC) * (D * 2), (LDS_AS char*)lvr_ + t * C::TILE_R, (LDS_AS char*)lsp_, wave);
+  }
+  LDS_AS const char* const vrow = (LDS_AS const char*)lvr_ + wave * KPW * RSR + k_lane_off<RSR>(lane);
   f32x16 dk[KBW][DB], dv[KBW][DB];
 #pragma unroll
   for (int kb = 0; kb < KBW; ++kb)
@@ -284,13 +302,16 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
   int first, ntq;
   fa_kv_query_tiles(p, w.k0, BC, first, ntq);
-  const int total = (ntq - first) * G;  // iterations: tile ntq - 1 - it / G of head it % G
+  // iterations: query tiles ntq - 1 down to first, the G heads of the group
+  // innermost; (t_c, h_c) is the tile and head of the iteration computed
+  const int total = (ntq - first) * G;
+  int t_c = ntq - 1, h_c = 0;
 
-  const int qoff_l = k_lane_off<RSX>(lane), toff_l = v_lane_off<RSX>(lane);
+  const int qoff_l = k_lane_off_p<RSX>(lane), toff_l = v_lane_off_p<RSX>(lane);
   CopyQ cp;
   cp.init(wave, lane);
-  auto issue = [&](int it, auto par) {
-    const int t = ntq - 1 - it / G, hq = w.hkv * G + it % G;
+  auto issue = [&](int t, int hh, auto par) {
+    const int hq = w.hkv * G + hh;
     const size_t rb = (size_t)(w.b * p.Hq + hq) * Nq;
     const __amdgpu_buffer_rsrc_t rq = CopyQ::rsrc(Q + rb * D, Nq), ro = CopyQ::rsrc(dO + rb * D, Nq);
     cp.issue_all(rq, t * (BC * D * 2), qslot(par), spare, wave);
@@ -303,11 +324,10 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     }
   };
 
-  auto compute = [&](int it, auto par) {
+  auto compute = [&](int q0, auto par) {
     LDS_AS const char* qt = qslot(par);
     LDS_AS const char* ot = oslot(par);
     LDS_AS const char* lt = lslot(par);
-    const int q0 = (ntq - 1 - it / G) * BC;
     // the two 32-row halves one after the other (overlapping them would need
     // a second set of score registers)
 #pragma unroll 1
@@ -328,11 +348,23 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb) {
           s[kb] = mfma(a, kf[kb][ds], s[kb]);
-          dp[kb] = mfma(b, vf[kb][ds], dp[kb]);
+          if constexpr (VLDS) dp[kb] = mfma(b, lds_b128(vrow + kb * 32 * RSR + ds * 32), dp[kb]);
+          else dp[kb] = mfma(b, vf[kb][ds], dp[kb]);
         }
       }
-      // causal: some row of the half misses one of the wave's keys
-      const bool need_mask = CAUSAL && k0w + KPW - 1 > qb0 + off;
+      // causal, halves that cross the diagonal only (a wave-uniform branch):
+      // scores of keys past a row's last visible key become -inf, so P = 0
+      if (CAUSAL && k0w + KPW - 1 > qb0 + off) {
+#pragma unroll
+        for (int kb = 0; kb < KBW; ++kb) {
+          // row qb0 + 8g + 4h + r misses this lane's key iff 8g + r < lim
+          const int lim = k0w + kb * 32 + (lane & 31) - off - qb0 - 4 * h;
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            if ((i >> 2) * 8 + (i & 3) < lim) s[kb][i] = NEG_INF;
+        }
+      }
+      // P and dS of the half, packed to bf16
       u32x4 pp[KBW][2], dsp[KBW][2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -342,15 +374,12 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
         const float l2v[4] = {la[0], la[2], lb[0], lb[2]}, ddv[4] = {la[1], la[3], lb[1], lb[3]};
 #pragma unroll
         for (int kb = 0; kb < KBW; ++kb) {
-          const int key = k0w + kb * 32 + (lane & 31);
 #pragma unroll
           for (int r = 0; r < 4; r += 2) {
             float pr[2], dsv[2];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              float sv = s[kb][4 * g + r + u];
-              if (need_mask && key > qb0 + 8 * g + 4 * h + r + u + off) sv = NEG_INF;
-              pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv, c, -l2v[r + u]));
+              pr[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * g + r + u], c, -l2v[r + u]));
               dsv[u] = pr[u] * (dp[kb][4 * g + r + u] - ddv[r + u]);
             }
             pp[kb][g / 2][2 * (g % 2) + r / 2] = pack_bf16(pr[0], pr[1]);
@@ -362,7 +391,7 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = v_frag<RSX>(oh + toff_l, ps, db);
+          const bf16x8 a = v_frag_p<RSX>(oh + toff_l, ps, db);
 #pragma unroll
           for (int kb = 0; kb < KBW; ++kb) dv[kb][db] = mfma(a, __builtin_bit_cast(bf16x8, pp[kb][ps]), dv[kb][db]);
         }
@@ -370,7 +399,7 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       for (int ps = 0; ps < 2; ++ps)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const bf16x8 a = v_frag<RSX>(qh + toff_l, ps, db);
+          const bf16x8 a = v_frag_p<RSX>(qh + toff_l, ps, db);
 #pragma unroll
           for (int kb = 0; kb < KBW; ++kb) dk[kb][db] = mfma(a, __builtin_bit_cast(bf16x8, dsp[kb][ps]), dk[kb][db]);
         }
@@ -381,13 +410,15 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     using other = std::integral_constant<int, 1 - decltype(par)::value>;
     vm_wait<0>();
     __syncthreads();
-    if (it + 1 < total) issue(it + 1, other{});
-    if (has_keys) {
-      const int q0 = (ntq - 1 - it / G) * BC;
-      if (!CAUSAL || q0 + BC - 1 + off >= k0w) compute(it, par);
-    }
+    const int h_n = h_c + 1 == G ? 0 : h_c + 1;
+    const int t_n = h_c + 1 == G ? t_c - 1 : t_c;
+    if (it + 1 < total) issue(t_n, h_n, other{});
+    const int q0 = t_c * BC;
+    if (has_keys && (!CAUSAL || q0 + BC - 1 + off >= k0w)) compute(q0, par);
+    t_c = t_n;
+    h_c = h_n;
   };
-  if (total > 0) issue(0, P0{});
+  if (total > 0) issue(ntq - 1, 0, P0{});
   for (int it = 0; it < total; it += 2) {
     iteration(it, P0{});
     if (it + 1 < total) iteration(it + 1, P1{});

@@ -53,14 +53,45 @@ __device__ __forceinline__ bf16x8 v_frag(LDS_AS const char* vlane, int ps, int d
   return join(a, b);
 }
 
+// Row order of tiles that are read both as row fragments and transposed.
+// Within each block of 16 rows, row 4a + b of the data is stored at LDS row
+// 4b + a (an involution).  With a row stride of an odd number of 16-byte
+// slots, a row-fragment read (16 lanes on 16 consecutive data rows, one
+// slot each) still covers 16 distinct groups of 4 banks, and a transposed
+// read (32 lanes on 4 consecutive data rows, 64 bytes each) now finds its 4
+// rows 4 LDS rows apart, 16 banks from each other: both are free of bank
+// conflicts, which no plain row stride achieves for both.
+__host__ __device__ __forceinline__ constexpr int perm16(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+// k_lane_off for a permuted tile.
+template <int RS>
+__device__ __forceinline__ int k_lane_off_p(int lane) { return perm16(lane & 31) * RS + (lane >> 5) * 16; }
+
+// Transposed fragment (the layout of v_frag) from a permuted tile: data row
+// ps*16 + 8j + 4h + c (h = lane / 32, c = (lane % 16) / 4) sits at LDS row
+// ps*16 + 4c + 2j + h.
+template <int RS>
+__device__ __forceinline__ int v_lane_off_p(int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  return (4 * (s >> 2) + (g >> 1)) * RS + (2 * (g & 1) + ((s & 3) >> 1)) * 16 + (s & 1) * 8;
+}
+
+template <int RS>
+__device__ __forceinline__ bf16x8 v_frag_p(LDS_AS const char* vlane, int ps, int db) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vlane + (ps * 16) * RS + db * 64));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vlane + (ps * 16 + 2) * RS + db * 64));
+  return join(a, b);
+}
+
 // HBM -> LDS copy plan of one wave: copy instruction i of the wave (global
 // instruction index i*NW + wave) fills LDS bytes [ins*1024, ins*1024 + 1024)
 // of the tile, lane t the slot ins*64 + t (BC*SPR is a multiple of 64, so
 // the last instruction ends exactly at the end of the tile).  goff is the
 // byte offset of the slot's data within the tile's rows in HBM (rows of D
-// bf16, contiguous); padding slots get an offset past any buffer range, so
-// their load reads zero and writes it into the (never read) padding.
-template <int D, int NW, int SPR>
+// bf16, contiguous; with PERM, LDS row r takes HBM row perm16(r)); padding
+// slots get an offset past any buffer range, so their load reads zero and
+// writes it into the (never read) padding.
+template <int D, int NW, int SPR, bool PERM = false>
 struct CopyPlan {
   static constexpr int CPR = D / 8;
   static constexpr int INS = BC * SPR / 64;            // 64-lane copy instructions per tile
@@ -74,7 +105,8 @@ struct CopyPlan {
       const int ins = i * NW + wave;
       const int sl = ins * 64 + lane;
       const int r = sl / SPR, pp = sl % SPR;
-      goff[i] = (ins < INS && pp < CPR) ? (unsigned)(r * (D * 2) + pp * 16) : OUT_OF_RANGE;
+      const int src = PERM ? perm16(r) : r;  // the HBM row whose data LDS row r holds
+      goff[i] = (ins < INS && pp < CPR) ? (unsigned)(src * (D * 2) + pp * 16) : OUT_OF_RANGE;
     }
   }
   // Buffer resource over a whole [Nk][D] bf16 matrix; the hardware range
