@@ -293,14 +293,15 @@ __device__ __forceinline__ void scores_full(Scores<D>& s, LDS_AS const char* kla
 
 // Mask keys past the visible range of each query (tiles that cross the
 // causal diagonal or the end of the keys only).
+// query: the row of the lane's query column.
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int q0w, int Nq, int Nk, int kend, int lane) {
+__device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int query, int Nq, int Nk, int kend, int lane) {
   using C = Cfg<D, false>;
+  static_assert(C::QB == 1, "one 32-row query block per wave");
 #pragma unroll
   for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
     for (int qb = 0; qb < C::QB; ++qb) {
-      const int query = q0w + qb * 32 + (lane & 31);
       const int klim = min(kend, CAUSAL ? min(Nk, query + Nk - Nq + 1) : Nk);  // keys < klim are visible
       const int kmax = klim - 1 - j0 - kb * 32 - (lane >> 5) * 4;
 #pragma unroll
@@ -370,14 +371,27 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   // tiles of the range this wave computes (t0 .. t0 + ntw - 1)
   const int ntw = (live && klast_w >= 0) ? max(0, min(t1, klast_w / BC + 1) - t0) : 0;
 
-  const size_t qoff = (size_t)(w.b * p.Hq + hq) * Nq * D;
   const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
+  // the lane's query column: head hq_l, row q_l (valid_l: a real query).
+  // Packed plans hold row c % Nq of head hq0 + c / Nq in column c; the wave
+  // then covers rows 0 .. Nq - 1 of every head, so the wave-level limits
+  // above hold unchanged.
+  const int col = lane & 31;
+  int hq_l = hq, q_l = q0w + col;
+  bool valid_l = q_l < Nq;
+  if (p.pack > 1) {
+    const int hh = col / Nq;
+    valid_l = hh < p.pack;
+    hq_l = w.hq0 + (valid_l ? hh : 0);
+    q_l = valid_l ? col - hh * Nq : 0;
+  }
+  const size_t qrow0 = (size_t)(w.b * p.Hq + hq_l) * Nq;  // first row of the lane's head
 
   bf16x8 qf[1][DS];
   {
-    const int qrow = min(q0w + (lane & 31), Nq - 1);
+    const int qrow = min(q_l, Nq - 1);
 #pragma unroll
-    for (int ds = 0; ds < DS; ++ds) qf[0][ds] = *(const bf16x8*)(Q + qoff + (size_t)qrow * D + ds * 16 + (lane >> 5) * 8);
+    for (int ds = 0; ds < DS; ++ds) qf[0][ds] = *(const bf16x8*)(Q + (qrow0 + qrow) * D + ds * 16 + (lane >> 5) * 8);
   }
 
   f32x16 o[DB];
@@ -455,7 +469,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     for (int t = 0; t < KPF; ++t) kbuf[t] = lds_b128(knext + (t % KB) * 32 * RSK + (t / KB) * 32);
 #pragma unroll
     for (int t = 0; t < VPF; ++t) vbuf[t] = v_frag<RSV>(vprev, t / DB, t % DB);
-    if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q0w, Nq, Nk, kend, lane);
+    if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q_l, Nq, Nk, kend, lane);
 
     float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
     float part0 = 0.f, part1 = 0.f, even = 0.f;
@@ -543,11 +557,10 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   if (!live) return;
   const float lt = xhalf_sum(lsum);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  const int query = q0w + (lane & 31);
-  if (query >= Nq) return;
+  if (!valid_l) return;
   const float lse_row = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
   if (p.nsplit > 1) {
-    const size_t row = ((size_t)w.split * p.B * p.Hq + (size_t)w.b * p.Hq + hq) * Nq + query;
+    const size_t row = (size_t)w.split * p.B * p.Hq * Nq + qrow0 + q_l;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -560,7 +573,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     if (lane < 32) LWS[row] = lse_row;
     return;
   }
-  const size_t orow = qoff + (size_t)query * D;
+  const size_t orow = (qrow0 + q_l) * D;
 #pragma unroll
   for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -571,7 +584,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
       for (int e = 0; e < 4; ++e) r[e] = (__bf16)(o[db][i4 * 4 + e] * inv);
       *(bf16x4*)(O + orow + d0) = r;
     }
-  if (LSE != nullptr && lane < 32) LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lse_row;
+  if (LSE != nullptr && lane < 32) LSE[qrow0 + q_l] = lse_row;
 }
 
 // ---------------------------------------------------------------- launchers

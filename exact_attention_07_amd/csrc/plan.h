@@ -25,7 +25,12 @@
 //     rows): each workgroup then covers one range and writes a partial
 //     result that a merge combines ("FlashAttention (SV)", section
 //     "Online-beräkning av Softmax": block statistics combine exactly).  The
-//     ranges of one query block are consecutive in the order.
+//     ranges of one query block are consecutive in the order;
+//   * with few query rows (G * Nq <= 32) the G query heads of a GQA group
+//     can share one wave (`pack` = G): its 32 query columns hold row c % Nq
+//     of head c / Nq, so one pass over the group's K/V computes all of them
+//     (decoding: one row per head would otherwise leave 31 of 32 columns
+//     idle in every matrix product).
 #ifndef FA_PLAN_H
 #define FA_PLAN_H
 
@@ -48,6 +53,7 @@ struct fa_plan_t {
   int xcd;    // 1 if workgroup ids are remapped XCD-contiguously
   int nsplit; // key ranges (1: no split)
   int tps;    // key tiles per range (nsplit > 1)
+  int pack;   // query heads sharing one wave's columns (1: one head per wave)
   long long nwg;  // workgroups in the grid
 };
 
@@ -70,7 +76,22 @@ FA_HD inline fa_plan_t fa_make_plan(int B, int Hq, int Hkv, int Nq, int Nk, int 
   p.nhg = p.G / p.hw;
   p.nsplit = 1;
   p.tps = 0;
+  p.pack = 1;
   p.nwg = (long long)B * Hkv * p.nhg * p.nqb;
+  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  return p;
+}
+
+// One single-wave workgroup per GQA group, its G heads packed into the
+// wave's query columns; requires G * Nq <= 32.
+FA_HD inline fa_plan_t fa_make_packed_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal) {
+  fa_plan_t p = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, 32, 1);
+  p.hw = p.G;
+  p.pos = Nq;
+  p.nqb = 1;
+  p.nhg = 1;
+  p.pack = p.G;
+  p.nwg = (long long)B * Hkv;
   p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
   return p;
 }

@@ -118,7 +118,47 @@ static void check_kvplan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int
   if (!p.xcd && p.nkb > 1) CHECK(fa_kv_decode(p, 0).k0 == 0 && fa_kv_decode(p, 1).k0 == p.kpb);
 }
 
+// Packed plans: every (b, query head, query row) is the column of exactly
+// one (workgroup, lane column), all heads of a workgroup read its kv head.
+static void check_packed(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int tps) {
+  fa_plan_t p = fa_make_packed_plan(B, Hq, Hkv, Nq, Nk, causal);
+  if (tps > 0) p = fa_split_plan(p, tps, 64);
+  CHECK(p.G * Nq <= 32 && p.pack == p.G && p.nw == 1 && p.nqb == 1 && p.nhg == 1);
+  const int tiles = (Nk + 63) / 64;
+  std::vector<int> cover((size_t)B * Hq * Nq * tiles, 0);
+  for (long long id = 0; id < p.nwg; ++id) {
+    fa_work_t w = fa_decode(p, id);
+    CHECK(w.qpos0 == 0 && w.hq0 == w.hkv * p.G);
+    int nt = fa_num_kv_tiles(p, w.qpos0, 64), t0, t1;
+    fa_split_tiles(p, w.split, nt, t0, t1);
+    for (int col = 0; col < 32; ++col) {
+      const int hh = col / Nq;
+      if (hh >= p.pack) continue;  // an idle column
+      const int hq = w.hq0 + hh, i = col - hh * Nq;
+      CHECK(hq / p.G == w.hkv && i < Nq);
+      int klast = causal ? (i + Nk - Nq < Nk - 1 ? i + Nk - Nq : Nk - 1) : Nk - 1;
+      for (int t = t0; t < t1; ++t)
+        if (t * 64 <= klast) cover[(((size_t)w.b * Hq + hq) * Nq + i) * tiles + t]++;
+    }
+  }
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < Hq; ++h)
+      for (int i = 0; i < Nq; ++i) {
+        int klast = causal ? (i + Nk - Nq < Nk - 1 ? i + Nk - Nq : Nk - 1) : Nk - 1;
+        for (int t = 0; t < tiles; ++t)
+          CHECK(cover[(((size_t)b * Hq + h) * Nq + i) * tiles + t] == (klast >= 0 && t * 64 <= klast ? 1 : 0));
+      }
+}
+
 int main() {
+  for (int causal = 0; causal < 2; ++causal)
+    for (int tps : {0, 1, 3, 100}) {
+      check_packed(2, 8, 2, 1, 1000, causal, tps);     // decoding, GQA 4
+      check_packed(1, 32, 1, 1, 300, causal, tps);     // MQA, 32 heads in one wave
+      check_packed(3, 6, 2, 10, 200, causal, tps);     // 3 heads x 10 rows
+      check_packed(1, 4, 2, 16, 70, causal, tps);      // 2 heads x 16 rows: all 32 columns
+      check_packed(1, 8, 2, 7, 5, causal, tps);        // Nq > Nk: rows without keys
+    }
   for (int causal = 0; causal < 2; ++causal)
     for (int nw : {1, 2, 4})
       for (int kpw : {32, 64}) {

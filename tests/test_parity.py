@@ -85,6 +85,12 @@ SHAPES = [
     (1, 2, 1, 70, 1),        # a single key
     (1, 2, 2, 150, 40),      # Nq > Nk: causal rows with no visible key
     (1, 4, 4, 64, 64),       # exactly one tile
+    # G * Nq <= 32: the GQA group's heads share one wave's query columns (bf16)
+    (2, 8, 2, 1, 300),       # decoding, GQA 4: 4 of 32 columns
+    (1, 32, 1, 1, 200),      # 32 heads in one wave
+    (3, 6, 2, 10, 100),      # 3 heads x 10 rows
+    (1, 4, 2, 16, 70),       # 2 heads x 16 rows: every column
+    (1, 8, 2, 7, 5),         # Nq > Nk: causal rows with no visible key
 ]
 
 

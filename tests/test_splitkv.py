@@ -48,6 +48,9 @@ CASES = [
     (1, 4, 1, 17, 3000, 256),    # MQA, 17 queries
     (3, 16, 2, 1, 1000, 128),    # GQA 8 (eight-wave workgroups)
     (1, 4, 2, 300, 1500, 128),   # prefill over several query blocks
+    (1, 32, 1, 1, 3000, 128),    # 32 query heads packed into one wave
+    (3, 6, 2, 10, 2000, 64),     # 3 heads x 10 rows packed
+    (1, 4, 2, 16, 700, 256),     # 2 heads x 16 rows: every column
 ]
 
 
