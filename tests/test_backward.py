@@ -215,3 +215,34 @@ def test_backward_stages_equal_the_whole(api):
     np.testing.assert_allclose(pairs[..., 0], lse.cpu().numpy() * math.log2(math.e), rtol=1e-6)
     d_ref = (do.float() * o.float()).sum(-1).cpu().numpy()
     np.testing.assert_allclose(pairs[..., 1], d_ref, rtol=1e-4, atol=1e-4)
+
+
+# Grids large enough that the planner picks the multi-wave workgroups (at
+# least 512 dK/dV workgroups, 1024 dQ workgroups where possible): d = 64 with
+# 4-wave, 64-key-per-wave dK/dV workgroups; d = 256 with 2-wave ones; d = 128
+# with 4-wave ones (8 would leave fewer than 512).  The kernels run the whole
+# problem; the oracle checks the gradients of one head group.
+LARGE = [
+    # B, Hq, Hkv, Nq, Nk, d, causal
+    (4, 32, 16, 2000, 2000, 64, True),
+    (2, 16, 8, 2048, 2048, 256, False),
+    (2, 16, 8, 1000, 4000, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", LARGE, ids=lambda c: "x".join(map(str, c)))
+def test_backward_large_grids_one_head_group(api, case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    w = gen.workload(B, Hq, Hkv, Nq, Nk, d, causal=causal)
+    x = gen.make_inputs(w, (27, sum(case[:6])))
+    do_bits = gen.make_dout(w, (27, sum(case[:6])))
+    print(f"case: backward large grid {w.name}", flush=True)
+    dq, dk, dv = run_backward(api, w, x, do_bits)
+    b, hk, G = B - 1, Hkv - 1, Hq // Hkv
+    hs = slice(hk * G, hk * G + G)
+    rq, rk, rv = attention_backward_fp64(to_f64(x["q"][b:b + 1, hs], "bf16"), to_f64(x["k"][b:b + 1, hk:hk + 1], "bf16"),
+                                         to_f64(x["v"][b:b + 1, hk:hk + 1], "bf16"),
+                                         to_f64(do_bits[b:b + 1, hs], "bf16"), w.softmax_scale, causal)
+    compare_grad(dq[b:b + 1, hs], rq, f"{w.name} dQ")
+    compare_grad(dk[b:b + 1, hk:hk + 1], rk, f"{w.name} dK")
+    compare_grad(dv[b:b + 1, hk:hk + 1], rv, f"{w.name} dV")
