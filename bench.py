@@ -373,7 +373,7 @@ def main():
         ll = lse.cpu().numpy()
         err = max(float(np.abs(oo[b, h, i] - o_ref[r]).max()) for r, (b, h, i) in enumerate(rows))
         lerr = max(abs(float(ll[b, h, i]) - l_ref[r]) for r, (b, h, i) in enumerate(rows))
-        log(f"check on {len(rows)} rows: max|dO|={err:.2e} max|dLSE|={lerr:.2e}")
+        log(f"check on {len(rows)} rows: max|O err|={err:.2e} max|LSE err|={lerr:.2e}")
 
     if decode:
         # the same step without the split, for comparison (stderr)
