@@ -55,11 +55,11 @@ struct BwdCfg {
   static constexpr int KB = BC / 32; // 32-row blocks of a 64-row tile
   static constexpr int PS = BC / 16; // k-steps over a 64-row tile
   static constexpr int CPR = D / 8;  // 16-byte data slots per row
-  // LDS row strides: an odd number of 16-byte slots per row.  Tiles read
-  // both as row fragments and transposed (K in the dQ kernel, Q and dO in
-  // the dK/dV kernel) also store their rows in perm16 order (fa_frag.h),
-  // which makes both kinds of read free of bank conflicts.
-  static constexpr int SPR_X = CPR + (D == 64 ? 1 : 3);
+  // LDS row strides: an odd number of 16-byte slots per row (one padding
+  // slot).  Tiles read both as row fragments and transposed (K in the dQ
+  // kernel, Q and dO in the dK/dV kernel) also store their rows in perm16
+  // order (fa_frag.h), which makes both kinds of read free of bank conflicts.
+  static constexpr int SPR_X = CPR + 1;
   static constexpr int SPR_R = CPR + 1;
   static constexpr int RSX = SPR_X * 16, RSR = SPR_R * 16;
   static constexpr int TILE_X = BC * RSX, TILE_R = BC * RSR;
