@@ -1,4 +1,4 @@
-"""MI355X-native fused exact-attention forward pass.
+"""MI355X-native fused exact attention: forward and backward passes.
 
 The compute path is the C-ABI library libfa.so (hand-written HIP kernels for
 gfx950, declared in include/fa.h).  `exact_attention_07_amd.api` is a thin

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the fused exact-attention forward pass.
+"""fp64 CPU oracle for exact attention (forward pass and its gradient).
 
 TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
 link this package: only the test-suite, the smoke check and the benchmark's

@@ -20,6 +20,10 @@ Sources (the pages these functions restate):
     maximum and sum of exponentials.  attention_keys_fp64 and merge_fp64 use
     this for attention split over key ranges (each part keeps its own
     normalised output and log-sum-exp).
+  * The pages report training results ("FlashAttention-4震撼发布",
+    FlashAttention-2 list; "FlashAttention (SV)", section "Prestanda och
+    fördelar") without a backward algorithm: attention_backward_fp64 is the
+    gradient of the definition above, written out.
 
 Layouts: q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d]; outputs o [B, Hq, Nq, d]
 (v may have its own last dimension, which o then has)
