@@ -123,9 +123,12 @@ fa_plan_t plan_bwd_dq(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal)
 
 fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
   const int kpw = fa::bwd_keys_per_wave(d);
+  // at d = 256 one workgroup fills a CU's LDS, so 256 workgroups fill the
+  // chip once; fewer waves per workgroup would leave SIMDs idle
+  const long long min_wg = d == 256 ? 256 : MIN_KV_WORKGROUPS;
   for (int nw = fa::bwd_dkdv_max_waves(d); nw > 1; nw >>= 1) {
     const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
-    if (p.nwg >= MIN_KV_WORKGROUPS) return p;
+    if (p.nwg >= min_wg) return p;
   }
   return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, 1);
 }

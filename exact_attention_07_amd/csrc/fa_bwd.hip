@@ -470,12 +470,12 @@ FA_DQ_VARIANTS(FA_INST_DQ)
   X(64, false, 1, 2) X(64, false, 2, 2) X(64, false, 4, 2) X(64, true, 1, 2) X(64, true, 2, 2)                 \
   X(64, true, 4, 2) X(128, false, 1, 1) X(128, false, 2, 1) X(128, false, 4, 1) X(128, false, 8, 1)            \
   X(128, true, 1, 1) X(128, true, 2, 1) X(128, true, 4, 1) X(128, true, 8, 1) X(256, false, 1, 1)              \
-  X(256, false, 2, 1) X(256, true, 1, 1) X(256, true, 2, 1)
+  X(256, false, 2, 1) X(256, false, 4, 1) X(256, true, 1, 1) X(256, true, 2, 1) X(256, true, 4, 1)
 FA_DKDV_VARIANTS(FA_INST_DKDV)
 
 int bwd_keys_per_wave(int d) { return d == 64 ? 64 : 32; }
 
-int bwd_dkdv_max_waves(int d) { return d == 64 ? 4 : d == 128 ? 8 : 2; }
+int bwd_dkdv_max_waves(int d) { return d == 64 ? 4 : d == 128 ? 8 : 4; }
 
 int bwd_dq_max_waves(int d) { return d == 256 ? 4 : 8; }
 
