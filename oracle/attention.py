@@ -216,36 +216,6 @@ def attention_keys_fp64(q, k, v, scale: float, causal: bool, k0: int, k1: int):
     return o, lse
 
 
-def attention_key_set_fp64(q, k, v, scale: float, causal: bool, keys):
-    """The definition over the keys with the given indices only (a part of
-    split attention whose key set is not one contiguous range), each key
-    visible to a query exactly when it is in the full problem: o normalised by
-    the part's own sum, lse of the part; a row that sees none of these keys
-    gets o = 0 and lse = -inf."""
-    q = np.asarray(q, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    v = np.asarray(v, dtype=np.float64)
-    keys = np.asarray(keys, dtype=np.int64)
-    B, HQ, NQ, _ = q.shape
-    _, HKV, NK, _ = k.shape
-    if keys.size and (keys.min() < 0 or keys.max() >= NK):
-        raise ValueError("key index out of bounds")
-    o = np.zeros((B, HQ, NQ, v.shape[-1]), dtype=np.float64)
-    lse = np.full((B, HQ, NQ), -np.inf, dtype=np.float64)
-    if keys.size == 0:
-        return o, lse
-    vis = _visible(NQ, NK, causal)[:, keys]
-    for b in range(B):
-        for h in range(HQ):
-            hk = kv_head_of(h, HQ, HKV)
-            s = scale * (q[b, h] @ k[b, hk, keys].T)
-            p, m, l = _softmax_rows(s, vis)
-            live = l > 0
-            o[b, h][live] = (p[live] @ v[b, hk, keys]) / l[live][:, None]
-            lse[b, h][live] = m[live] + np.log(l[live])
-    return o, lse
-
-
 def merge_fp64(o_parts, lse_parts):
     """Combine attention over disjoint key sets: parts o_s (normalised by their
     own sums) and lse_s, stacked on axis 0.  With L = ln sum_s exp(lse_s):

@@ -13,8 +13,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (attention_backward_fp64, attention_fp64, attention_key_set_fp64, attention_keys_fp64,
-                    attention_rows_fp64, merge_fp64,
+from oracle import (attention_backward_fp64, attention_fp64, attention_keys_fp64, attention_rows_fp64, merge_fp64,
                     online_fp64, formats, fp8)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
@@ -455,44 +454,3 @@ def test_backward_gqa_equals_mha_with_repeated_kv_heads():
     np.testing.assert_allclose(dq, dq2, atol=1e-13)
     np.testing.assert_allclose(dk, dk2.reshape(2, 2, 2, 8, 3).sum(axis=2), atol=1e-13)
     np.testing.assert_allclose(dv, dv2.reshape(2, 2, 2, 8, 3).sum(axis=2), atol=1e-13)
-
-
-# ---------------------------------------------------------------- key sets
-@pytest.mark.parametrize("causal", [False, True])
-def test_key_set_parts_merge_to_full_attention(causal):
-    """Parts over the even and odd 32-key blocks of key ranges (and over a
-    random partition) merge to the full definition."""
-    rng = np.random.default_rng(31 + causal)
-    q = rng.standard_normal((1, 4, 5, 8)); k = rng.standard_normal((1, 2, 150, 8)); v = rng.standard_normal((1, 2, 150, 8))
-    ref_o, ref_l = attention_fp64(q, k, v, 0.4, causal)
-    parts = []
-    for r0, r1 in ((0, 64), (64, 128), (128, 150)):
-        for par in (0, 1):
-            keys = [j for j in range(r0, r1) if (j // 32) % 2 == par]
-            parts.append(attention_key_set_fp64(q, k, v, 0.4, causal, keys))
-    o, l = merge_fp64([p[0] for p in parts], [p[1] for p in parts])
-    np.testing.assert_allclose(o, ref_o, atol=1e-12)
-    np.testing.assert_allclose(l, ref_l, atol=1e-12)
-    perm = rng.permutation(150)
-    parts = [attention_key_set_fp64(q, k, v, 0.4, causal, np.sort(perm[a:a + 37])) for a in range(0, 150, 37)]
-    o, l = merge_fp64([p[0] for p in parts], [p[1] for p in parts])
-    np.testing.assert_allclose(o, ref_o, atol=1e-12)
-    np.testing.assert_allclose(l, ref_l, atol=1e-12)
-
-
-def test_key_set_brute_force_and_empty():
-    rng = np.random.default_rng(33)
-    q = rng.standard_normal((1, 1, 3, 2)); k = rng.standard_normal((1, 1, 6, 2)); v = rng.standard_normal((1, 1, 6, 2))
-    keys = [1, 4, 5]
-    o, l = attention_key_set_fp64(q, k, v, 0.9, True, keys)
-    for i in range(3):
-        # bottom-right causal: query i sees key j iff j <= i + 3
-        vis = [j for j in keys if j <= i + 3]
-        e = [math.exp(0.9 * sum(q[0, 0, i, c] * k[0, 0, j, c] for c in range(2))) for j in vis]
-        tot = sum(e)
-        for c in range(2):
-            want = sum(e[t] * v[0, 0, j, c] for t, j in enumerate(vis)) / tot
-            assert abs(o[0, 0, i, c] - want) < 1e-12
-        assert abs(l[0, 0, i] - math.log(tot)) < 1e-12
-    o, l = attention_key_set_fp64(q, k, v, 0.9, False, [])
-    assert (o == 0).all() and np.isneginf(l).all()
