@@ -396,9 +396,12 @@ def main():
             "dtype": "bf16", "data": "synthetic (seeded N(0,1), resident in HBM before timing)",
             "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
                        "causal": w.causal, "path": "fa_fwd_splitkv (attention kernel over key ranges + merge)"},
+            # achieved: algorithmic bytes over the whole step (attention kernel
+            # over the key ranges + the merge, one library call); traffic: HBM
+            # bytes of the attention kernel (rocprofv3 counters)
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                         "frac": round(gbs / 8000.0, 4), "traffic": None, "step_ms": round(ms, 5),
-                         "tflops": round(tflops, 2)},
+                         "frac": round(gbs / 8000.0, 4), "traffic": load_traffic("decode", "bf16"),
+                         "step_ms": round(ms, 5), "call_ms": round(kernel_ms, 5), "tflops": round(tflops, 2)},
         }
         print(json.dumps(line), flush=True)
         return
