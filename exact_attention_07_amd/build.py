@@ -23,6 +23,14 @@ ARCH = "gfx950"
 # Packed fp32 VALU instructions are kept out of the device code on purpose.
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Forward kernels: matrix-core results in VGPRs (-amdgpu-mfma-vgpr-form).
+# Where a forward kernel may use more than 256 registers per lane (head
+# dimension 256, or one wave per SIMD where LDS limits the occupancy), the
+# default keeps every MFMA result in AGPRs and copies the scores to VGPRs
+# and back around the softmax work.  The backward kernels keep the default:
+# their dK/dV accumulators are only ever MFMA operands and are best left in
+# AGPRs.  Kernels that fit in 256 VGPRs compile to the same code either way.
+EXTRA_FLAGS = {src: ["-mllvm", "-amdgpu-mfma-vgpr-form=1"] for src in ("fa_fwd.hip", "fa_fwd_fp8.hip")}
 
 
 def hipcc() -> str:
@@ -38,7 +46,7 @@ def build(verbose: bool = False) -> str:
 
     def compile_one(src):
         obj = os.path.join(HERE, "_build", src + ".o")
-        cmd = [hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
