@@ -150,6 +150,48 @@ static void check_packed(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int
       }
 }
 
+// Shapes near the library's size limits (the coverage arrays of the checks
+// above would not fit): sampled workgroup ids decode into range, tile counts
+// follow the visibility rule and key ranges stay inside the tiles.  Built
+// with the undefined-behaviour sanitizer, any signed overflow in the planning
+// arithmetic fails here.
+static unsigned long long lcg_state = 12345;
+static long long sample_id(long long n) {
+  lcg_state = lcg_state * 6364136223846793005ULL + 1442695040888963407ULL;
+  return (long long)((lcg_state >> 17) % (unsigned long long)n);
+}
+static void check_large_plan(fa_plan_t p) {
+  CHECK(p.nwg > 0 && p.nwg < (1LL << 31));
+  const long long fixed[] = {0, 1, p.nwg / 2, p.nwg - 1};
+  for (int s = 0; s < 2004; ++s) {
+    const long long id = s < 4 ? fixed[s] : sample_id(p.nwg);
+    fa_work_t w = fa_decode(p, id);
+    CHECK(w.b >= 0 && w.b < p.B && w.hkv >= 0 && w.hkv < p.Hkv && w.hq0 >= 0 && w.hq0 < p.Hq);
+    CHECK(w.hq0 / p.G == w.hkv && w.qpos0 >= 0 && w.qpos0 < p.Nq && w.split >= 0 && w.split < p.nsplit);
+    const int nt = fa_num_kv_tiles(p, w.qpos0, 64);
+    const long long rows = p.pack > 1 ? p.Nq : p.pos;
+    const long long qlast = w.qpos0 + rows - 1 < p.Nq - 1 ? w.qpos0 + rows - 1 : p.Nq - 1;
+    const long long kl = p.causal ? qlast + p.Nk - p.Nq : p.Nk - 1;
+    const long long klast = kl < p.Nk - 1 ? kl : p.Nk - 1;
+    CHECK(nt == (klast < 0 ? 0 : klast / 64 + 1));
+    int t0, t1;
+    fa_split_tiles(p, w.split, nt, t0, t1);
+    CHECK(0 <= t0 && t0 <= t1 && (t1 <= nt || t0 == t1));
+  }
+}
+static void check_large_kvplan(fa_kvplan_t p) {
+  CHECK(p.nwg > 0 && p.nwg < (1LL << 31));
+  for (int s = 0; s < 2004; ++s) {
+    const long long id = s < 2 ? s * (p.nwg - 1) : sample_id(p.nwg);
+    fa_kvwork_t w = fa_kv_decode(p, id);
+    CHECK(w.b >= 0 && w.b < p.B && w.hkv >= 0 && w.hkv < p.Hkv && w.k0 >= 0 && w.k0 < p.Nk && w.k0 % p.kpb == 0);
+    int first, ntq;
+    fa_kv_query_tiles(p, w.k0, 64, first, ntq);
+    CHECK(ntq == (p.Nq + 63) / 64 && 0 <= first && first <= ntq);
+    if (first > 0) CHECK(p.causal && (long long)first * 64 - 1 + p.Nk - p.Nq < w.k0);
+  }
+}
+
 int main() {
   for (int causal = 0; causal < 2; ++causal)
     for (int tps : {0, 1, 3, 100}) {
@@ -207,6 +249,16 @@ int main() {
   CHECK(c2.nw == 2 && c2.nwg == 8 * 12 * 16);
   fa_plan_t c3 = fa_choose_plan(2, 32, 8, 8192, 8192, 1, 32, 1024, 8);
   CHECK(c3.nw == 8 && c3.hw == 4 && c3.pos == 64 && c3.nwg == 2048);
+  for (int causal = 0; causal < 2; ++causal) {
+    check_large_plan(fa_make_plan(64, 128, 8, 1 << 20, 1 << 20, causal, 32, 8));   // 33.5 M workgroups
+    check_large_plan(fa_make_plan(1, 1, 1, 8000000, 8000000, causal, 32, 4));      // d = 64 key limit
+    check_large_plan(fa_make_plan(2, 64, 64, 1000000, 3000000, causal, 32, 2));    // Nq < Nk
+    check_large_plan(fa_split_plan(fa_make_plan(4, 16, 2, 7, 8000000, causal, 32, 8), 1, 64));
+    check_large_plan(fa_split_plan(fa_make_packed_plan(64, 32, 8, 1, 8000000, causal), 5, 64));
+    check_large_kvplan(fa_make_kvplan(64, 128, 8, 1 << 20, 1 << 20, causal, 32, 8));
+    check_large_kvplan(fa_make_kvplan(1, 4, 1, 8000000, 3000000, causal, 64, 4));
+    check_large_kvplan(fa_make_kvplan(2, 8, 8, 5, 8000000, causal, 32, 1));
+  }
   std::printf("plan checks passed\n");
   return 0;
 }
