@@ -7,6 +7,8 @@
 * The parts the kernel leaves in the workspace against the definition over
   each key range (attention_keys_fp64), which pins the range arithmetic and
   the layout the header documents.
+* The decoding workload at full size (B8 Hq32 Hkv8, 32768 keys) in the
+  launch configuration the benchmark times, on every row.
 """
 import math
 
@@ -124,3 +126,17 @@ def test_splitkv_workspace_errors(api):
     with pytest.raises(api.FaError) as e:
         api.fa_fwd_splitkv(q, k, k, o, None, 0.1, False, 4, small)
     assert e.value.status == 9
+
+
+def test_decode_workload_full_size(api):
+    """The decoding workload the benchmark times (GQA B8 Hq32 Hkv8, one query
+    over 32768 keys, d = 128, causal), in its launch configuration (the
+    library's own split count), against the oracle on every one of its 256
+    rows."""
+    w, x = gen.make_config("decode")
+    print(f"case: splitkv full size {w.name}", flush=True)
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    o, lse = api.attention_splitkv(q, k, v, causal=w.causal, scale=w.softmax_scale, nsplit=0)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = attention_fp64(*(to_f64(x[t], "bf16") for t in "qkv"), w.softmax_scale, w.causal)
+    compare(out_to_f64(o), lse.cpu().numpy().astype(np.float64), o_ref, lse_ref, what=w.name)
