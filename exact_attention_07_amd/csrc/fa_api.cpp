@@ -64,12 +64,8 @@ bool packable(int Hq, int Hkv, int Nq) { return Hq / Hkv > 1 && (long long)(Hq /
 fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int kind) {
   if (kind == KIND_BF16 && packable(Hq, Hkv, Nq)) return fa_make_packed_plan(B, Hq, Hkv, Nq, Nk, causal);
   const int qpw = fa::queries_per_wave(d, kind == KIND_F32);
-  // fp32: 4-wave workgroups.  fp8: up to 4 waves (two workgroups share a CU
-  // at d <= 128).  bf16 at d = 128: up to 8 waves, one workgroup per CU, so
-  // that each K/V tile copied from L2 serves twice the query rows.
   if (kind == KIND_F32) return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4);
-  const int max_nw = (kind == KIND_BF16 && d == 128) ? 8 : 4;
-  return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, MIN_WORKGROUPS, max_nw);
+  return fa_forward_plan(B, Hq, Hkv, Nq, Nk, causal, d, kind == KIND_FP8, qpw);
 }
 
 // Key-split plan of the bf16 path.  Few query rows: one workgroup holds all

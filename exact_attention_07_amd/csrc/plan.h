@@ -109,16 +109,40 @@ FA_HD inline fa_plan_t fa_split_plan(fa_plan_t p, int tps, int bc) {
   return p;
 }
 
-// Waves per workgroup: the largest power of two <= max_nw that still leaves
-// at least `min_wg` workgroups (enough to fill the chip several times); 1
-// otherwise.
+// Waves per workgroup: the largest power of two in [min_nw, max_nw] that
+// still leaves at least `min_wg` workgroups; min_nw otherwise.
 FA_HD inline fa_plan_t fa_choose_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int qpw,
-                                      long long min_wg, int max_nw) {
-  for (int nw = max_nw; nw > 1; nw >>= 1) {
+                                      long long min_wg, int max_nw, int min_nw = 1) {
+  for (int nw = max_nw; nw > min_nw; nw >>= 1) {
     fa_plan_t p = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, nw);
     if (p.nwg >= min_wg) return p;
   }
-  return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 1);
+  return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, min_nw);
+}
+
+// Waves per workgroup of the bf16 and fp8 forward kernels.  A workgroup's
+// K/V ring takes the same LDS whatever its wave count (bf16: 43 KB at
+// d = 64, 75 KB at d = 128, 139 KB at d = 256; fp8: 21, 39, 75 KB), so LDS
+// caps the workgroups per CU (3, 2, 1; 7, 4, 2) and too few waves per
+// workgroup leave SIMDs idle: one-wave workgroups at d = 128 put 2 waves on
+// a CU that holds 8.  Measured over 16 bf16 and 6 fp8 shapes (d = 64, 128,
+// 256; 8 K to 524 K query rows), every choice below is the fastest or within
+// 2.5 % of it, and up to 2.7x faster than the fewest waves that still leave
+// 1024 workgroups:
+//   bf16 d = 256: 4 waves, one workgroup per CU;
+//   bf16 d = 128: 8 waves with at least 1024 workgroups (each K/V tile then
+//     serves 256 query rows, at 4 or more workgroups per CU for the balance
+//     of causal work), else 4;
+//   bf16 d = 64, fp8 d = 256: 4 waves with at least 512 workgroups, else 2;
+//   fp8 d <= 128: 4 waves with at least 1024 workgroups, else 2, else 1
+//     (4 to 7 one-wave workgroups share a CU, and smaller workgroups
+//     balance causal work better).
+FA_HD inline fa_plan_t fa_forward_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int d, int fp8,
+                                       int qpw) {
+  if (!fp8 && d == 256) return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4);
+  if (!fp8 && d == 128) return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 1024, 8, 4);
+  if (fp8 && d <= 128) return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 1024, 4, 1);
+  return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 512, 4, 2);
 }
 
 struct fa_work_t {

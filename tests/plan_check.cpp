@@ -259,6 +259,24 @@ int main() {
     check_large_kvplan(fa_make_kvplan(1, 4, 1, 8000000, 3000000, causal, 64, 4));
     check_large_kvplan(fa_make_kvplan(2, 8, 8, 5, 8000000, causal, 32, 1));
   }
+  // forward wave counts: the occupancy rule of fa_forward_plan
+  CHECK(fa_forward_plan(2, 32, 8, 8192, 8192, 1, 128, 0, 32).nw == 8);    // 2048 workgroups of 8 waves
+  CHECK(fa_forward_plan(16, 16, 16, 512, 512, 1, 128, 0, 32).nw == 4);    // 8 waves would leave 512
+  CHECK(fa_forward_plan(4, 8, 8, 1024, 1024, 0, 128, 0, 32).nw == 4);     // never fewer than 4 at d = 128
+  CHECK(fa_forward_plan(1, 1, 1, 1, 77, 0, 128, 0, 32).nw == 4);
+  CHECK(fa_forward_plan(4, 16, 16, 4096, 4096, 0, 256, 0, 32).nw == 4);   // d = 256: always 4
+  CHECK(fa_forward_plan(1, 2, 2, 70, 70, 1, 256, 0, 32).nw == 4);
+  CHECK(fa_forward_plan(8, 12, 12, 1024, 1024, 1, 64, 0, 32).nw == 4);    // 768 workgroups of 4 waves
+  CHECK(fa_forward_plan(1, 12, 12, 4096, 4096, 1, 64, 0, 32).nw == 2);    // 384 would be too few
+  CHECK(fa_forward_plan(4, 16, 16, 8192, 8192, 0, 128, 1, 32).nw == 4);   // fp8: up to 4
+  CHECK(fa_forward_plan(2, 8, 8, 2048, 2048, 1, 128, 1, 32).nw == 1);     // fp8 d <= 128: 1024 one-wave workgroups
+  CHECK(fa_forward_plan(1, 8, 8, 2048, 2048, 1, 256, 1, 32).nw == 2);     // fp8 d = 256: at least 2
+  for (int d : {64, 128, 256})
+    for (int fp8 = 0; fp8 < 2; ++fp8) {
+      const fa_plan_t f = fa_forward_plan(3, 12, 4, 333, 500, 1, d, fp8, 32);
+      CHECK(f.nw >= (fp8 && d <= 128 ? 1 : 2) && f.nw <= (d == 128 && !fp8 ? 8 : 4));
+      check_plan(3, 12, 4, 333, 500, 1, 32, f.nw);
+    }
   std::printf("plan checks passed\n");
   return 0;
 }
