@@ -107,14 +107,18 @@ size_t splitkv_workspace_bytes(const fa_plan_t& p, int d) {
   return (size_t)p.nsplit * rows * (size_t)(d + 1) * sizeof(float);
 }
 
-// Backward plans.  dQ: the forward kernel's plan (32 query rows per wave,
-// up to bwd_dq_max_waves waves).  dK/dV: key blocks of up to
-// bwd_dkdv_max_waves waves (a workgroup of that size fills a CU on its
-// own), fewer while the grid would have under MIN_KV_WORKGROUPS workgroups.
+// Backward plans.  dQ: the forward kernel's plan (32 query rows per wave).
+// dK/dV: key blocks of up to bwd_dkdv_max_waves waves (a workgroup of that
+// size fills a CU on its own), fewer while the grid would have under
+// MIN_KV_WORKGROUPS workgroups.
 constexpr long long MIN_KV_WORKGROUPS = 512;
 
+// The dQ kernel has the forward kernel's shape, K/V ring and occupancy, and
+// the forward's wave-count rule (plan.h, fa_forward_plan) measured the
+// fastest or within 4 % of it over 13 shapes (d = 64, 128, 256), up to 3.6x
+// faster than the most waves that still leave 1024 workgroups.
 fa_plan_t plan_bwd_dq(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
-  return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, 32, MIN_WORKGROUPS, fa::bwd_dq_max_waves(d));
+  return fa_forward_plan(B, Hq, Hkv, Nq, Nk, causal, d, 0, 32);
 }
 
 fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
@@ -122,11 +126,14 @@ fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
   // at d = 256 one workgroup fills a CU's LDS, so 256 workgroups fill the
   // chip once; fewer waves per workgroup would leave SIMDs idle
   const long long min_wg = d == 256 ? 256 : MIN_KV_WORKGROUPS;
-  for (int nw = fa::bwd_dkdv_max_waves(d); nw > 1; nw >>= 1) {
+  // at d = 128 never fewer than 2 waves: one-wave workgroups leave most of a
+  // CU idle (B1 H8 N2048 d128: 132 us against 69 us with two waves)
+  const int min_nw = d == 128 ? 2 : 1;
+  for (int nw = fa::bwd_dkdv_max_waves(d); nw > min_nw; nw >>= 1) {
     const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
     if (p.nwg >= min_wg) return p;
   }
-  return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, 1);
+  return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, min_nw);
 }
 
 size_t bwd_workspace_bytes(int B, int Hq, int Nq) { return (size_t)B * Hq * Nq * 2 * sizeof(float); }

@@ -477,8 +477,6 @@ int bwd_keys_per_wave(int d) { return d == 64 ? 64 : 32; }
 
 int bwd_dkdv_max_waves(int d) { return d == 64 ? 4 : d == 128 ? 8 : 4; }
 
-int bwd_dq_max_waves(int d) { return d == 256 ? 4 : 8; }
-
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, void* dq, float* ld, const fa_plan_t& pq, int d, float c, float scale,
                          hipStream_t stream) {

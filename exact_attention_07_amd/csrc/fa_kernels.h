@@ -39,10 +39,9 @@ hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, void*
                               int Nk, int d, hipStream_t stream);
 
 // Backward pass: keys per wave and most waves per workgroup of the dK/dV
-// kernel, most waves per workgroup of the dQ kernel, for head dimension d.
+// kernel for head dimension d.
 int bwd_keys_per_wave(int d);
 int bwd_dkdv_max_waves(int d);
-int bwd_dq_max_waves(int d);
 
 // Enqueue the dQ kernel of the backward pass (plan pq).  It also writes the
 // per-row pairs (LSE log2 e, rowsum(dO o O)) into ld, [B][Hq][Nq][2] fp32.
