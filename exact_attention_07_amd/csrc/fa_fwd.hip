@@ -387,17 +387,22 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   }
   const size_t qrow0 = (size_t)(w.b * p.Hq + hq_l) * Nq;  // first row of the lane's head
 
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
+
+  // A range without key tiles (causal rows that see no key, or a key range
+  // past every visible key of the workgroup's rows; uniform over the
+  // workgroup) loads and copies nothing: the epilogue writes O = 0 and
+  // LSE = -inf straight away.
+  if (t1 > t0) {
   bf16x8 qf[1][DS];
   {
     const int qrow = min(q_l, Nq - 1);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[0][ds] = *(const bf16x8*)(Q + (qrow0 + qrow) * D + ds * 16 + (lane >> 5) * 8);
   }
-
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
-  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
 
   const int koff_l = k_lane_off<RSK>(lane);
   const int voff_l = v_lane_off<RSV>(lane);
@@ -551,6 +556,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   // the last copies (zeros past the final tile) land before the workgroup's
   // LDS can pass to another workgroup
   vm_wait<0>();
+  }  // t1 > t0
 
   // ---- epilogue: O / l, LSE = ln2 * (m_ref + log2 l); with a key split, the
   // range's partial result (fp32) goes to the workspace for the merge

@@ -130,9 +130,10 @@ FA_HD inline fa_plan_t fa_choose_plan(int B, int Hq, int Hkv, int Nq, int Nk, in
 // 2.5 % of it, and up to 2.7x faster than the fewest waves that still leave
 // 1024 workgroups:
 //   bf16 d = 256: 4 waves, one workgroup per CU;
-//   bf16 d = 128: 8 waves with at least 1024 workgroups (each K/V tile then
-//     serves 256 query rows, at 4 or more workgroups per CU for the balance
-//     of causal work), else 4;
+//   bf16 d = 128: 8 waves with at least 1024 workgroups, 2048 if causal
+//     (each K/V tile then serves 256 query rows; causal work, which differs
+//     between query blocks, needs the finer grid to balance: 4-wave
+//     workgroups measured 6-11 % faster at 1024), else 4;
 //   bf16 d = 64, fp8 d = 256: 4 waves with at least 512 workgroups, else 2;
 //   fp8 d <= 128: 4 waves with at least 1024 workgroups, else 2, else 1
 //     (4 to 7 one-wave workgroups share a CU, and smaller workgroups
@@ -140,7 +141,7 @@ FA_HD inline fa_plan_t fa_choose_plan(int B, int Hq, int Hkv, int Nq, int Nk, in
 FA_HD inline fa_plan_t fa_forward_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int d, int fp8,
                                        int qpw) {
   if (!fp8 && d == 256) return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4);
-  if (!fp8 && d == 128) return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 1024, 8, 4);
+  if (!fp8 && d == 128) return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, causal ? 2048 : 1024, 8, 4);
   if (fp8 && d <= 128) return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 1024, 4, 1);
   return fa_choose_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 512, 4, 2);
 }

@@ -261,6 +261,8 @@ int main() {
   }
   // forward wave counts: the occupancy rule of fa_forward_plan
   CHECK(fa_forward_plan(2, 32, 8, 8192, 8192, 1, 128, 0, 32).nw == 8);    // 2048 workgroups of 8 waves
+  CHECK(fa_forward_plan(4, 16, 16, 4096, 4096, 1, 128, 0, 32).nw == 4);   // causal: 1024 of 8 are too few
+  CHECK(fa_forward_plan(4, 16, 16, 4096, 4096, 0, 128, 0, 32).nw == 8);   // not causal: 1024 suffice
   CHECK(fa_forward_plan(16, 16, 16, 512, 512, 1, 128, 0, 32).nw == 4);    // 8 waves would leave 512
   CHECK(fa_forward_plan(4, 8, 8, 1024, 1024, 0, 128, 0, 32).nw == 4);     // never fewer than 4 at d = 128
   CHECK(fa_forward_plan(1, 1, 1, 1, 77, 0, 128, 0, 32).nw == 4);
