@@ -283,7 +283,8 @@ def fa_bwd_dq(q, k, v, o, lse, do, dq, scale: float, causal: bool, workspace, st
 
 
 def fa_bwd_dkdv(q, k, v, o, lse, do, dk, dv, scale: float, causal: bool, workspace, stream=None) -> None:
-    """Second stage of fa_bwd: dk and dv from the workspace fa_bwd_dq filled (o, lse: shape checks only)."""
+    """Second stage of fa_bwd: dk and dv from the pairs fa_bwd_dq left in the workspace, which also takes
+    the partial sums when the heads of a group are split (o, lse: shape checks only)."""
     dims, nbytes = _bwd_args(q, k, v, o, lse, do, q, dk, dv, workspace)
     _check(lib().fa_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(dk), _ptr(dv), *dims, float(scale),
                              int(bool(causal)), _ptr(workspace), nbytes, _stream(stream)), "fa_bwd_dkdv")

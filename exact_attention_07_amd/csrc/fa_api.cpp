@@ -133,10 +133,28 @@ fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
     const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
     if (p.nwg >= min_wg) return p;
   }
-  return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, min_nw);
+  const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, min_nw);
+  if (p.nwg >= min_wg || p.G == 1) return p;
+  // Too few (group, key block) pairs even with the smallest workgroups: a
+  // group's query heads are split into parts (the fewest that reach min_wg
+  // workgroups; a divisor of G) at the largest workgroups, each part adding
+  // its heads' share of dK and dV into an fp32 partial sum in the workspace.
+  const fa_kvplan_t big = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, fa::bwd_dkdv_max_waves(d));
+  for (int parts = 2; parts < p.G; ++parts)
+    if (p.G % parts == 0 && big.nwg * parts >= min_wg) return fa_split_kvplan_heads(big, parts);
+  return fa_split_kvplan_heads(big, p.G);
 }
 
-size_t bwd_workspace_bytes(int B, int Hq, int Nq) { return (size_t)B * Hq * Nq * 2 * sizeof(float); }
+// Workspace of the backward pass: the (L2, D) pair of every query row,
+// rounded up to 256 bytes, then (with the heads of a group split into parts)
+// the parts' fp32 partial sums of dK and of dV.
+size_t bwd_pairs_bytes(int B, int Hq, int Nq) { return ((size_t)B * Hq * Nq * 2 * sizeof(float) + 255) / 256 * 256; }
+size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
+  const fa_kvplan_t pk = plan_bwd_dkdv(B, Hq, Hkv, Nq, Nk, d, causal);
+  size_t n = bwd_pairs_bytes(B, Hq, Nq);
+  if (pk.hsplit > 1) n += (size_t)2 * pk.hsplit * B * Hkv * (size_t)Nk * d * sizeof(float);
+  return n;
+}
 
 }  // namespace
 
@@ -233,7 +251,7 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
   if (validate_shape(B, Hq, Hkv, Nq, Nk, d) != FA_OK || (causal != 0 && causal != 1)) return 0;
-  return bwd_workspace_bytes(B, Hq, Nq);
+  return bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal);
 }
 
 namespace {
@@ -252,7 +270,8 @@ fa_status validate_bwd(const void* const* ptrs, int nptrs, int B, int Hq, int Hk
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
   // one query head's rows (the range of a buffer resource) fit in 31 bits
   if (((double)Nq + 64.0) * d * 4.0 >= 2147483648.0) return FA_ERR_SHAPE;
-  if (workspace == nullptr || workspace_bytes < bwd_workspace_bytes(B, Hq, Nq) || !aligned16(workspace))
+  if (workspace == nullptr || workspace_bytes < bwd_workspace_bytes(B, Hq, Hkv, Nq, Nk, d, causal) ||
+      !aligned16(workspace))
     return FA_ERR_WORKSPACE;
   return FA_OK;
 }
@@ -271,14 +290,15 @@ fa_status bwd_dq(const void* q, const void* k, const void* v, const void* o, con
 }
 
 fa_status bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B, int Hq,
-                   int Hkv, int Nq, int Nk, int d, float scale, int causal, const void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   int Hkv, int Nq, int Nk, int d, float scale, int causal, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   const void* ptrs[] = {q, k, v, dout, dk, dv};
   const fa_status st = validate_bwd(ptrs, 6, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes);
   if (st != FA_OK) return st;
   const fa_kvplan_t pk = plan_bwd_dkdv(B, Hq, Hkv, Nq, Nk, d, causal);
   if (pk.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
-  const hipError_t e = fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, (const float*)workspace, pk, d,
+  float* part = pk.hsplit > 1 ? (float*)((char*)workspace + bwd_pairs_bytes(B, Hq, Nq)) : nullptr;
+  const hipError_t e = fa::launch_bwd_dkdv(q, k, v, dout, dk, dv, (const float*)workspace, part, pk, d,
                                            (float)((double)scale * LOG2E), scale, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -292,7 +312,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, 
 }
 
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv, int B,
-                      int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, const void* workspace,
+                      int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* workspace,
                       size_t workspace_bytes, void* stream) {
   return bwd_dkdv(q, k, v, dout, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes, stream);
 }

@@ -238,7 +238,7 @@ template <int D, bool CAUSAL, int NW, int KBW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1)))
 void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                         const __bf16* __restrict__ dO, const float* __restrict__ LD, __bf16* __restrict__ dK,
-                        __bf16* __restrict__ dV, fa_kvplan_t p, float c, float scale) {
+                        __bf16* __restrict__ dV, float* __restrict__ PART, fa_kvplan_t p, float c, float scale) {
   using C = BwdCfg<D>;
   constexpr int DS = C::DS, DB = C::DB, RSX = C::RSX;
   constexpr int KPW = 32 * KBW;
@@ -268,6 +268,8 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   const int h = lane >> 5;
   const int k0w = w.k0 + wave * KPW;
   const int Nq = p.Nq, Nk = p.Nk, off = Nk - Nq, G = p.G;
+  // the workgroup's query heads: hps heads of part w.hs of the group
+  const int HP = p.hps, h0 = w.hs * p.hps;
   const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
   const bool has_keys = k0w < Nk;
 
@@ -302,16 +304,17 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
   int first, ntq;
   fa_kv_query_tiles(p, w.k0, BC, first, ntq);
-  // iterations: query tiles ntq - 1 down to first, the G heads of the group
-  // innermost; (t_c, h_c) is the tile and head of the iteration computed
-  const int total = (ntq - first) * G;
+  // iterations: query tiles ntq - 1 down to first, the HP heads of the
+  // workgroup innermost; (t_c, h_c) is the tile and head of the iteration
+  // computed
+  const int total = (ntq - first) * HP;
   int t_c = ntq - 1, h_c = 0;
 
   const int qoff_l = k_lane_off_p<RSX>(lane), toff_l = v_lane_off_p<RSX>(lane);
   CopyQ cp;
   cp.init(wave, lane);
   auto issue = [&](int t, int hh, auto par) {
-    const int hq = w.hkv * G + hh;
+    const int hq = w.hkv * G + h0 + hh;
     const size_t rb = (size_t)(w.b * p.Hq + hq) * Nq;
     const __amdgpu_buffer_rsrc_t rq = CopyQ::rsrc(Q + rb * D, Nq), ro = CopyQ::rsrc(dO + rb * D, Nq);
     cp.issue_all(rq, t * (BC * D * 2), qslot(par), spare, wave);
@@ -410,8 +413,8 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
     using other = std::integral_constant<int, 1 - decltype(par)::value>;
     vm_wait<0>();
     __syncthreads();
-    const int h_n = h_c + 1 == G ? 0 : h_c + 1;
-    const int t_n = h_c + 1 == G ? t_c - 1 : t_c;
+    const int h_n = h_c + 1 == HP ? 0 : h_c + 1;
+    const int t_n = h_c + 1 == HP ? t_c - 1 : t_c;
     if (it + 1 < total) issue(t_n, h_n, other{});
     const int q0 = t_c * BC;
     if (has_keys && (!CAUSAL || q0 + BC - 1 + off >= k0w)) compute(q0, par);
@@ -425,11 +428,33 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   }
   vm_wait<0>();
 
+  // with the heads split into parts, this part's sums (dK already scaled)
+  // go to its fp32 slice of the workspace; fa_bwd_reduce_kernel adds them
+  const size_t part_elems = (size_t)p.B * p.Hkv * Nk * D;
 #pragma unroll
   for (int kb = 0; kb < KBW; ++kb) {
     const int key = k0w + kb * 32 + (lane & 31);
     if (key >= Nk) continue;
     const size_t krow = kvoff + (size_t)key * D;
+    if (p.hsplit > 1) {
+      float* pk = PART + (size_t)w.hs * part_elems + krow;
+      float* pv = PART + (size_t)(p.hsplit + w.hs) * part_elems + krow;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int d0 = db * 32 + i4 * 8 + h * 4;
+          f32x4 rk, rv;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            rk[e] = dk[kb][db][i4 * 4 + e] * scale;
+            rv[e] = dv[kb][db][i4 * 4 + e];
+          }
+          *(f32x4*)(pk + d0) = rk;
+          *(f32x4*)(pv + d0) = rv;
+        }
+      continue;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -448,6 +473,26 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 }
 
 // ---------------------------------------------------------------- launchers
+// dK and dV from the head parts' partial sums: for every element, the sum
+// over the parts of the fp32 partials (dK's already scaled), rounded to bf16.
+// PART holds [parts][B][Hkv][Nk][d] for dK, then the same for dV; n4 is the
+// number of 4-element groups of one tensor.  A grid-stride loop over both.
+__global__ __launch_bounds__(256) void fa_bwd_reduce_kernel(const float* __restrict__ PART, int parts, long long n4,
+                                                            __bf16* __restrict__ dK, __bf16* __restrict__ dV) {
+  const long long n = 4 * n4;
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < 2 * n4; i += (long long)gridDim.x * 256) {
+    const int tensor = i < n4 ? 0 : 1;
+    const long long j = i - tensor * n4;
+    const float* src = PART + (size_t)tensor * parts * n + 4 * j;
+    f32x4 acc = *(const f32x4*)src;
+    for (int sp = 1; sp < parts; ++sp) acc += *(const f32x4*)(src + (size_t)sp * n);
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = (__bf16)acc[e];
+    *(bf16x4*)((tensor == 0 ? dK : dV) + 4 * j) = r;
+  }
+}
+
 #define FA_INST_DQ(DD, CC, NN)                                                                                  \
   template __global__ void fa_bwd_dq_kernel<DD, CC, NN>(                                                       \
       const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, \
@@ -464,7 +509,8 @@ FA_DQ_VARIANTS(FA_INST_DQ)
 #define FA_INST_DKDV(DD, CC, NN, KK)                                                                           \
   template __global__ void fa_bwd_dkdv_kernel<DD, CC, NN, KK>(                                                \
       const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, \
-      const float* __restrict__, __bf16* __restrict__, __bf16* __restrict__, fa_kvplan_t, float, float);
+      const float* __restrict__, __bf16* __restrict__, __bf16* __restrict__, float* __restrict__, fa_kvplan_t,   \
+      float, float);
 // (head dim, causal, waves per workgroup, 32-key blocks per wave)
 #define FA_DKDV_VARIANTS(X)                                                                                  \
   X(64, false, 1, 2) X(64, false, 2, 2) X(64, false, 4, 2) X(64, true, 1, 2) X(64, true, 2, 2)                 \
@@ -493,17 +539,25 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 }
 
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
-                           const float* ld, const fa_kvplan_t& pk, int d, float c, float scale, hipStream_t stream) {
+                           const float* ld, float* part, const fa_kvplan_t& pk, int d, float c, float scale,
+                           hipStream_t stream) {
+  if (pk.hsplit > 1 && part == nullptr) return hipErrorInvalidValue;
+  hipError_t e = hipErrorInvalidValue;
 #define FA_CASE_DKDV(DD, CC, NN, KK)                                                                        \
   if (d == DD && (pk.causal != 0) == CC && pk.nw == NN && pk.kpw == 32 * KK) {                              \
     hipLaunchKernelGGL((fa_bwd_dkdv_kernel<DD, CC, NN, KK>), dim3((unsigned)pk.nwg), dim3(64 * NN), 0, stream, \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld,          \
-                       (__bf16*)dk, (__bf16*)dv, pk, c, scale);                                               \
-    return hipGetLastError();                                                                               \
-  }
-  FA_DKDV_VARIANTS(FA_CASE_DKDV)
+                       (__bf16*)dk, (__bf16*)dv, part, pk, c, scale);                                         \
+    e = hipGetLastError();                                                                                  \
+  } else
+  FA_DKDV_VARIANTS(FA_CASE_DKDV) {}
 #undef FA_CASE_DKDV
-  return hipErrorInvalidValue;
+  if (e != hipSuccess || pk.hsplit == 1) return e;
+  const long long n4 = (long long)pk.B * pk.Hkv * pk.Nk * d / 4;  // float4 groups per tensor
+  const long long blocks = (2 * n4 + 255) / 256;
+  hipLaunchKernelGGL(fa_bwd_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream,
+                     (const float*)part, pk.hsplit, n4, (__bf16*)dk, (__bf16*)dv);
+  return hipGetLastError();
 }
 
 }  // namespace fa

@@ -52,8 +52,12 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
 
 // Enqueue the dK/dV kernel of the backward pass (plan pk); reads the pairs
 // launch_bwd_dq wrote into ld.
+// With pk.hsplit > 1 the partial sums of the head parts go to `part`
+// (2 * hsplit * B * Hkv * Nk * d floats, 16-byte aligned) and a second kernel
+// adds them into dK and dV.
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
-                           const float* ld, const fa_kvplan_t& pk, int d, float c, float scale, hipStream_t stream);
+                           const float* ld, float* part, const fa_kvplan_t& pk, int d, float c, float scale,
+                           hipStream_t stream);
 
 }  // namespace fa
 

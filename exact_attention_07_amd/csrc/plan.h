@@ -217,6 +217,8 @@ struct fa_kvplan_t {
   int nw;    // waves per workgroup
   int kpb;   // keys per workgroup
   int nkb;   // key blocks per key/value head: ceil(Nk / kpb)
+  int hsplit;  // parts the G query heads of a group are split into (divides G)
+  int hps;     // query heads per part: G / hsplit
   int xcd;
   long long nwg;
 };
@@ -229,22 +231,40 @@ FA_HD inline fa_kvplan_t fa_make_kvplan(int B, int Hq, int Hkv, int Nq, int Nk, 
   p.nw = nw;
   p.kpb = kpw * nw;
   p.nkb = (Nk + p.kpb - 1) / p.kpb;
+  p.hsplit = 1;
+  p.hps = p.G;
   p.nwg = (long long)B * Hkv * p.nkb;
+  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  return p;
+}
+
+// Split the G query heads of every group of plan p into `parts` parts of
+// G / parts heads (parts divides G): parts times the workgroups, each adding
+// its heads' share of dK and dV into a partial sum.
+FA_HD inline fa_kvplan_t fa_split_kvplan_heads(fa_kvplan_t p, int parts) {
+  p.hsplit = parts;
+  p.hps = p.G / parts;
+  p.nwg = (long long)p.B * p.Hkv * p.nkb * parts;
   p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
   return p;
 }
 
 struct fa_kvwork_t {
   int b, hkv, k0;  // batch, kv head, first key of the workgroup
+  int hs;          // part of the group's query heads (0 without a split)
 };
 
-// Workgroup hardware id -> its key block; a bijection of [0, nwg) onto the
-// (group, key block) pairs.
+// Workgroup hardware id -> its key block and head part; a bijection of
+// [0, nwg) onto the (group, head part, key block) triples, key blocks
+// innermost, so that the workgroups of one (group, head part), which read
+// the same query tiles, run on one XCD.
 FA_HD inline fa_kvwork_t fa_kv_decode(const fa_kvplan_t& p, long long id) {
   const long long L = p.xcd ? (id % 8) * (p.nwg / 8) + id / 8 : id;
   fa_kvwork_t w;
-  const long long g = L / p.nkb;
+  const long long gs = L / p.nkb;
   w.k0 = (int)(L % p.nkb) * p.kpb;
+  w.hs = (int)(gs % p.hsplit);
+  const long long g = gs / p.hsplit;
   w.hkv = (int)(g % p.Hkv);
   w.b = (int)(g / p.Hkv);
   return w;

@@ -184,11 +184,16 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const floa
  *   dout       dL/dO, bf16, q's layout
  *   dq         out: dL/dQ, bf16, q's layout
  *   dk, dv     out: dL/dK, dL/dV, bf16, k's layout (every element written)
- *   workspace  device memory of at least fa_bwd_workspace_size(...) bytes
- *              (8 bytes per query row: B * Hq * Nq * 8), 16-byte aligned,
- *              owned by the caller and not shared with a call in flight.
- *              It holds the per-row pair (LSE log2(e), D) between the two
- *              kernels; its contents on entry do not matter.
+ *   workspace  device memory of at least fa_bwd_workspace_size(...) bytes,
+ *              16-byte aligned, owned by the caller and not shared with a
+ *              call in flight; its contents on entry do not matter.  It
+ *              holds the per-row pair (LSE log2(e), D) between the two
+ *              kernels (B * Hq * Nq * 8 bytes, rounded up to 256).  When a
+ *              group has too few key blocks to fill the GPU (few key/value
+ *              heads, G = Hq / Hkv > 1), the G query heads of each group are
+ *              split into parts whose fp32 partial sums of dK and dV follow
+ *              the pairs (2 * parts * B * Hkv * Nk * d * 4 bytes) and are
+ *              added by a second kernel; fa_bwd_workspace_size includes them.
  * Products run on bf16 MFMA with fp32 accumulation; P and dS multiply in
  * bf16; the gradients are rounded to bf16 (nearest even).  D is formed from
  * the bf16 O.  Rows that see no key (LSE = -inf) contribute nothing.
@@ -200,9 +205,10 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const floa
  * fa_bwd runs two kernels in stream order, also available on their own:
  *   fa_bwd_dq    dq, plus the per-row pairs (LSE log2(e), D) into the
  *                workspace ([B][Hq][Nq][2] float32);
- *   fa_bwd_dkdv  dk and dv; reads those pairs, so it must follow an
- *                fa_bwd_dq with the same arguments and workspace (on the same
- *                stream, or after it has completed).
+ *   fa_bwd_dkdv  dk and dv; reads those pairs (and writes the partial
+ *                sums, if any, after them), so it must follow an fa_bwd_dq
+ *                with the same arguments and workspace (on the same stream,
+ *                or after it has completed).
  * fa_bwd(...) is fa_bwd_dq(...) followed by fa_bwd_dkdv(...).
  */
 size_t fa_bwd_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal);
@@ -215,7 +221,7 @@ fa_status fa_bwd_dq(const void* q, const void* k, const void* v, const void* o, 
                     float scale, int causal, void* workspace, size_t workspace_bytes, void* stream);
 fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk, void* dv,
                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
-                      const void* workspace, size_t workspace_bytes, void* stream);
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -118,6 +118,28 @@ static void check_kvplan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int
   if (!p.xcd && p.nkb > 1) CHECK(fa_kv_decode(p, 0).k0 == 0 && fa_kv_decode(p, 1).k0 == p.kpb);
 }
 
+// Key plans whose groups' query heads are split into parts: every
+// (b, query head, key) is covered by exactly one workgroup, whose part holds
+// the head, and the decode is a bijection onto (group, part, key block).
+static void check_kvplan_split(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int kpw, int nw, int parts) {
+  fa_kvplan_t p = fa_split_kvplan_heads(fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw), parts);
+  CHECK(p.hsplit == parts && p.hps * parts == p.G && p.nwg == (long long)B * Hkv * p.nkb * parts);
+  std::vector<int> cover((size_t)B * Hq * Nk, 0);
+  std::set<std::tuple<int, int, int, int>> seen;
+  for (long long id = 0; id < p.nwg; ++id) {
+    fa_kvwork_t w = fa_kv_decode(p, id);
+    CHECK(w.b >= 0 && w.b < B && w.hkv >= 0 && w.hkv < Hkv && w.hs >= 0 && w.hs < parts);
+    CHECK(w.k0 >= 0 && w.k0 < Nk && w.k0 % p.kpb == 0);
+    CHECK(seen.insert({w.b, w.hkv, w.hs, w.k0}).second);
+    for (int hh = 0; hh < p.hps; ++hh) {
+      const int hq = w.hkv * p.G + w.hs * p.hps + hh;
+      CHECK(hq / p.G == w.hkv);
+      for (int j = w.k0; j < w.k0 + p.kpb && j < Nk; ++j) cover[((size_t)w.b * Hq + hq) * Nk + j]++;
+    }
+  }
+  for (int c : cover) CHECK(c == 1);
+}
+
 // Packed plans: every (b, query head, query row) is the column of exactly
 // one (workgroup, lane column), all heads of a workgroup read its kv head.
 static void check_packed(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int tps) {
@@ -211,6 +233,13 @@ int main() {
         check_kvplan(1, 3, 3, 40, 150, causal, kpw, nw);
         check_kvplan(3, 5, 5, 1, 100, causal, kpw, nw);
       }
+  for (int causal = 0; causal < 2; ++causal)
+    for (int nw : {1, 2, 8}) {
+      check_kvplan_split(2, 16, 1, 300, 700, causal, 32, nw, 4);   // MQA, 4 parts of 4 heads
+      check_kvplan_split(1, 12, 2, 100, 333, causal, 64, nw, 3);   // G = 6 in 3 parts
+      check_kvplan_split(3, 8, 8, 64, 100, causal, 32, nw, 1);     // G = 1: one part
+      check_kvplan_split(1, 32, 2, 50, 260, causal, 32, nw, 16);   // one head per part
+    }
   for (int causal = 0; causal < 2; ++causal)
     for (int tps : {1, 2, 3, 7, 100}) {
       check_split(2, 8, 2, 1, 1000, causal, 4, tps);    // decoding: one query, GQA 4

@@ -164,9 +164,22 @@ def call_bwd(lib, **kw):
 def test_bwd_workspace_size(lib):
     f = lib.fa_bwd_workspace_size
     f.restype = ctypes.c_size_t
-    # one (LSE log2 e, D) pair of floats per query row
-    assert f(1, 4, 2, 100, 300, 128, 1) == 4 * 100 * 8
-    assert f(2, 32, 8, 8192, 8192, 128, 1) == 2 * 32 * 8192 * 8
+
+    def pairs(B, Hq, Nq):  # one (LSE log2 e, D) pair of floats per query row, rounded up to 256 bytes
+        return -(-B * Hq * Nq * 8 // 256) * 256
+
+    # enough key blocks: the pairs only
+    assert f(2, 32, 8, 8192, 8192, 128, 1) == pairs(2, 32, 8192)
+    assert f(8, 16, 16, 1000, 1000, 64, 0) == pairs(8, 16, 1000)
+    # two key/value heads of 300 keys: the G = 2 query heads of a group are
+    # split, and the parts' fp32 dK and dV sums follow the pairs
+    extra = f(1, 4, 2, 100, 300, 128, 1) - pairs(1, 4, 100)
+    per_part = 2 * 1 * 2 * 300 * 128 * 4
+    assert extra > 0 and extra % per_part == 0 and 2 % (extra // per_part) == 0
+    # one key/value head and 16 query heads: some divisor of 16 parts
+    extra = f(1, 16, 1, 64, 512, 256, 0) - pairs(1, 16, 64)
+    per_part = 2 * 1 * 1 * 512 * 256 * 4
+    assert extra > 0 and extra % per_part == 0 and 16 % (extra // per_part) == 0
     assert f(1, 4, 3, 100, 300, 128, 1) == 0 and f(1, 4, 2, 100, 300, 96, 0) == 0 and f(1, 4, 2, 0, 300, 128, 0) == 0
     assert f(1, 4, 2, 100, 300, 128, 2) == 0
 

@@ -210,8 +210,9 @@ def test_backward_stages_equal_the_whole(api):
     torch.cuda.synchronize()
     for a, b in ((dq1, dq2), (dk1, dk2), (dv1, dv2)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    # the workspace holds (LSE log2 e, D) per row
-    pairs = ws.view(2, 8, 200, 2).cpu().numpy().astype(np.float64)
+    # the workspace starts with (LSE log2 e, D) per row (partial sums of the
+    # split heads, G = 4 here, follow them)
+    pairs = ws[: 2 * 8 * 200 * 2].view(2, 8, 200, 2).cpu().numpy().astype(np.float64)
     np.testing.assert_allclose(pairs[..., 0], lse.cpu().numpy() * math.log2(math.e), rtol=1e-6)
     d_ref = (do.float() * o.float()).sum(-1).cpu().numpy()
     np.testing.assert_allclose(pairs[..., 1], d_ref, rtol=1e-4, atol=1e-4)
@@ -246,3 +247,23 @@ def test_backward_large_grids_one_head_group(api, case):
     compare_grad(dq[b:b + 1, hs], rq, f"{w.name} dQ")
     compare_grad(dk[b:b + 1, hk:hk + 1], rk, f"{w.name} dK")
     compare_grad(dv[b:b + 1, hk:hk + 1], rv, f"{w.name} dV")
+
+
+# Few key/value heads (MQA and small-batch GQA): too few (group, key block)
+# pairs to fill the GPU, so the G query heads of every group are split into
+# parts whose fp32 partial sums of dK and dV are added by a second kernel.
+# Whole problems against the oracle.
+HEAD_SPLIT = [
+    # B, Hq, Hkv, Nq, Nk, d, causal
+    (1, 16, 1, 2048, 2048, 128, True),
+    (2, 8, 1, 1000, 1500, 64, False),
+    (1, 12, 2, 700, 900, 256, True),
+    (1, 6, 3, 500, 700, 128, False),
+]
+
+
+@pytest.mark.parametrize("case", HEAD_SPLIT, ids=lambda c: "x".join(map(str, c)))
+def test_backward_with_split_heads(api, case):
+    B, Hq, Hkv, Nq, Nk, d, causal = case
+    w = gen.workload(B, Hq, Hkv, Nq, Nk, d, causal=causal)
+    check(api, w, (28, sum(case[:6])))
