@@ -127,8 +127,10 @@ fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
   // chip once; fewer waves per workgroup would leave SIMDs idle
   const long long min_wg = d == 256 ? 256 : MIN_KV_WORKGROUPS;
   // at d = 128 never fewer than 2 waves: one-wave workgroups leave most of a
-  // CU idle (B1 H8 N2048 d128: 132 us against 69 us with two waves)
-  const int min_nw = d == 128 ? 2 : 1;
+  // CU idle (B1 H8 N2048 d128: 132 us against 69 us with two waves); with
+  // G > 1 never fewer than 4, splitting the heads instead (B1 H32 Hkv8 N4096
+  // causal: 2 waves 562 us, 8 waves and 4 head parts 362 us)
+  const int min_nw = d == 128 ? (Hq / Hkv > 1 ? 4 : 2) : 1;
   for (int nw = fa::bwd_dkdv_max_waves(d); nw > min_nw; nw >>= 1) {
     const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
     if (p.nwg >= min_wg) return p;
