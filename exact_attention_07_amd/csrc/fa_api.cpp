@@ -109,8 +109,8 @@ size_t splitkv_workspace_bytes(const fa_plan_t& p, int d) {
 
 // Backward plans.  dQ: the forward kernel's plan (32 query rows per wave).
 // dK/dV: key blocks of up to bwd_dkdv_max_waves waves (a workgroup of that
-// size fills a CU on its own), fewer while the grid would have under
-// MIN_KV_WORKGROUPS workgroups.
+// size fills a CU on its own), and enough workgroups through fewer waves or
+// split head groups (plan_bwd_dkdv).
 constexpr long long MIN_KV_WORKGROUPS = 512;
 
 // The dQ kernel has the forward kernel's shape, K/V ring and occupancy, and
@@ -123,28 +123,46 @@ fa_plan_t plan_bwd_dq(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal)
 
 fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal) {
   const int kpw = fa::bwd_keys_per_wave(d);
-  // at d = 256 one workgroup fills a CU's LDS, so 256 workgroups fill the
-  // chip once; fewer waves per workgroup would leave SIMDs idle
-  const long long min_wg = d == 256 ? 256 : MIN_KV_WORKGROUPS;
-  // at d = 128 never fewer than 2 waves: one-wave workgroups leave most of a
-  // CU idle (B1 H8 N2048 d128: 132 us against 69 us with two waves); with
-  // G > 1 never fewer than 4, splitting the heads instead (B1 H32 Hkv8 N4096
-  // causal: 2 waves 562 us, 8 waves and 4 head parts 362 us)
-  const int min_nw = d == 128 ? (Hq / Hkv > 1 ? 4 : 2) : 1;
-  for (int nw = fa::bwd_dkdv_max_waves(d); nw > min_nw; nw >>= 1) {
+  const int G = Hq / Hkv, max_nw = fa::bwd_dkdv_max_waves(d);
+  // the fewest head parts (a divisor of G) that give at least `target`
+  // workgroups: each part adds its heads' share of dK and dV into an fp32
+  // partial sum in the workspace
+  auto split_to = [&](const fa_kvplan_t& p, long long target) {
+    if (p.nwg >= target || G == 1) return p;
+    for (int parts = 2; parts < G; ++parts)
+      if (G % parts == 0 && p.nwg * parts >= target) return fa_split_kvplan_heads(p, parts);
+    return fa_split_kvplan_heads(p, G);
+  };
+  const fa_kvplan_t big = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, max_nw);
+  // d = 256: one workgroup fills a CU's LDS whatever its wave count.  With
+  // G > 1 the most waves, heads split up to 256 workgroups, 512 if causal
+  // (B2 H16 Hkv1 N4096 causal: 4377 us at one wave per workgroup, 746 us with
+  // 4 waves and 8 parts); with G = 1 fewer waves while under 256 workgroups
+  // (B1 H8 N2048: 2 waves 3 % faster than 4).
+  if (d == 256) {
+    if (G > 1) return split_to(big, causal ? 512 : 256);
+    for (int nw = max_nw; nw > 1; nw >>= 1) {
+      const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
+      if (p.nwg >= 256) return p;
+    }
+    return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, 1);
+  }
+  // d = 64 with G > 1: the most waves, heads split up to 512 workgroups (1024
+  // if causal, whose key blocks differ in work: more parts balance them)
+  if (d == 64 && G > 1) return split_to(big, causal ? 1024 : 512);
+  // d = 128, and d = 64 with G = 1: fewer waves while under 512 workgroups,
+  // but at d = 128 never fewer than 2 (one-wave workgroups leave most of a
+  // CU idle: B1 H8 N2048: 132 us against 69 us with two) and with G > 1 never
+  // fewer than 4, splitting the heads at the most waves instead (B1 H32 Hkv8
+  // N4096 causal: 2 waves 562 us, 8 waves and 4 parts 362 us)
+  const int min_nw = d == 128 ? (G > 1 ? 4 : 2) : 1;
+  for (int nw = max_nw; nw > min_nw; nw >>= 1) {
     const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
-    if (p.nwg >= min_wg) return p;
+    if (p.nwg >= MIN_KV_WORKGROUPS) return p;
   }
   const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, min_nw);
-  if (p.nwg >= min_wg || p.G == 1) return p;
-  // Too few (group, key block) pairs even with the smallest workgroups: a
-  // group's query heads are split into parts (the fewest that reach min_wg
-  // workgroups; a divisor of G) at the largest workgroups, each part adding
-  // its heads' share of dK and dV into an fp32 partial sum in the workspace.
-  const fa_kvplan_t big = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, fa::bwd_dkdv_max_waves(d));
-  for (int parts = 2; parts < p.G; ++parts)
-    if (p.G % parts == 0 && big.nwg * parts >= min_wg) return fa_split_kvplan_heads(big, parts);
-  return fa_split_kvplan_heads(big, p.G);
+  if (p.nwg >= MIN_KV_WORKGROUPS || G == 1) return p;
+  return split_to(big, MIN_KV_WORKGROUPS);
 }
 
 // Workspace of the backward pass: the (L2, D) pair of every query row,
