@@ -57,20 +57,22 @@ fa_status forward(const void* q, const void* k, const void* v, void* o, float* l
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-// bf16 with few query rows: the G query heads of a GQA group share one
-// wave's 32 query columns (plan.h, fa_make_packed_plan).
-bool packable(int Hq, int Hkv, int Nq) { return Hq / Hkv > 1 && (long long)(Hq / Hkv) * Nq <= 32; }
+// bf16 with few query rows: the G query heads of a GQA group share the 32
+// query columns of one wave, or of a few (plan.h, fa_make_packed_plan).
+bool packable(int Hq, int Hkv, int Nq, int d) {
+  return Hq / Hkv > 1 && Nq <= 16 && fa_packed_waves(Hq / Hkv, Nq) <= (d == 128 ? 8 : 4);
+}
 
 fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int kind) {
-  if (kind == KIND_BF16 && packable(Hq, Hkv, Nq)) return fa_make_packed_plan(B, Hq, Hkv, Nq, Nk, causal);
+  if (kind == KIND_BF16 && packable(Hq, Hkv, Nq, d)) return fa_make_packed_plan(B, Hq, Hkv, Nq, Nk, causal);
   const int qpw = fa::queries_per_wave(d, kind == KIND_F32);
   if (kind == KIND_F32) return fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, qpw, 4);
   return fa_forward_plan(B, Hq, Hkv, Nq, Nk, causal, d, kind == KIND_FP8, qpw);
 }
 
 // Key-split plan of the bf16 path.  Few query rows: one workgroup holds all
-// query heads of a GQA group, packed into one wave's query columns when
-// G * Nq <= 32, else one head per wave (up to the wave limit), so each K/V
+// query heads of a GQA group, packed into the query columns of its waves
+// when Nq <= 16, else one head per wave (up to the wave limit), so each K/V
 // tile is read once for all of them.  Then the keys are split into ranges
 // until the grid has MIN_WORKGROUPS workgroups (nsplit_req = 0), or into
 // nsplit_req ranges of equal tile counts (the last may be shorter; fewer
@@ -78,7 +80,7 @@ fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, in
 fa_plan_t plan_splitkv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int nsplit_req) {
   const int qpw = fa::queries_per_wave(d, 0);
   fa_plan_t base;
-  if (packable(Hq, Hkv, Nq)) {
+  if (packable(Hq, Hkv, Nq, d)) {
     base = fa_make_packed_plan(B, Hq, Hkv, Nq, Nk, causal);
   } else if (Nq <= qpw) {
     const int max_nw = d == 128 ? 8 : 4;
@@ -90,9 +92,9 @@ fa_plan_t plan_splitkv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal
   }
   const long long tiles = ((long long)Nk + 63) / 64;
   long long want = nsplit_req;
-  // packed plans: single-wave workgroups, two per CU (LDS), so 512 fill the
-  // chip once; more only queue behind them (measured on decoding, B8 Hq32
-  // Hkv8 Nk32K d128: 8 ranges 0.197 ms, 16 ranges 0.214 ms)
+  // packed plans: two workgroups per CU (LDS), so 512 fill the chip once;
+  // more only queue behind them (measured on decoding, B8 Hq32 Hkv8 Nk32K
+  // d128: 8 ranges 0.197 ms, 16 ranges 0.214 ms)
   const long long target = base.pack > 1 ? 512 : MIN_WORKGROUPS;
   if (want == 0) want = base.nwg >= target ? 1 : (target + base.nwg - 1) / base.nwg;
   if (want > tiles) want = tiles;

@@ -373,16 +373,16 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 
   const size_t kvoff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
   // the lane's query column: head hq_l, row q_l (valid_l: a real query).
-  // Packed plans hold row c % Nq of head hq0 + c / Nq in column c; the wave
-  // then covers rows 0 .. Nq - 1 of every head, so the wave-level limits
-  // above hold unchanged.
+  // Packed plans hold, in column c of wave v, row c % Nq of head
+  // hq0 + v * pack + c / Nq; every wave then covers rows 0 .. Nq - 1 of its
+  // heads, so the wave-level limits above hold unchanged.
   const int col = lane & 31;
   int hq_l = hq, q_l = q0w + col;
   bool valid_l = q_l < Nq;
   if (p.pack > 1) {
-    const int hh = col / Nq;
-    valid_l = hh < p.pack;
-    hq_l = w.hq0 + (valid_l ? hh : 0);
+    const int hh = col / Nq, head = wave * p.pack + hh;
+    valid_l = hh < p.pack && head < p.G;
+    hq_l = w.hq0 + (valid_l ? head : 0);
     q_l = valid_l ? col - hh * Nq : 0;
   }
   const size_t qrow0 = (size_t)(w.b * p.Hq + hq_l) * Nq;  // first row of the lane's head

@@ -82,15 +82,26 @@ FA_HD inline fa_plan_t fa_make_plan(int B, int Hq, int Hkv, int Nq, int Nk, int 
   return p;
 }
 
-// One single-wave workgroup per GQA group, its G heads packed into the
-// wave's query columns; requires G * Nq <= 32.
+// Waves of a packed workgroup: the fewest (a power of two) whose query
+// columns hold all G heads' Nq rows, ceil(G / waves) heads per wave.
+FA_HD inline int fa_packed_waves(int G, int Nq) {
+  int nw = 1;
+  while ((long long)((G + nw - 1) / nw) * Nq > 32) nw *= 2;
+  return nw;
+}
+
+// One workgroup per GQA group, its G heads packed into the query columns of
+// its waves: wave v holds heads v * pack .. v * pack + pack - 1 (those below
+// G), column c of a wave row c % Nq of its head c / Nq.  Requires Nq <= 16
+// (at least two heads per wave); one wave when G * Nq <= 32.
 FA_HD inline fa_plan_t fa_make_packed_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal) {
-  fa_plan_t p = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, 32, 1);
+  const int G = Hq / Hkv, nw = fa_packed_waves(G, Nq);
+  fa_plan_t p = fa_make_plan(B, Hq, Hkv, Nq, Nk, causal, 32, nw);
   p.hw = p.G;
   p.pos = Nq;
   p.nqb = 1;
   p.nhg = 1;
-  p.pack = p.G;
+  p.pack = (G + nw - 1) / nw;
   p.nwg = (long long)B * Hkv;
   p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
   return p;

@@ -141,11 +141,15 @@ static void check_kvplan_split(int B, int Hq, int Hkv, int Nq, int Nk, int causa
 }
 
 // Packed plans: every (b, query head, query row) is the column of exactly
-// one (workgroup, lane column), all heads of a workgroup read its kv head.
+// one (workgroup, wave, lane column), all heads of a workgroup read its kv
+// head.
 static void check_packed(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int tps) {
   fa_plan_t p = fa_make_packed_plan(B, Hq, Hkv, Nq, Nk, causal);
   if (tps > 0) p = fa_split_plan(p, tps, 64);
-  CHECK(p.G * Nq <= 32 && p.pack == p.G && p.nw == 1 && p.nqb == 1 && p.nhg == 1);
+  CHECK(p.pack * Nq <= 32 && p.pack * p.nw >= p.G && (p.nw & (p.nw - 1)) == 0 && p.nqb == 1 && p.nhg == 1);
+  // the fewest waves: half as many would need more than 32 columns per wave
+  if (p.nw > 1) CHECK((p.G + p.nw / 2 - 1) / (p.nw / 2) * Nq > 32);
+  if (p.G * Nq <= 32) CHECK(p.nw == 1 && p.pack == p.G);
   const int tiles = (Nk + 63) / 64;
   std::vector<int> cover((size_t)B * Hq * Nq * tiles, 0);
   for (long long id = 0; id < p.nwg; ++id) {
@@ -153,10 +157,11 @@ static void check_packed(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int
     CHECK(w.qpos0 == 0 && w.hq0 == w.hkv * p.G);
     int nt = fa_num_kv_tiles(p, w.qpos0, 64), t0, t1;
     fa_split_tiles(p, w.split, nt, t0, t1);
+    for (int wave = 0; wave < p.nw; ++wave)
     for (int col = 0; col < 32; ++col) {
-      const int hh = col / Nq;
-      if (hh >= p.pack) continue;  // an idle column
-      const int hq = w.hq0 + hh, i = col - hh * Nq;
+      const int hh = col / Nq, head = wave * p.pack + hh;
+      if (hh >= p.pack || head >= p.G) continue;  // an idle column
+      const int hq = w.hq0 + head, i = col - hh * Nq;
       CHECK(hq / p.G == w.hkv && i < Nq);
       int klast = causal ? (i + Nk - Nq < Nk - 1 ? i + Nk - Nq : Nk - 1) : Nk - 1;
       for (int t = t0; t < t1; ++t)
@@ -222,6 +227,10 @@ int main() {
       check_packed(3, 6, 2, 10, 200, causal, tps);     // 3 heads x 10 rows
       check_packed(1, 4, 2, 16, 70, causal, tps);      // 2 heads x 16 rows: all 32 columns
       check_packed(1, 8, 2, 7, 5, causal, tps);        // Nq > Nk: rows without keys
+      check_packed(2, 64, 8, 8, 700, causal, tps);     // 8 heads x 8 rows: 2 waves
+      check_packed(1, 24, 2, 10, 300, causal, tps);    // G = 12, 10 rows: 4 waves of 3 heads
+      check_packed(1, 16, 1, 16, 129, causal, tps);    // G = 16, 16 rows: 8 waves of 2 heads
+      check_packed(3, 12, 2, 5, 200, causal, tps);     // G = 6, 5 rows: 1 wave
     }
   for (int causal = 0; causal < 2; ++causal)
     for (int nw : {1, 2, 4})

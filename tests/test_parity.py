@@ -91,6 +91,9 @@ SHAPES = [
     (3, 6, 2, 10, 100),      # 3 heads x 10 rows
     (1, 4, 2, 16, 70),       # 2 heads x 16 rows: every column
     (1, 8, 2, 7, 5),         # Nq > Nk: causal rows with no visible key
+    # more heads than one wave's columns hold: packed over several waves
+    (2, 32, 4, 8, 200),      # 8 heads x 8 rows: two waves
+    (1, 24, 2, 10, 150),     # 12 heads x 10 rows: four waves of 3 heads
 ]
 
 

@@ -53,6 +53,10 @@ CASES = [
     (1, 32, 1, 1, 3000, 128),    # 32 query heads packed into one wave
     (3, 6, 2, 10, 2000, 64),     # 3 heads x 10 rows packed
     (1, 4, 2, 16, 700, 256),     # 2 heads x 16 rows: every column
+    (2, 64, 8, 8, 1500, 128),    # 8 heads x 8 rows: two waves of 4 heads
+    (1, 24, 2, 10, 900, 64),     # 12 heads x 10 rows: four waves of 3 heads
+    (1, 16, 1, 16, 700, 128),    # 16 heads x 16 rows: eight waves of 2 heads
+    (1, 8, 1, 12, 500, 256),     # 8 heads x 12 rows: four waves of 2 heads
 ]
 
 
