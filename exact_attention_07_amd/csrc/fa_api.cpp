@@ -152,19 +152,20 @@ fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
   // d = 64 with G > 1: the most waves, heads split up to 512 workgroups (1024
   // if causal, whose key blocks differ in work: more parts balance them)
   if (d == 64 && G > 1) return split_to(big, causal ? 1024 : 512);
-  // d = 128, and d = 64 with G = 1: fewer waves while under 512 workgroups,
-  // but at d = 128 never fewer than 2 (one-wave workgroups leave most of a
-  // CU idle: B1 H8 N2048: 132 us against 69 us with two) and with G > 1 never
-  // fewer than 4, splitting the heads at the most waves instead (B1 H32 Hkv8
-  // N4096 causal: 2 waves 562 us, 8 waves and 4 parts 362 us)
-  const int min_nw = d == 128 ? (G > 1 ? 4 : 2) : 1;
+  // d = 128 with G > 1: 8 waves (256 such workgroups already hold 8 waves
+  // on every CU), heads split up to 256 workgroups, 512 if causal (B1 H32
+  // Hkv4 N16384 causal: 4 waves 6836 us, 8 waves and 2 parts 3998 us; B2 H32
+  // Hkv8 N4096: 4 waves 1141 us, 8 waves 948 us)
+  if (d == 128 && G > 1) return split_to(big, causal ? 512 : 256);
+  // d = 128 with G = 1, and d = 64 with G = 1: fewer waves while under 512
+  // workgroups, but at d = 128 never fewer than 2 (one-wave workgroups leave
+  // most of a CU idle: B1 H8 N2048: 132 us against 69 us with two)
+  const int min_nw = d == 128 ? 2 : 1;
   for (int nw = max_nw; nw > min_nw; nw >>= 1) {
     const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, nw);
     if (p.nwg >= MIN_KV_WORKGROUPS) return p;
   }
-  const fa_kvplan_t p = fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, min_nw);
-  if (p.nwg >= MIN_KV_WORKGROUPS || G == 1) return p;
-  return split_to(big, MIN_KV_WORKGROUPS);
+  return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, min_nw);
 }
 
 // Workspace of the backward pass: the (L2, D) pair of every query row,
