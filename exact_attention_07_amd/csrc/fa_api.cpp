@@ -149,9 +149,16 @@ fa_kvplan_t plan_bwd_dkdv(int B, int Hq, int Hkv, int Nq, int Nk, int d, int cau
     }
     return fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, 1);
   }
-  // d = 64 with G > 1: the most waves, heads split up to 512 workgroups (1024
-  // if causal, whose key blocks differ in work: more parts balance them)
-  if (d == 64 && G > 1) return split_to(big, causal ? 1024 : 512);
+  // d = 64 with G > 1.  Causal with Nq >= Nk / 2, where the key blocks'
+  // work differs most: 2-wave workgroups, heads split up to 2048 workgroups
+  // (B2 H32 Hkv8 N4096: 404 us against 546 us at 4 waves unsplit).
+  // Otherwise every key block sees about the same rows: 4 waves, heads split
+  // only up to 256 workgroups (B2 H32 Hkv8 Nq1024 Nk8192 causal: unsplit
+  // 299 us, 2 parts 337 us).
+  if (d == 64 && G > 1) {
+    if (causal && 2LL * Nq >= Nk) return split_to(fa_make_kvplan(B, Hq, Hkv, Nq, Nk, causal, kpw, 2), 2048);
+    return split_to(big, 256);
+  }
   // d = 128 with G > 1: 8 waves (256 such workgroups already hold 8 waves
   // on every CU), heads split up to 256 workgroups, 512 if causal (B1 H32
   // Hkv4 N16384 causal: 4 waves 6836 us, 8 waves and 2 parts 3998 us; B2 H32
