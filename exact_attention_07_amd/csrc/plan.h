@@ -19,7 +19,11 @@
 //   * the hardware hands workgroup ids round-robin to the 8 XCDs of an
 //     MI355X, each with its own L2.  When the count divides by 8 the id is
 //     remapped so that XCD x runs the x-th contiguous eighth of that order,
-//     which keeps the workgroups that read one K/V head on one L2;
+//     which keeps the workgroups that read one K/V head on one L2.  Causal
+//     work falls along a group's query blocks, so an eighth that holds part
+//     of a group would get only its heavy or only its light blocks: then the
+//     k XCDs (k = 2, 4 or 8) whose k eighths hold whole groups take the
+//     blocks of those groups in turn (fa_xcd_ways);
 //   * optionally the keys are split into `nsplit` ranges of `tps` tiles
 //     (for grids too small to fill the chip, e.g. decoding with few query
 //     rows): each workgroup then covers one range and writes a partial
@@ -50,12 +54,37 @@ struct fa_plan_t {
   int pos;    // query positions per workgroup
   int nqb;    // query blocks per head: ceil(Nq / pos)
   int nhg;    // head subsets per GQA group: G / hw
-  int xcd;    // 1 if workgroup ids are remapped XCD-contiguously
+  int xcd;    // XCD remap of the workgroup ids (fa_xcd_ways; 0: none)
   int nsplit; // key ranges (1: no split)
   int tps;    // key tiles per range (nsplit > 1)
   int pack;   // query heads sharing one wave's columns (1: one head per wave)
   long long nwg;  // workgroups in the grid
 };
+
+// XCD remap of a grid of nwg workgroups whose logical order is made of runs
+// of `run` workgroups (one group's query or key blocks), heaviest first
+// within a run when `uneven` (causal).  0: no remap (nwg is not a multiple
+// of 8); 1: XCD x runs the x-th contiguous eighth of the order; k = 2, 4, 8:
+// the order is cut into 8 / k pieces of k eighths, the smallest such pieces
+// that hold whole runs, and the k XCDs of a piece take its workgroups in
+// turn, in a snake (XCD 0 .. k-1, then k-1 .. 0), so that over a run that
+// gets lighter block by block none of them always draws the heaviest.
+FA_HD inline int fa_xcd_ways(long long nwg, long long run, int uneven) {
+  if (nwg % 8 != 0) return 0;
+  if (!uneven) return 1;
+  const long long c = nwg / 8;
+  for (int k = 1; k < 8; k *= 2)
+    if ((k * c) % run == 0) return k;
+  return 8;
+}
+
+// Position in the logical order of workgroup id under XCD remap `ways`: the
+// id's XCD x = id % 8 runs its (id / 8)-th workgroup.
+FA_HD inline long long fa_xcd_order(long long id, long long nwg, int ways) {
+  if (ways == 0) return id;
+  const long long c = nwg / 8, x = id % 8, u = id / 8, r = x % ways;
+  return (x / ways) * ways * c + u * ways + ((u & 1) ? ways - 1 - r : r);
+}
 
 // Largest of {nw, nw/2, ..., 1} that divides g (nw is a power of two).
 FA_HD inline int fa_heads_per_wg(int g, int nw) {
@@ -78,7 +107,7 @@ FA_HD inline fa_plan_t fa_make_plan(int B, int Hq, int Hkv, int Nq, int Nk, int 
   p.tps = 0;
   p.pack = 1;
   p.nwg = (long long)B * Hkv * p.nhg * p.nqb;
-  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  p.xcd = fa_xcd_ways(p.nwg, p.nqb, causal);
   return p;
 }
 
@@ -103,7 +132,7 @@ FA_HD inline fa_plan_t fa_make_packed_plan(int B, int Hq, int Hkv, int Nq, int N
   p.nhg = 1;
   p.pack = (G + nw - 1) / nw;
   p.nwg = (long long)B * Hkv;
-  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  p.xcd = fa_xcd_ways(p.nwg, 1, causal);
   return p;
 }
 
@@ -116,7 +145,7 @@ FA_HD inline fa_plan_t fa_split_plan(fa_plan_t p, int tps, int bc) {
   p.tps = tps;
   p.nsplit = (tiles + tps - 1) / tps;
   p.nwg = (long long)p.B * p.Hkv * p.nhg * p.nqb * p.nsplit;
-  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  p.xcd = fa_xcd_ways(p.nwg, (long long)p.nqb * p.nsplit, p.causal);
   return p;
 }
 
@@ -165,7 +194,7 @@ struct fa_work_t {
 // Workgroup hardware id -> its work.  A bijection of [0, nwg) onto the
 // (group, query block) pairs.
 FA_HD inline fa_work_t fa_decode(const fa_plan_t& p, long long id) {
-  long long L = p.xcd ? (id % 8) * (p.nwg / 8) + id / 8 : id;
+  long long L = fa_xcd_order(id, p.nwg, p.xcd);
   fa_work_t w;
   w.split = (int)(L % p.nsplit);
   L /= p.nsplit;
@@ -219,7 +248,9 @@ FA_HD inline void fa_split_tiles(const fa_plan_t& p, int split, int nt, int& t0,
 // group-major (group = batch, kv head) with the key blocks of a group
 // consecutive, first key block first: with causal masking the first keys
 // are seen by the most query rows, so the heaviest workgroups start first.
-// The same XCD remap as above keeps the workgroups of one head on one L2.
+// The same XCD remap as above keeps the workgroups of one head on one L2
+// (with causal masking, key blocks are runs that get heavier towards the
+// start).
 struct fa_kvplan_t {
   int B, Hq, Hkv, Nq, Nk;
   int causal;
@@ -245,7 +276,7 @@ FA_HD inline fa_kvplan_t fa_make_kvplan(int B, int Hq, int Hkv, int Nq, int Nk, 
   p.hsplit = 1;
   p.hps = p.G;
   p.nwg = (long long)B * Hkv * p.nkb;
-  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  p.xcd = fa_xcd_ways(p.nwg, p.nkb, causal);
   return p;
 }
 
@@ -256,7 +287,7 @@ FA_HD inline fa_kvplan_t fa_split_kvplan_heads(fa_kvplan_t p, int parts) {
   p.hsplit = parts;
   p.hps = p.G / parts;
   p.nwg = (long long)p.B * p.Hkv * p.nkb * parts;
-  p.xcd = (p.nwg % 8 == 0) ? 1 : 0;
+  p.xcd = fa_xcd_ways(p.nwg, p.nkb, p.causal);
   return p;
 }
 
@@ -270,7 +301,7 @@ struct fa_kvwork_t {
 // innermost, so that the workgroups of one (group, head part), which read
 // the same query tiles, run on one XCD.
 FA_HD inline fa_kvwork_t fa_kv_decode(const fa_kvplan_t& p, long long id) {
-  const long long L = p.xcd ? (id % 8) * (p.nwg / 8) + id / 8 : id;
+  const long long L = fa_xcd_order(id, p.nwg, p.xcd);
   fa_kvwork_t w;
   const long long gs = L / p.nkb;
   w.k0 = (int)(L % p.nkb) * p.kpb;

@@ -44,8 +44,9 @@ static void check_plan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int q
   }
   CHECK((long long)seen.size() == p.nwg);
   for (int c : cover) CHECK(c == 1);
-  // without the XCD remap, causal workgroups of one group come heaviest first
-  if (causal && !p.xcd && p.nqb > 1) {
+  // where the first two ids are the first two of the logical order, causal
+  // workgroups of one group come heaviest first
+  if (causal && (p.xcd == 0 || p.xcd == 8) && p.nqb > 1) {
     fa_work_t a = fa_decode(p, 0), b = fa_decode(p, 1);
     CHECK(a.qpos0 > b.qpos0);
   }
@@ -85,10 +86,47 @@ static void check_split(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int 
           CHECK(cover[(((size_t)b * Hq + h) * Nq + i) * tiles + t] == (klast >= 0 && t * 64 <= klast ? 1 : 0));
       }
   // the ranges of one query block are consecutive in the logical order
-  if (!p.xcd && p.nsplit > 1) {
+  if ((p.xcd == 0 || p.xcd == 8) && p.nsplit > 1) {
     fa_work_t a = fa_decode(p, 0), b = fa_decode(p, 1);
     CHECK(a.split == 0 && b.split == 1 && a.qpos0 == b.qpos0 && a.hq0 == b.hq0);
   }
+}
+
+// XCD remap of causal grids: the k XCDs that share a piece of the order hold
+// whole runs (query or key blocks of one group) and the busiest XCD gets at
+// most `slack` times the average work (key tiles, or query tiles for the
+// backward's key blocks).
+static void check_xcd_ways(long long nwg, long long run, int ways) {
+  CHECK(ways == fa_xcd_ways(nwg, run, 1));
+  if (ways == 0) return;
+  CHECK(nwg % 8 == 0 && (ways == 8 || (ways * (nwg / 8)) % run == 0));
+  for (int k = 1; k < ways; k *= 2) CHECK((k * (nwg / 8)) % run != 0);  // the smallest such pieces
+  std::set<long long> seen;
+  for (long long id = 0; id < nwg; ++id) CHECK(seen.insert(fa_xcd_order(id, nwg, ways)).second);
+  CHECK(*seen.begin() == 0 && *seen.rbegin() == nwg - 1);
+}
+static void check_balance(const fa_plan_t& p, double slack) {
+  CHECK(p.causal && p.xcd > 0);
+  check_xcd_ways(p.nwg, (long long)p.nqb * p.nsplit, p.xcd);
+  double load[8] = {0}, total = 0;
+  for (long long id = 0; id < p.nwg; ++id) {
+    const double t = fa_num_kv_tiles(p, fa_decode(p, id).qpos0, 64);
+    load[id % 8] += t;
+    total += t;
+  }
+  for (double l : load) CHECK(l <= slack * total / 8);
+}
+static void check_kv_balance(const fa_kvplan_t& p, double slack) {
+  CHECK(p.causal && p.xcd > 0);
+  check_xcd_ways(p.nwg, p.nkb, p.xcd);
+  double load[8] = {0}, total = 0;
+  for (long long id = 0; id < p.nwg; ++id) {
+    int first, ntq;
+    fa_kv_query_tiles(p, fa_kv_decode(p, id).k0, 64, first, ntq);
+    load[id % 8] += ntq - first;
+    total += ntq - first;
+  }
+  for (double l : load) CHECK(l <= slack * total / 8);
 }
 
 // Backward key-block plans: every (b, kv head, key) is owned by exactly one
@@ -115,7 +153,7 @@ static void check_kvplan(int B, int Hq, int Hkv, int Nq, int Nk, int causal, int
   }
   CHECK((long long)seen.size() == p.nwg);
   for (int c : cover) CHECK(c == 1);
-  if (!p.xcd && p.nkb > 1) CHECK(fa_kv_decode(p, 0).k0 == 0 && fa_kv_decode(p, 1).k0 == p.kpb);
+  if ((p.xcd == 0 || p.xcd == 8) && p.nkb > 1) CHECK(fa_kv_decode(p, 0).k0 == 0 && fa_kv_decode(p, 1).k0 == p.kpb);
 }
 
 // Key plans whose groups' query heads are split into parts: every
@@ -282,6 +320,35 @@ int main() {
   }
   // the first ids of an XCD get the heaviest (last) query block
   CHECK(fa_decode(p, 0).qpos0 == 8192 - 64 && fa_decode(p, 8).qpos0 == 8192 - 128);
+  // causal grids whose groups span several XCDs: the blocks of a group
+  // alternate over them (k = 2, 4, 8), each XCD within 1 % of the average
+  // work (one eighth holding part of a group had up to 1.9x)
+  for (int causal = 0; causal < 2; ++causal) {
+    check_plan(1, 16, 4, 32768, 32768, causal, 32, 8);   // 4 groups of 512 blocks: k = 2
+    check_plan(1, 2, 2, 8192, 8192, causal, 32, 8);      // 2 groups of 32 blocks: k = 4
+    check_plan(1, 8, 1, 32768, 32768, causal, 32, 8);    // MQA, one group of 1024 blocks: k = 8
+    check_plan(1, 12, 12, 8192, 8192, causal, 32, 8);    // 12 groups of 32 blocks: k = 2
+    check_kvplan(1, 4, 1, 32768, 32768, causal, 32, 4);  // one key group: k = 8
+    check_kvplan(1, 6, 2, 8192, 8192, causal, 64, 4);    // 2 groups of 32 key blocks: k = 4
+  }
+  CHECK(fa_make_plan(1, 16, 4, 32768, 32768, 1, 32, 8).xcd == 2);
+  CHECK(fa_make_plan(1, 2, 2, 8192, 8192, 1, 32, 8).xcd == 4);
+  CHECK(fa_make_plan(1, 8, 1, 32768, 32768, 1, 32, 8).xcd == 8);
+  CHECK(fa_make_plan(1, 16, 4, 32768, 32768, 0, 32, 8).xcd == 1);   // even work: contiguous eighths
+  CHECK(fa_make_plan(2, 32, 8, 8192, 8192, 1, 32, 8).xcd == 1);     // 2 whole groups per XCD
+  check_balance(fa_make_plan(1, 16, 4, 32768, 32768, 1, 32, 8), 1.01);
+  check_balance(fa_make_plan(1, 8, 1, 32768, 32768, 1, 32, 8), 1.01);
+  check_balance(fa_make_plan(1, 12, 12, 8192, 8192, 1, 32, 8), 1.01);
+  check_balance(fa_make_plan(1, 2, 2, 8192, 8192, 1, 32, 8), 1.01);
+  check_balance(fa_make_plan(2, 32, 8, 8192, 8192, 1, 32, 8), 1.01);
+  check_balance(fa_split_plan(fa_make_plan(1, 4, 1, 2048, 2048, 1, 32, 4), 4, 64), 1.01);
+  check_kv_balance(fa_make_kvplan(1, 4, 1, 32768, 32768, 1, 32, 4), 1.01);
+  check_kv_balance(fa_make_kvplan(1, 6, 2, 8192, 8192, 1, 64, 4), 1.01);
+  check_kv_balance(fa_split_kvplan_heads(fa_make_kvplan(1, 8, 1, 16384, 16384, 1, 32, 4), 2), 1.01);
+  check_kv_balance(fa_make_kvplan(2, 32, 8, 8192, 8192, 1, 32, 4), 1.01);
+  for (long long nwg : {8LL, 24LL, 64LL, 3000LL, 8000LL})
+    for (long long run : {1LL, 2LL, 3LL, 5LL, 64LL, 1000LL})
+      check_xcd_ways(nwg, run, fa_xcd_ways(nwg, run, 1));
   // plan choice keeps >= 1024 workgroups when possible
   fa_plan_t c2 = fa_choose_plan(8, 12, 12, 1024, 1024, 1, 32, 1024, 8);
   CHECK(c2.nw == 2 && c2.nwg == 8 * 12 * 16);
