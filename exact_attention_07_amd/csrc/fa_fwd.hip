@@ -322,11 +322,14 @@ __device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int query, int
 // LDS ring (two slots each): iteration j reads K_{j+1} and V_{j-1} and
 // refills the slots of K_j and V_{j-2} with K_{j+2} and V_j; every copy has
 // one iteration to land before the barrier that publishes it.
+//
+// One work item (fa_decode of id) per call; a persistent workgroup calls it
+// once per item, with a barrier in between (the LDS ring is reused).
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
-void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                        __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c,
-                        float* __restrict__ OWS, float* __restrict__ LWS) {
+__device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                                              const __bf16* __restrict__ V, __bf16* __restrict__ O,
+                                              float* __restrict__ LSE, const fa_plan_t& p, float c,
+                                              float* __restrict__ OWS, float* __restrict__ LWS, unsigned id) {
   using C = Cfg<D, false>;
   constexpr int KB = C::KB, DS = C::DS, DB = C::DB, PS = C::PS, RSK = C::RSK, RSV = C::RSV;
   static_assert(C::QB == 1, "one 32-row query block per wave");
@@ -353,7 +356,7 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   auto vslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lv0_ : lv1_); };
   LDS_AS char* const spare = (LDS_AS char*)lsp_;
 
-  const fa_work_t w = fa_decode(p, blockIdx.x);
+  const fa_work_t w = fa_decode(p, id);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hq = w.hq0 + wave % p.hw;
   const int q0w = w.qpos0 + (wave / p.hw) * 32;
@@ -593,6 +596,29 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   if (LSE != nullptr && lane < 32) LSE[qrow0 + q_l] = lse_row;
 }
 
+// A grid of p.nwg workgroups runs one work item each.  The 8-wave d = 128
+// kernel, which holds a whole CU, also runs as a persistent grid of one
+// workgroup per CU (fa_persistent_item): each workgroup then takes its
+// items one after another, so a CU's next item starts without a new
+// workgroup's dispatch, and the snake order over the heaviest-first causal
+// work gives every workgroup an even share.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
+void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                        __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c,
+                        float* __restrict__ OWS, float* __restrict__ LWS) {
+  if constexpr (!(D == 128 && NW == 8)) {
+    fwd_bf16_item<D, CAUSAL, NW>(Q, K, V, O, LSE, p, c, OWS, LWS, blockIdx.x);
+  } else {
+    for (unsigned r = 0;; ++r) {
+      const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
+      if (id == ~0u) break;
+      if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
+      fwd_bf16_item<D, CAUSAL, NW>(Q, K, V, O, LSE, p, c, OWS, LWS, id);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 // Every variant is instantiated explicitly (implicit instantiation through
 // the launch expression alone does not always emit the host-side stub).
@@ -661,6 +687,23 @@ hipError_t launch_merge(const float* ows, const float* lws, void* o, float* lse,
 
 int queries_per_wave(int, int) { return 32; }
 
+// Workgroups of a bf16 forward launch: p.nwg, or, for the 8-wave d = 128
+// kernel (one workgroup per CU), a persistent grid of one workgroup per CU
+// of the current device (rounded down to a multiple of 8) when p.nwg is
+// larger.
+static unsigned fwd_grid(const fa_plan_t& p, int d) {
+  if (d != 128 || p.nw != 8) return (unsigned)p.nwg;
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (unsigned)p.nwg;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n >= 8 ? n / 8 * 8 : -1;
+  }
+  return (cus[dev] > 0 && p.nwg > cus[dev]) ? (unsigned)cus[dev] : (unsigned)p.nwg;
+}
+
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
                       float c, int f32, float* ows, float* lws, hipStream_t stream) {
 #define FA_CASE_F32(DD, CC)                                                                               \
@@ -671,7 +714,7 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
   }
 #define FA_CASE_BF16(DD, CC, NN)                                                                       \
   if (!f32 && d == DD && (p.causal != 0) == CC && p.nw == NN) {                                         \
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream,      \
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN>), dim3(fwd_grid(p, d)), dim3(64 * NN), 0, stream,      \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c, ows, lws); \
     return hipGetLastError();                                                                           \
   }

@@ -79,11 +79,14 @@ FA_HD inline int fa_xcd_ways(long long nwg, long long run, int uneven) {
 }
 
 // Position in the logical order of workgroup id under XCD remap `ways`: the
-// id's XCD x = id % 8 runs its (id / 8)-th workgroup.
+// id's XCD x = id % 8 runs its (id / 8)-th workgroup.  Grids hold at most
+// 2^31 - 1 workgroups (the launch checks refuse larger ones), so 32-bit
+// arithmetic holds every position (cheaper on the GPU than 64-bit division).
 FA_HD inline long long fa_xcd_order(long long id, long long nwg, int ways) {
   if (ways == 0) return id;
-  const long long c = nwg / 8, x = id % 8, u = id / 8, r = x % ways;
-  return (x / ways) * ways * c + u * ways + ((u & 1) ? ways - 1 - r : r);
+  const unsigned k = (unsigned)ways, c = (unsigned)(nwg / 8), i = (unsigned)id;
+  const unsigned x = i % 8, u = i / 8, r = x % k;
+  return (long long)((x / k) * k * c + u * k + ((u & 1) ? k - 1 - r : r));
 }
 
 // Largest of {nw, nw/2, ..., 1} that divides g (nw is a power of two).
@@ -194,20 +197,36 @@ struct fa_work_t {
 // Workgroup hardware id -> its work.  A bijection of [0, nwg) onto the
 // (group, query block) pairs.
 FA_HD inline fa_work_t fa_decode(const fa_plan_t& p, long long id) {
-  long long L = fa_xcd_order(id, p.nwg, p.xcd);
+  unsigned L = (unsigned)fa_xcd_order(id, p.nwg, p.xcd);  // < 2^31 (fa_xcd_order)
   fa_work_t w;
-  w.split = (int)(L % p.nsplit);
-  L /= p.nsplit;
-  long long g = L / p.nqb;
-  int qi = (int)(L % p.nqb);
+  w.split = (int)(L % (unsigned)p.nsplit);
+  L /= (unsigned)p.nsplit;
+  unsigned g = L / (unsigned)p.nqb;
+  int qi = (int)(L % (unsigned)p.nqb);
   if (p.causal) qi = p.nqb - 1 - qi;
-  int hg = (int)(g % p.nhg);
-  g /= p.nhg;
-  w.hkv = (int)(g % p.Hkv);
-  w.b = (int)(g / p.Hkv);
+  int hg = (int)(g % (unsigned)p.nhg);
+  g /= (unsigned)p.nhg;
+  w.hkv = (int)(g % (unsigned)p.Hkv);
+  w.b = (int)(g / (unsigned)p.Hkv);
   w.hq0 = w.hkv * p.G + hg * p.hw;
   w.qpos0 = qi * p.pos;
   return w;
+}
+
+// Persistent grids: G workgroups (a multiple of 8, fewer than nwg) that
+// each take several work items.  Workgroup g runs on XCD x = g % 8 and takes
+// the ids the hardware would have handed to that XCD (x, x + 8, x + 16, ...,
+// in that order), the U = G / 8 workgroups of the XCD sharing them in
+// rounds of U: in round r workgroup u = g / 8 takes the u-th id of the round,
+// or the (U-1-u)-th in odd rounds (a snake, so that over heaviest-first
+// causal work each gets an even share).  Returns the id of round r, or ~0u
+// past the last; a grid of nwg or more workgroups runs id = g (if g < nwg)
+// in round 0.
+FA_HD inline unsigned fa_persistent_item(unsigned G, long long nwg, unsigned g, unsigned r) {
+  if ((long long)G >= nwg) return (r == 0 && (long long)g < nwg) ? g : ~0u;
+  const unsigned x = g % 8, u = g / 8, U = G / 8;
+  const unsigned id = x + 8 * (r * U + ((r & 1) ? U - 1 - u : u));  // < 2^31 + 8 G while r is in range
+  return (long long)id < nwg ? id : ~0u;
 }
 
 // Number of key tiles of `bc` keys a workgroup starting at query position
@@ -301,14 +320,14 @@ struct fa_kvwork_t {
 // innermost, so that the workgroups of one (group, head part), which read
 // the same query tiles, run on one XCD.
 FA_HD inline fa_kvwork_t fa_kv_decode(const fa_kvplan_t& p, long long id) {
-  const long long L = fa_xcd_order(id, p.nwg, p.xcd);
+  const unsigned L = (unsigned)fa_xcd_order(id, p.nwg, p.xcd);  // < 2^31 (fa_xcd_order)
   fa_kvwork_t w;
-  const long long gs = L / p.nkb;
-  w.k0 = (int)(L % p.nkb) * p.kpb;
-  w.hs = (int)(gs % p.hsplit);
-  const long long g = gs / p.hsplit;
-  w.hkv = (int)(g % p.Hkv);
-  w.b = (int)(g / p.Hkv);
+  const unsigned gs = L / (unsigned)p.nkb;
+  w.k0 = (int)(L % (unsigned)p.nkb) * p.kpb;
+  w.hs = (int)(gs % (unsigned)p.hsplit);
+  const unsigned g = gs / (unsigned)p.hsplit;
+  w.hkv = (int)(g % (unsigned)p.Hkv);
+  w.b = (int)(g / (unsigned)p.Hkv);
   return w;
 }
 

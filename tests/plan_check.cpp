@@ -129,6 +129,35 @@ static void check_kv_balance(const fa_kvplan_t& p, double slack) {
   for (double l : load) CHECK(l <= slack * total / 8);
 }
 
+// Persistent grids of G workgroups: every work item is taken exactly once,
+// by a workgroup on the XCD the hardware would have sent it to (id % 8), the
+// rounds end for good once they run out, and with `slack` > 0 the busiest
+// workgroup gets at most slack times the average key tiles.
+static void check_persistent(const fa_plan_t& p, unsigned G, double slack) {
+  std::vector<int> seen((size_t)p.nwg, 0);
+  std::vector<double> load(G, 0.0);
+  double total = 0;
+  for (unsigned g = 0; g < G; ++g) {
+    unsigned r = 0, last = 0;
+    for (;; ++r) {
+      const unsigned id = fa_persistent_item(G, p.nwg, g, r);
+      if (id == ~0u) break;
+      CHECK((long long)id < p.nwg && id % 8 == g % 8);
+      CHECK(r == 0 || id > last);  // an XCD's ids in the hardware's order
+      last = id;
+      seen[id]++;
+      const double t = fa_num_kv_tiles(p, fa_decode(p, id).qpos0, 64);
+      load[g] += t;
+      total += t;
+    }
+    for (unsigned k = 1; k < 4; ++k) CHECK(fa_persistent_item(G, p.nwg, g, r + k) == ~0u);
+    if ((long long)G >= p.nwg) CHECK(r == ((long long)g < p.nwg ? 1u : 0u));
+  }
+  for (int v : seen) CHECK(v == 1);
+  if (slack > 0)
+    for (double l : load) CHECK(l <= slack * total / G);
+}
+
 // Backward key-block plans: every (b, kv head, key) is owned by exactly one
 // wave, and every query row that sees one of a workgroup's keys lies in the
 // query tiles the workgroup visits.
@@ -349,6 +378,34 @@ int main() {
   for (long long nwg : {8LL, 24LL, 64LL, 3000LL, 8000LL})
     for (long long run : {1LL, 2LL, 3LL, 5LL, 64LL, 1000LL})
       check_xcd_ways(nwg, run, fa_xcd_ways(nwg, run, 1));
+  // persistent grids of the 8-wave forward kernel (one workgroup per CU)
+  for (int causal = 0; causal < 2; ++causal) {
+    const fa_plan_t h = fa_make_plan(2, 32, 8, 8192, 8192, causal, 32, 8);  // 2048 items
+    check_persistent(h, 256, causal ? 1.01 : 1.0);
+    check_persistent(h, 248, 0);
+    check_persistent(h, 304, 0);
+    check_persistent(h, 8, 0);
+    check_persistent(h, 4096, 0);                                            // more workgroups than items
+    check_persistent(fa_make_plan(1, 36, 9, 7350, 7350, causal, 32, 8), 256, 0);  // 1035 items
+    check_persistent(fa_make_plan(1, 16, 4, 32768, 32768, causal, 32, 8), 256, causal ? 1.01 : 1.0);
+    check_persistent(fa_make_plan(1, 8, 1, 32768, 32768, causal, 32, 8), 256, causal ? 1.01 : 1.0);
+    check_persistent(fa_make_plan(3, 8, 2, 500, 700, causal, 32, 8), 16, 0);
+    check_persistent(fa_split_plan(fa_make_plan(2, 8, 2, 300, 3000, causal, 32, 8), 5, 64), 64, 0);
+  }
+  {
+    // near the size limit: ids stay in range and every workgroup's rounds
+    // add up to the grid
+    const fa_plan_t big = fa_make_plan(64, 128, 8, 1 << 20, 1 << 20, 1, 32, 8);
+    long long count = 0;
+    for (unsigned g = 0; g < 256; ++g)
+      for (unsigned r = 0;; ++r) {
+        const unsigned id = fa_persistent_item(256, big.nwg, g, r);
+        if (id == ~0u) break;
+        CHECK((long long)id < big.nwg && id % 8 == g % 8);
+        ++count;
+      }
+    CHECK(count == big.nwg);
+  }
   // plan choice keeps >= 1024 workgroups when possible
   fa_plan_t c2 = fa_choose_plan(8, 12, 12, 1024, 1024, 1, 32, 1024, 8);
   CHECK(c2.nw == 2 && c2.nwg == 8 * 12 * 16);

@@ -189,3 +189,27 @@ def test_large_grid_ragged(api, nq, nk, causal):
     if causal and nq > nk:
         # queries that see no key (i + nk - nq < 0): O = 0, LSE = -inf
         assert (o[:, :, : nq - nk] == 0).all() and np.isneginf(lse[:, :, : nq - nk]).all()
+
+
+@pytest.mark.parametrize("causal,n", [(True, 14600), (False, 7300)], ids=["causal_2061_items", "noncausal_1035_items"])
+def test_persistent_grid_covers_every_row(api, causal, n):
+    """Eight-wave d = 128 grids with more work items than CUs run as one
+    persistent workgroup per CU, each taking items in rounds.  Here the item
+    counts (2061 causal, 1035 not) are not multiples of 8 or of the CU count:
+    O and LSE start as NaN and must be written everywhere, and sampled rows
+    (block ends, the tail, random) match the oracle."""
+    w = gen.workload(1, 36, 9, n, n, 128, causal=causal)
+    x = gen.make_inputs(w, (n, int(causal), 77))
+    print(f"case: persistent grid {w.name}", flush=True)
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((1, 36, n), float("nan"), dtype=torch.float32, device="cuda")
+    api.fa_fwd(q, k, v, o, lse, w.softmax_scale, causal)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item(), "rows left unwritten"
+    of, lf = out_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    rows = _edge_rows(w, np.random.default_rng(n), 48)
+    qf, kf, vf = (to_f64(x[t], "bf16") for t in "qkv")
+    o_ref, lse_ref = attention_rows_fp64(qf, kf, vf, w.softmax_scale, causal, rows)
+    compare(np.stack([of[b, h, i] for b, h, i in rows]), np.array([lf[b, h, i] for b, h, i in rows]),
+            o_ref, lse_ref, what=w.name)
