@@ -549,16 +549,32 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
       copy_all(j, par);
     }
   };
-  // t1 - t0 + 1 iterations (the last one only adds P V of the range's last
-  // tile); score and probability buffers alternate (unrolled by two)
+  // iterations 0 .. n-1 (n = t1 - t0); score and probability buffers
+  // alternate (unrolled by two)
   const int n = t1 - t0;
-  for (int i = 0; i <= n; i += 2) {
+  for (int i = 0; i <= n - 1; i += 2) {
     iteration(i, P0{}, sa, sb, pa, pb);
-    if (i + 1 <= n) iteration(i + 1, P1{}, sb, sa, pb, pa);
+    if (i + 1 <= n - 1) iteration(i + 1, P1{}, sb, sa, pb, pa);
   }
-  // the last copies (zeros past the final tile) land before the workgroup's
-  // LDS can pass to another workgroup
+  // iteration n only adds O += V_{t1-1} P_{t1-1} (no tile follows: no
+  // scores, exponentials or copies); its buffers by the parity of n
   vm_wait<0>();
+  __syncthreads();
+  if (n <= ntw) {
+    LDS_AS const char* vprev = ((n & 1) ? (LDS_AS const char*)lv0_ : (LDS_AS const char*)lv1_) + voff_l;
+    Probs pp;
+#pragma unroll
+    for (int ps = 0; ps < PS; ++ps) pp.v[ps] = (n & 1) ? pa.v[ps] : pb.v[ps];
+    bf16x8 vbuf[VPF];
+#pragma unroll
+    for (int t = 0; t < VPF; ++t) vbuf[t] = v_frag<RSV>(vprev, t / DB, t % DB);
+#pragma unroll
+    for (int m = 0; m < NPV; ++m) {
+      const int ps = m / DB, db = m % DB;
+      o[db] = mfma(vbuf[m % VPF], __builtin_bit_cast(bf16x8, pp.v[ps]), o[db]);
+      if (m + VPF < NPV) vbuf[m % VPF] = v_frag<RSV>(vprev, (m + VPF) / DB, (m + VPF) % DB);
+    }
+  }
   }  // t1 > t0
 
   // ---- epilogue: O / l, LSE = ln2 * (m_ref + log2 l); with a key split, the
