@@ -76,11 +76,14 @@ using P1 = std::integral_constant<int, 1>;
 //   P^T  = 2^(S^T c - L2), dS^T = P^T o (dP^T - D), packed to bf16 in place
 //   dQ^T += K^T dS^T (A = K^T, transposed LDS reads in the row order of the
 //   S^T accumulator)
+// One work item (fa_decode of id) per call; a persistent workgroup calls it
+// once per item, with a barrier in between (the LDS ring is reused).
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
-void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-                      const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
-                      float* __restrict__ LD, __bf16* __restrict__ dQ, fa_plan_t p, float c, float scale) {
+__device__ __forceinline__ void bwd_dq_item(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                                            const __bf16* __restrict__ V, const __bf16* __restrict__ O,
+                                            const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+                                            float* __restrict__ LD, __bf16* __restrict__ dQ, const fa_plan_t& p,
+                                            float c, float scale, unsigned id) {
   using C = BwdCfg<D>;
   constexpr int DS = C::DS, DB = C::DB, KB = C::KB, PS = C::PS, RSX = C::RSX, RSR = C::RSR;
   using CopyK = CopyPlan<D, NW, C::SPR_X, true>;
@@ -94,7 +97,7 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
   auto vslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lv0_ : lv1_); };
   LDS_AS char* const spare = (LDS_AS char*)lsp_;
 
-  const fa_work_t w = fa_decode(p, blockIdx.x);
+  const fa_work_t w = fa_decode(p, id);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hq = w.hq0 + wave % p.hw;
   const int q0w = w.qpos0 + (wave / p.hw) * 32;
@@ -220,6 +223,26 @@ void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K
       for (int e = 0; e < 4; ++e) r[e] = (__bf16)(dq[db][i4 * 4 + e] * scale);
       *(bf16x4*)(dQ + orow + db * 32 + i4 * 8 + (lane >> 5) * 4) = r;
     }
+}
+
+// One workgroup per work item, or, for the 8-wave d = 128 kernel (one
+// workgroup per CU), the forward kernel's persistent grid
+// (fa_persistent_item) when the plan has more items than CUs.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+                      const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
+                      float* __restrict__ LD, __bf16* __restrict__ dQ, fa_plan_t p, float c, float scale) {
+  if constexpr (!(D == 128 && NW == 8)) {
+    bwd_dq_item<D, CAUSAL, NW>(Q, K, V, O, dO, LSE, LD, dQ, p, c, scale, blockIdx.x);
+  } else {
+    for (unsigned r = 0;; ++r) {
+      const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
+      if (id == ~0u) break;
+      if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
+      bwd_dq_item<D, CAUSAL, NW>(Q, K, V, O, dO, LSE, LD, dQ, p, c, scale, id);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- dK, dV
@@ -526,9 +549,10 @@ int bwd_dkdv_max_waves(int d) { return d == 64 ? 4 : d == 128 ? 8 : 4; }
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, void* dq, float* ld, const fa_plan_t& pq, int d, float c, float scale,
                          hipStream_t stream) {
+  const unsigned grid = (d == 128 && pq.nw == 8) ? persistent_grid(pq.nwg) : (unsigned)pq.nwg;
 #define FA_CASE_DQ(DD, CC, NN)                                                                             \
   if (d == DD && (pq.causal != 0) == CC && pq.nw == NN) {                                                   \
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<DD, CC, NN>), dim3((unsigned)pq.nwg), dim3(64 * NN), 0, stream,       \
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DD, CC, NN>), dim3(grid), dim3(64 * NN), 0, stream,                  \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o,                  \
                        (const __bf16*)dout, lse, ld, (__bf16*)dq, pq, c, scale);                              \
     return hipGetLastError();                                                                               \

@@ -703,21 +703,22 @@ hipError_t launch_merge(const float* ows, const float* lws, void* o, float* lse,
 
 int queries_per_wave(int, int) { return 32; }
 
-// Workgroups of a bf16 forward launch: p.nwg, or, for the 8-wave d = 128
-// kernel (one workgroup per CU), a persistent grid of one workgroup per CU
-// of the current device (rounded down to a multiple of 8) when p.nwg is
-// larger.
-static unsigned fwd_grid(const fa_plan_t& p, int d) {
-  if (d != 128 || p.nw != 8) return (unsigned)p.nwg;
+unsigned persistent_grid(long long nwg) {
   static int cus[64] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (unsigned)p.nwg;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (unsigned)nwg;
   if (cus[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
     cus[dev] = n >= 8 ? n / 8 * 8 : -1;
   }
-  return (cus[dev] > 0 && p.nwg > cus[dev]) ? (unsigned)cus[dev] : (unsigned)p.nwg;
+  return (cus[dev] > 0 && nwg > cus[dev]) ? (unsigned)cus[dev] : (unsigned)nwg;
+}
+
+// Workgroups of a bf16 forward launch: p.nwg, or a persistent grid for the
+// 8-wave d = 128 kernel (one workgroup per CU).
+static unsigned fwd_grid(const fa_plan_t& p, int d) {
+  return (d == 128 && p.nw == 8) ? persistent_grid(p.nwg) : (unsigned)p.nwg;
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,

@@ -11,6 +11,12 @@ namespace fa {
 // Query rows per wave of the forward kernel for head dimension d.
 int queries_per_wave(int d, int f32);
 
+// Workgroups of a launch whose kernel holds a whole CU per workgroup (the
+// 8-wave d = 128 forward and dQ kernels): nwg, or one per CU of the current
+// device (rounded down to a multiple of 8) when nwg is larger; the kernel
+// then takes its work items in rounds (fa_persistent_item).
+unsigned persistent_grid(long long nwg);
+
 // Enqueue the forward kernel.  c = scale * log2(e).  f32 selects fp32
 // operands (split into bf16 hi/lo parts inside the kernel).  With a key
 // split (p.nsplit > 1, bf16 only) the kernel writes the partial results of
