@@ -304,3 +304,36 @@ def test_backward_persistent_dq_covers_every_row(api, causal, n):
             got.append(dqf[0, h, i])
             ref.append(rq[0, 0, 0])
     compare_grad(np.array(got), np.array(ref), f"{w.name} dQ rows")
+
+
+@pytest.mark.parametrize("case", [(8, 32, 8, 2048, True), (11, 28, 7, 1700, False)],
+                         ids=["causal_512_items", "noncausal_539_items"])
+def test_backward_persistent_dkdv_covers_every_key(api, case):
+    """Up to 4096 query rows, the eight-wave d = 128 dK/dV kernel runs as a
+    persistent grid when its plan has at least two key blocks per CU (here 512
+    and 539 items, the second not a multiple of 8).  dQ, dK and dV start as NaN
+    and must be written everywhere; one head group's gradients match the
+    oracle."""
+    B, Hq, Hkv, N, causal = case
+    w = gen.workload(B, Hq, Hkv, N, N, 128, causal=causal)
+    x = gen.make_inputs(w, (N, int(causal), 79))
+    do_bits = gen.make_dout(w, (N, int(causal), 79))
+    print(f"case: backward persistent dK/dV {w.name}", flush=True)
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    do = to_device(do_bits, "bf16")
+    o, lse = api.attention(q, k, v, causal=causal, scale=w.softmax_scale)
+    dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
+    nbytes = api.bwd_workspace_size(B, Hq, Hkv, N, N, 128, causal)
+    ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device="cuda")
+    api.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.softmax_scale, causal, ws)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert not torch.isnan(t).any().item(), f"{name} left unwritten"
+    b, hk, G = B - 1, Hkv - 1, Hq // Hkv
+    hs = slice(hk * G, hk * G + G)
+    rq, rk, rv = attention_backward_fp64(to_f64(x["q"][b:b + 1, hs], "bf16"), to_f64(x["k"][b:b + 1, hk:hk + 1], "bf16"),
+                                         to_f64(x["v"][b:b + 1, hk:hk + 1], "bf16"),
+                                         to_f64(do_bits[b:b + 1, hs], "bf16"), w.softmax_scale, causal)
+    compare_grad(out_to_f64(dq)[b:b + 1, hs], rq, f"{w.name} dQ")
+    compare_grad(out_to_f64(dk)[b:b + 1, hk:hk + 1], rk, f"{w.name} dK")
+    compare_grad(out_to_f64(dv)[b:b + 1, hk:hk + 1], rv, f"{w.name} dV")
