@@ -612,18 +612,18 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
   if (LSE != nullptr && lane < 32) LSE[qrow0 + q_l] = lse_row;
 }
 
-// A grid of p.nwg workgroups runs one work item each.  The 8-wave d = 128
-// kernel, which holds a whole CU, also runs as a persistent grid of one
-// workgroup per CU (fa_persistent_item): each workgroup then takes its
-// items one after another, so a CU's next item starts without a new
-// workgroup's dispatch, and the snake order over the heaviest-first causal
-// work gives every workgroup an even share.
+// A grid of p.nwg workgroups runs one work item each.  The kernels that hold
+// a whole CU per workgroup (8 waves at d = 128, 4 at d = 256) also run as a
+// persistent grid of one workgroup per CU (fa_persistent_item): each
+// workgroup then takes its items one after another, so a CU's next item
+// starts without a new workgroup's dispatch, and the snake order over the
+// heaviest-first causal work gives every workgroup an even share.
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                         __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c,
                         float* __restrict__ OWS, float* __restrict__ LWS) {
-  if constexpr (!(D == 128 && NW == 8)) {
+  if constexpr (!((D == 128 && NW == 8) || (D == 256 && NW == 4))) {
     fwd_bf16_item<D, CAUSAL, NW>(Q, K, V, O, LSE, p, c, OWS, LWS, blockIdx.x);
   } else {
     for (unsigned r = 0;; ++r) {
@@ -716,9 +716,9 @@ unsigned persistent_grid(long long nwg) {
 }
 
 // Workgroups of a bf16 forward launch: p.nwg, or a persistent grid for the
-// 8-wave d = 128 kernel (one workgroup per CU).
+// kernels that hold a whole CU per workgroup.
 static unsigned fwd_grid(const fa_plan_t& p, int d) {
-  return (d == 128 && p.nw == 8) ? persistent_grid(p.nwg) : (unsigned)p.nwg;
+  return ((d == 128 && p.nw == 8) || (d == 256 && p.nw == 4)) ? persistent_grid(p.nwg) : (unsigned)p.nwg;
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,

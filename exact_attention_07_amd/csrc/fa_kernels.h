@@ -12,9 +12,10 @@ namespace fa {
 int queries_per_wave(int d, int f32);
 
 // Workgroups of a launch whose kernel holds a whole CU per workgroup (the
-// 8-wave d = 128 forward and dQ kernels): nwg, or one per CU of the current
-// device (rounded down to a multiple of 8) when nwg is larger; the kernel
-// then takes its work items in rounds (fa_persistent_item).
+// forward at 8 waves and d = 128 or 4 waves and d = 256, the 8-wave d = 128
+// dQ and dK/dV kernels): nwg, or one per CU of the current device (rounded
+// down to a multiple of 8) when nwg is larger; the kernel then takes its
+// work items in rounds (fa_persistent_item).
 unsigned persistent_grid(long long nwg);
 
 // Enqueue the forward kernel.  c = scale * log2(e).  f32 selects fp32

@@ -191,19 +191,30 @@ def test_large_grid_ragged(api, nq, nk, causal):
         assert (o[:, :, : nq - nk] == 0).all() and np.isneginf(lse[:, :, : nq - nk]).all()
 
 
-@pytest.mark.parametrize("causal,n", [(True, 14600), (False, 7300)], ids=["causal_2061_items", "noncausal_1035_items"])
-def test_persistent_grid_covers_every_row(api, causal, n):
-    """Eight-wave d = 128 grids with more work items than CUs run as one
-    persistent workgroup per CU, each taking items in rounds.  Here the item
-    counts (2061 causal, 1035 not) are not multiples of 8 or of the CU count:
-    O and LSE start as NaN and must be written everywhere, and sampled rows
-    (block ends, the tail, random) match the oracle."""
-    w = gen.workload(1, 36, 9, n, n, 128, causal=causal)
+PERSISTENT = [
+    # B, Hq, Hkv, N, d, causal: work items of the plan
+    (1, 36, 9, 14600, 128, True),    # 2061 items of 8 waves
+    (1, 36, 9, 7300, 128, False),    # 1035
+    (1, 7, 7, 4990, 256, True),      # 273 items of 4 waves
+    (3, 12, 6, 2000, 256, False),    # 576
+]
+
+
+@pytest.mark.parametrize("case", PERSISTENT, ids=lambda c: "x".join(map(str, c)))
+def test_persistent_grid_covers_every_row(api, case):
+    """The kernels that hold a whole CU per workgroup (8 waves at d = 128, 4
+    at d = 256) run grids with more work items than CUs as one persistent
+    workgroup per CU, each taking items in rounds.  Item counts here are not
+    multiples of the CU count (nor, but one, of 8): O and LSE start as NaN and
+    must be written everywhere, and sampled rows (block ends, the tail,
+    random) match the oracle."""
+    B, Hq, Hkv, n, d, causal = case
+    w = gen.workload(B, Hq, Hkv, n, n, d, causal=causal)
     x = gen.make_inputs(w, (n, int(causal), 77))
     print(f"case: persistent grid {w.name}", flush=True)
     q, k, v = (to_device(x[t], "bf16") for t in "qkv")
     o = torch.full_like(q, float("nan"))
-    lse = torch.full((1, 36, n), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((B, Hq, n), float("nan"), dtype=torch.float32, device="cuda")
     api.fa_fwd(q, k, v, o, lse, w.softmax_scale, causal)
     torch.cuda.synchronize()
     assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item(), "rows left unwritten"
