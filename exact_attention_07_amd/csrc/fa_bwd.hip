@@ -225,25 +225,42 @@ __device__ __forceinline__ void bwd_dq_item(const __bf16* __restrict__ Q, const 
     }
 }
 
-// One workgroup per work item, or, for the 8-wave d = 128 kernel (one
-// workgroup per CU), the forward kernel's persistent grid
-// (fa_persistent_item) when the plan has more items than CUs.
+// One workgroup per work item.
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void fa_bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                       const __bf16* __restrict__ O, const __bf16* __restrict__ dO, const float* __restrict__ LSE,
                       float* __restrict__ LD, __bf16* __restrict__ dQ, fa_plan_t p, float c, float scale) {
-  if constexpr (!(D == 128 && NW == 8)) {
-    bwd_dq_item<D, CAUSAL, NW>(Q, K, V, O, dO, LSE, LD, dQ, p, c, scale, blockIdx.x);
-  } else {
-    for (unsigned r = 0;; ++r) {
-      const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
-      if (id == ~0u) break;
-      if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
-      bwd_dq_item<D, CAUSAL, NW>(Q, K, V, O, dO, LSE, LD, dQ, p, c, scale, id);
-    }
+  bwd_dq_item<D, CAUSAL, NW>(Q, K, V, O, dO, LSE, LD, dQ, p, c, scale, blockIdx.x);
+}
+
+// The kernels that hold a whole CU per workgroup (8 waves at d = 128, 4 at
+// d = 256) as the forward kernel's persistent grid (fa_persistent_item),
+// for plans with more items than CUs.  A kernel of its own, so that the
+// one-item kernel keeps its code where it is used.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void fa_bwd_dq_persistent_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+                                 const __bf16* __restrict__ V, const __bf16* __restrict__ O,
+                                 const __bf16* __restrict__ dO, const float* __restrict__ LSE, float* __restrict__ LD,
+                                 __bf16* __restrict__ dQ, fa_plan_t p, float c, float scale) {
+  for (unsigned r = 0;; ++r) {
+    const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
+    if (id == ~0u) break;
+    if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
+    bwd_dq_item<D, CAUSAL, NW>(Q, K, V, O, dO, LSE, LD, dQ, p, c, scale, id);
   }
 }
+#define FA_INST_DQ_P(DD, CC, NN)                                                                               \
+  template __global__ void fa_bwd_dq_persistent_kernel<DD, CC, NN>(                                            \
+      const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, \
+      const __bf16* __restrict__, const float* __restrict__, float* __restrict__, __bf16* __restrict__, fa_plan_t, \
+      float, float);
+FA_INST_DQ_P(128, false, 8)
+FA_INST_DQ_P(128, true, 8)
+FA_INST_DQ_P(256, false, 4)
+FA_INST_DQ_P(256, true, 4)
+#undef FA_INST_DQ_P
 
 // ---------------------------------------------------------------- dK, dV
 // Wave state: K and V rows of KBW blocks of 32 keys as B operands (lane: key
@@ -508,13 +525,14 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   bwd_dkdv_item<D, CAUSAL, NW, KBW>(Q, K, V, dO, LD, dK, dV, PART, p, c, scale, blockIdx.x);
 }
 
-// The 8-wave d = 128 kernel (one workgroup per CU) as a persistent grid of
-// fewer workgroups than items (fa_persistent_item over the key-block order):
-// the snake gives every workgroup heavy and light causal key blocks alike.
-// A kernel of its own: the loop around the item slows the one-item kernel's
-// inner loop by 3-5 % where it is kept (Nq > 4096).
-template <bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1)))
+// The kernels that hold a whole CU per workgroup (8 waves at d = 128, 4 at
+// d = 256) as a persistent grid of fewer workgroups than items
+// (fa_persistent_item over the key-block order): the snake gives every
+// workgroup heavy and light causal key blocks alike.  A kernel of its own:
+// the loop around the item slows the one-item kernel's inner loop by 3-5 %
+// where that is kept (Nq > 4096).
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1)))
 void fa_bwd_dkdv_persistent_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
                                    const float* __restrict__ LD, __bf16* __restrict__ dK, __bf16* __restrict__ dV,
@@ -523,17 +541,19 @@ void fa_bwd_dkdv_persistent_kernel(const __bf16* __restrict__ Q, const __bf16* _
     const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
     if (id == ~0u) break;
     if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
-    bwd_dkdv_item<128, CAUSAL, 8, 1>(Q, K, V, dO, LD, dK, dV, PART, p, c, scale, id);
+    bwd_dkdv_item<D, CAUSAL, NW, 1>(Q, K, V, dO, LD, dK, dV, PART, p, c, scale, id);
   }
 }
-template __global__ void fa_bwd_dkdv_persistent_kernel<false>(
-    const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__,
-    const float* __restrict__, __bf16* __restrict__, __bf16* __restrict__, float* __restrict__, fa_kvplan_t, float,
-    float);
-template __global__ void fa_bwd_dkdv_persistent_kernel<true>(
-    const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__,
-    const float* __restrict__, __bf16* __restrict__, __bf16* __restrict__, float* __restrict__, fa_kvplan_t, float,
-    float);
+#define FA_INST_DKDV_P(DD, CC, NN)                                                                             \
+  template __global__ void fa_bwd_dkdv_persistent_kernel<DD, CC, NN>(                                          \
+      const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, \
+      const float* __restrict__, __bf16* __restrict__, __bf16* __restrict__, float* __restrict__, fa_kvplan_t,   \
+      float, float);
+FA_INST_DKDV_P(128, false, 8)
+FA_INST_DKDV_P(128, true, 8)
+FA_INST_DKDV_P(256, false, 4)
+FA_INST_DKDV_P(256, true, 4)
+#undef FA_INST_DKDV_P
 
 // ---------------------------------------------------------------- launchers
 // dK and dV from the head parts' partial sums: for every element, the sum
@@ -589,10 +609,29 @@ int bwd_dkdv_max_waves(int d) { return d == 64 ? 4 : d == 128 ? 8 : 4; }
 hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
                          const float* lse, void* dq, float* ld, const fa_plan_t& pq, int d, float c, float scale,
                          hipStream_t stream) {
-  const unsigned grid = (d == 128 && pq.nw == 8) ? persistent_grid(pq.nwg) : (unsigned)pq.nwg;
+  // persistent: the 8-wave d = 128 kernel always (configuration-3 backward
+  // +0.4 %, N2048 +1.6 %), the 4-wave d = 256 one up to Nq = 4096 (causal
+  // N1024-2048 +22-29 % with the dK/dV grid; at N8192 2 % slower)
+  const bool persist = (d == 128 && pq.nw == 8) || (d == 256 && pq.nw == 4 && pq.Nq <= 4096);
+  const unsigned grid = persist ? persistent_grid(pq.nwg) : 0;
+  if (grid > 0 && (long long)grid < pq.nwg) {
+#define FA_DQ_P(DD, CC, NN)                                                                                    \
+  hipLaunchKernelGGL((fa_bwd_dq_persistent_kernel<DD, CC, NN>), dim3(grid), dim3(64 * NN), 0, stream,            \
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, (const __bf16*)dout, \
+                     lse, ld, (__bf16*)dq, pq, c, scale)
+    if (d == 128) {
+      if (pq.causal) FA_DQ_P(128, true, 8);
+      else FA_DQ_P(128, false, 8);
+    } else {
+      if (pq.causal) FA_DQ_P(256, true, 4);
+      else FA_DQ_P(256, false, 4);
+    }
+#undef FA_DQ_P
+    return hipGetLastError();
+  }
 #define FA_CASE_DQ(DD, CC, NN)                                                                             \
   if (d == DD && (pq.causal != 0) == CC && pq.nw == NN) {                                                   \
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<DD, CC, NN>), dim3(grid), dim3(64 * NN), 0, stream,                  \
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<DD, CC, NN>), dim3((unsigned)pq.nwg), dim3(64 * NN), 0, stream,       \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o,                  \
                        (const __bf16*)dout, lse, ld, (__bf16*)dq, pq, c, scale);                              \
     return hipGetLastError();                                                                               \
@@ -611,16 +650,21 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   // key block (Nq <= 4096) and with at least two items per workgroup:
   // measured 7-24 % faster there (causal MHA and GQA, N 2048-4096); longer
   // sequences and partial second rounds keep one workgroup per item
-  const unsigned grid = (d == 128 && pk.nw == 8 && pk.kpw == 32 && pk.Nq <= 4096) ? persistent_grid(pk.nwg) : 0;
+  const bool whole_cu = ((d == 128 && pk.nw == 8) || (d == 256 && pk.nw == 4)) && pk.kpw == 32;
+  const unsigned grid = (whole_cu && pk.Nq <= 4096) ? persistent_grid(pk.nwg) : 0;
   if (grid > 0 && 2LL * grid <= pk.nwg) {
-    if (pk.causal)
-      hipLaunchKernelGGL(fa_bwd_dkdv_persistent_kernel<true>, dim3(grid), dim3(512), 0, stream, (const __bf16*)q,
-                         (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld, (__bf16*)dk, (__bf16*)dv, part,
-                         pk, c, scale);
-    else
-      hipLaunchKernelGGL(fa_bwd_dkdv_persistent_kernel<false>, dim3(grid), dim3(512), 0, stream, (const __bf16*)q,
-                         (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld, (__bf16*)dk, (__bf16*)dv, part,
-                         pk, c, scale);
+#define FA_DKDV_P(DD, CC, NN)                                                                                  \
+  hipLaunchKernelGGL((fa_bwd_dkdv_persistent_kernel<DD, CC, NN>), dim3(grid), dim3(64 * NN), 0, stream,          \
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld, (__bf16*)dk, \
+                     (__bf16*)dv, part, pk, c, scale)
+    if (d == 128) {
+      if (pk.causal) FA_DKDV_P(128, true, 8);
+      else FA_DKDV_P(128, false, 8);
+    } else {
+      if (pk.causal) FA_DKDV_P(256, true, 4);
+      else FA_DKDV_P(256, false, 4);
+    }
+#undef FA_DKDV_P
     e = hipGetLastError();
   } else
 #define FA_CASE_DKDV(DD, CC, NN, KK)                                                                        \

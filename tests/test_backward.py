@@ -306,16 +306,19 @@ def test_backward_persistent_dq_covers_every_row(api, causal, n):
     compare_grad(np.array(got), np.array(ref), f"{w.name} dQ rows")
 
 
-@pytest.mark.parametrize("case", [(8, 32, 8, 2048, True), (11, 28, 7, 1700, False)],
-                         ids=["causal_512_items", "noncausal_539_items"])
+@pytest.mark.parametrize("case", [(8, 32, 8, 2048, 128, True), (11, 28, 7, 1700, 128, False),
+                                  (4, 16, 16, 2048, 256, True), (6, 16, 8, 1500, 256, False)],
+                         ids=["d128_causal_512_items", "d128_noncausal_539_items", "d256_causal_1024_items",
+                              "d256_noncausal_576_items"])
 def test_backward_persistent_dkdv_covers_every_key(api, case):
-    """Up to 4096 query rows, the eight-wave d = 128 dK/dV kernel runs as a
-    persistent grid when its plan has at least two key blocks per CU (here 512
-    and 539 items, the second not a multiple of 8).  dQ, dK and dV start as NaN
-    and must be written everywhere; one head group's gradients match the
+    """Up to 4096 query rows, the dK/dV kernels that hold a whole CU per
+    workgroup (8 waves at d = 128, 4 at d = 256) run as persistent grids when
+    the plan has at least two key blocks per CU (here 512 to 1024 items, one
+    count not a multiple of 8); so do the dQ kernels.  dQ, dK and dV start as
+    NaN and must be written everywhere; one head group's gradients match the
     oracle."""
-    B, Hq, Hkv, N, causal = case
-    w = gen.workload(B, Hq, Hkv, N, N, 128, causal=causal)
+    B, Hq, Hkv, N, d, causal = case
+    w = gen.workload(B, Hq, Hkv, N, N, d, causal=causal)
     x = gen.make_inputs(w, (N, int(causal), 79))
     do_bits = gen.make_dout(w, (N, int(causal), 79))
     print(f"case: backward persistent dK/dV {w.name}", flush=True)
@@ -323,7 +326,7 @@ def test_backward_persistent_dkdv_covers_every_key(api, case):
     do = to_device(do_bits, "bf16")
     o, lse = api.attention(q, k, v, causal=causal, scale=w.softmax_scale)
     dq, dk, dv = (torch.full_like(t, float("nan")) for t in (q, k, v))
-    nbytes = api.bwd_workspace_size(B, Hq, Hkv, N, N, 128, causal)
+    nbytes = api.bwd_workspace_size(B, Hq, Hkv, N, N, d, causal)
     ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device="cuda")
     api.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, w.softmax_scale, causal, ws)
     torch.cuda.synchronize()
