@@ -614,7 +614,8 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
 
 // A grid of p.nwg workgroups runs one work item each.  The kernels that hold
 // a whole CU per workgroup (8 waves at d = 128, 4 at d = 256) also run as a
-// persistent grid of one workgroup per CU (fa_persistent_item): each
+// persistent grid of one workgroup per CU (fa_persistent_item), and so do the
+// causal 4-wave kernels at d = 64 and 128, two workgroups per CU: each
 // workgroup then takes its items one after another, so a CU's next item
 // starts without a new workgroup's dispatch, and the snake order over the
 // heaviest-first causal work gives every workgroup an even share.
@@ -623,7 +624,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, 
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                         __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c,
                         float* __restrict__ OWS, float* __restrict__ LWS) {
-  if constexpr (!((D == 128 && NW == 8) || (D == 256 && NW == 4))) {
+  if constexpr (!((D == 128 && NW == 8) || (D == 256 && NW == 4) || (CAUSAL && NW == 4 && (D == 64 || D == 128)))) {
     fwd_bf16_item<D, CAUSAL, NW>(Q, K, V, O, LSE, p, c, OWS, LWS, blockIdx.x);
   } else {
     for (unsigned r = 0;; ++r) {
@@ -703,7 +704,7 @@ hipError_t launch_merge(const float* ows, const float* lws, void* o, float* lse,
 
 int queries_per_wave(int, int) { return 32; }
 
-unsigned persistent_grid(long long nwg) {
+unsigned persistent_grid(long long nwg, int per_cu) {
   static int cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (unsigned)nwg;
@@ -712,13 +713,18 @@ unsigned persistent_grid(long long nwg) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
     cus[dev] = n >= 8 ? n / 8 * 8 : -1;
   }
-  return (cus[dev] > 0 && nwg > cus[dev]) ? (unsigned)cus[dev] : (unsigned)nwg;
+  const long long g = (long long)cus[dev] * per_cu;
+  return (cus[dev] > 0 && nwg > g) ? (unsigned)g : (unsigned)nwg;
 }
 
 // Workgroups of a bf16 forward launch: p.nwg, or a persistent grid for the
-// kernels that hold a whole CU per workgroup.
+// kernels that hold a whole CU per workgroup and for the causal 4-wave ones
+// that fit two per CU (LDS and registers; non-causal items are all alike,
+// and measured 1.8 % slower at d = 64).
 static unsigned fwd_grid(const fa_plan_t& p, int d) {
-  return ((d == 128 && p.nw == 8) || (d == 256 && p.nw == 4)) ? persistent_grid(p.nwg) : (unsigned)p.nwg;
+  if ((d == 128 && p.nw == 8) || (d == 256 && p.nw == 4)) return persistent_grid(p.nwg);
+  if ((d == 128 || d == 64) && p.nw == 4 && p.causal) return persistent_grid(p.nwg, 2);
+  return (unsigned)p.nwg;
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,

@@ -11,12 +11,13 @@ namespace fa {
 // Query rows per wave of the forward kernel for head dimension d.
 int queries_per_wave(int d, int f32);
 
-// Workgroups of a launch whose kernel holds a whole CU per workgroup (the
-// forward at 8 waves and d = 128 or 4 waves and d = 256, the 8-wave d = 128
-// dQ and dK/dV kernels): nwg, or one per CU of the current device (rounded
-// down to a multiple of 8) when nwg is larger; the kernel then takes its
-// work items in rounds (fa_persistent_item).
-unsigned persistent_grid(long long nwg);
+// Workgroups of a persistent launch whose kernel fits per_cu workgroups on
+// a CU (one: the forward at 8 waves and d = 128 or 4 waves and d = 256, the
+// dQ and dK/dV kernels of those shapes; two: the causal 4-wave forward at
+// d = 64 and 128): nwg, or per_cu per CU of the current device (the CU
+// count rounded down to a multiple of 8) when nwg is larger; the kernel then
+// takes its work items in rounds (fa_persistent_item).
+unsigned persistent_grid(long long nwg, int per_cu = 1);
 
 // Enqueue the forward kernel.  c = scale * log2(e).  f32 selects fp32
 // operands (split into bf16 hi/lo parts inside the kernel).  With a key

@@ -197,6 +197,8 @@ PERSISTENT = [
     (1, 36, 9, 7300, 128, False),    # 1035
     (1, 7, 7, 4990, 256, True),      # 273 items of 4 waves
     (3, 12, 6, 2000, 256, False),    # 576
+    (4, 10, 5, 1900, 64, True),      # 600 items of 4 waves, two workgroups per CU
+    (3, 12, 12, 1900, 128, True),    # 540
 ]
 
 
@@ -204,10 +206,11 @@ PERSISTENT = [
 def test_persistent_grid_covers_every_row(api, case):
     """The kernels that hold a whole CU per workgroup (8 waves at d = 128, 4
     at d = 256) run grids with more work items than CUs as one persistent
-    workgroup per CU, each taking items in rounds.  Item counts here are not
-    multiples of the CU count (nor, but one, of 8): O and LSE start as NaN and
-    must be written everywhere, and sampled rows (block ends, the tail,
-    random) match the oracle."""
+    workgroup per CU, each taking items in rounds; the causal 4-wave kernels at
+    d = 64 and 128 do so with two workgroups per CU.  Item counts here are not
+    multiples of the grid (most not of 8): O and LSE start as NaN and must be
+    written everywhere, and sampled rows (block ends, the tail, random) match
+    the oracle."""
     B, Hq, Hkv, n, d, causal = case
     w = gen.workload(B, Hq, Hkv, n, n, d, causal=causal)
     x = gen.make_inputs(w, (n, int(causal), 77))
