@@ -531,7 +531,7 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
 // workgroup heavy and light causal key blocks alike.  A kernel of its own:
 // the loop around the item slows the one-item kernel's inner loop by 3-5 %
 // where that is kept (Nq > 4096).
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, int KBW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1)))
 void fa_bwd_dkdv_persistent_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                    const __bf16* __restrict__ V, const __bf16* __restrict__ dO,
@@ -541,18 +541,22 @@ void fa_bwd_dkdv_persistent_kernel(const __bf16* __restrict__ Q, const __bf16* _
     const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
     if (id == ~0u) break;
     if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
-    bwd_dkdv_item<D, CAUSAL, NW, 1>(Q, K, V, dO, LD, dK, dV, PART, p, c, scale, id);
+    bwd_dkdv_item<D, CAUSAL, NW, KBW>(Q, K, V, dO, LD, dK, dV, PART, p, c, scale, id);
   }
 }
-#define FA_INST_DKDV_P(DD, CC, NN)                                                                             \
-  template __global__ void fa_bwd_dkdv_persistent_kernel<DD, CC, NN>(                                          \
+#define FA_INST_DKDV_P(DD, CC, NN, KK)                                                                         \
+  template __global__ void fa_bwd_dkdv_persistent_kernel<DD, CC, NN, KK>(                                      \
       const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, const __bf16* __restrict__, \
       const float* __restrict__, __bf16* __restrict__, __bf16* __restrict__, float* __restrict__, fa_kvplan_t,   \
       float, float);
-FA_INST_DKDV_P(128, false, 8)
-FA_INST_DKDV_P(128, true, 8)
-FA_INST_DKDV_P(256, false, 4)
-FA_INST_DKDV_P(256, true, 4)
+FA_INST_DKDV_P(128, false, 8, 1)
+FA_INST_DKDV_P(128, true, 8, 1)
+FA_INST_DKDV_P(256, false, 4, 1)
+FA_INST_DKDV_P(256, true, 4, 1)
+FA_INST_DKDV_P(64, false, 4, 2)
+FA_INST_DKDV_P(64, true, 4, 2)
+FA_INST_DKDV_P(64, false, 2, 2)
+FA_INST_DKDV_P(64, true, 2, 2)
 #undef FA_INST_DKDV_P
 
 // ---------------------------------------------------------------- launchers
@@ -646,23 +650,33 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
                            hipStream_t stream) {
   if (pk.hsplit > 1 && part == nullptr) return hipErrorInvalidValue;
   hipError_t e = hipErrorInvalidValue;
-  // the 8-wave d = 128 kernel as a persistent grid up to 64 query tiles per
-  // key block (Nq <= 4096) and with at least two items per workgroup:
-  // measured 7-24 % faster there (causal MHA and GQA, N 2048-4096); longer
-  // sequences and partial second rounds keep one workgroup per item
-  const bool whole_cu = ((d == 128 && pk.nw == 8) || (d == 256 && pk.nw == 4)) && pk.kpw == 32;
-  const unsigned grid = (whole_cu && pk.Nq <= 4096) ? persistent_grid(pk.nwg) : 0;
+  // persistent grids up to 64 query tiles per key block (Nq <= 4096) and
+  // with at least two items per workgroup: measured 3-29 % faster there
+  // (d = 64, 128, 256; MHA and GQA; N 1024-4096); longer sequences and
+  // partial second rounds keep one workgroup per item
+  // workgroups per CU of the kernels with a persistent form: one for 8 waves
+  // at d = 128 (two waves per SIMD) and 4 waves at d = 256 and 64 (one wave
+  // per SIMD), two for 2 waves at d = 64
+  const int per_cu = ((d == 128 && pk.nw == 8) || (d == 256 && pk.nw == 4) || (d == 64 && pk.nw == 4)) ? 1
+                     : (d == 64 && pk.nw == 2) ? 2 : 0;
+  const unsigned grid = (per_cu > 0 && pk.Nq <= 4096) ? persistent_grid(pk.nwg, per_cu) : 0;
   if (grid > 0 && 2LL * grid <= pk.nwg) {
-#define FA_DKDV_P(DD, CC, NN)                                                                                  \
-  hipLaunchKernelGGL((fa_bwd_dkdv_persistent_kernel<DD, CC, NN>), dim3(grid), dim3(64 * NN), 0, stream,          \
+#define FA_DKDV_P(DD, CC, NN, KK)                                                                              \
+  hipLaunchKernelGGL((fa_bwd_dkdv_persistent_kernel<DD, CC, NN, KK>), dim3(grid), dim3(64 * NN), 0, stream,      \
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld, (__bf16*)dk, \
                      (__bf16*)dv, part, pk, c, scale)
     if (d == 128) {
-      if (pk.causal) FA_DKDV_P(128, true, 8);
-      else FA_DKDV_P(128, false, 8);
+      if (pk.causal) FA_DKDV_P(128, true, 8, 1);
+      else FA_DKDV_P(128, false, 8, 1);
+    } else if (d == 256) {
+      if (pk.causal) FA_DKDV_P(256, true, 4, 1);
+      else FA_DKDV_P(256, false, 4, 1);
+    } else if (pk.nw == 4) {
+      if (pk.causal) FA_DKDV_P(64, true, 4, 2);
+      else FA_DKDV_P(64, false, 4, 2);
     } else {
-      if (pk.causal) FA_DKDV_P(256, true, 4);
-      else FA_DKDV_P(256, false, 4);
+      if (pk.causal) FA_DKDV_P(64, true, 2, 2);
+      else FA_DKDV_P(64, false, 2, 2);
     }
 #undef FA_DKDV_P
     e = hipGetLastError();

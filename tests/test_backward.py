@@ -307,16 +307,18 @@ def test_backward_persistent_dq_covers_every_row(api, causal, n):
 
 
 @pytest.mark.parametrize("case", [(8, 32, 8, 2048, 128, True), (11, 28, 7, 1700, 128, False),
-                                  (4, 16, 16, 2048, 256, True), (6, 16, 8, 1500, 256, False)],
+                                  (4, 16, 16, 2048, 256, True), (6, 16, 8, 1500, 256, False),
+                                  (4, 16, 16, 2048, 64, True), (2, 32, 8, 4096, 64, True)],
                          ids=["d128_causal_512_items", "d128_noncausal_539_items", "d256_causal_1024_items",
-                              "d256_noncausal_576_items"])
+                              "d256_noncausal_576_items", "d64_causal_512_items", "d64_causal_2048_items_head_parts"])
 def test_backward_persistent_dkdv_covers_every_key(api, case):
-    """Up to 4096 query rows, the dK/dV kernels that hold a whole CU per
-    workgroup (8 waves at d = 128, 4 at d = 256) run as persistent grids when
-    the plan has at least two key blocks per CU (here 512 to 1024 items, one
-    count not a multiple of 8); so do the dQ kernels.  dQ, dK and dV start as
-    NaN and must be written everywhere; one head group's gradients match the
-    oracle."""
+    """Up to 4096 query rows, the dK/dV kernels that fill a CU with one or two
+    workgroups (8 waves at d = 128, 4 at d = 256 and 64, 2 at d = 64) run as
+    persistent grids when the plan has at least two key blocks per workgroup
+    (here 512 to 2048 items, one count not a multiple of 8, one plan with the
+    query heads split into parts); so do the dQ kernels at d = 128 and 256.
+    dQ, dK and dV start as NaN and must be written everywhere; one head
+    group's gradients match the oracle."""
     B, Hq, Hkv, N, d, causal = case
     w = gen.workload(B, Hq, Hkv, N, N, d, causal=causal)
     x = gen.make_inputs(w, (N, int(causal), 79))
