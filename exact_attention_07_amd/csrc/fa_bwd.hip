@@ -260,6 +260,7 @@ FA_INST_DQ_P(128, false, 8)
 FA_INST_DQ_P(128, true, 8)
 FA_INST_DQ_P(256, false, 4)
 FA_INST_DQ_P(256, true, 4)
+FA_INST_DQ_P(128, true, 4)
 #undef FA_INST_DQ_P
 
 // ---------------------------------------------------------------- dK, dV
@@ -616,14 +617,19 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void
   // persistent: the 8-wave d = 128 kernel always (configuration-3 backward
   // +0.4 %, N2048 +1.6 %), the 4-wave d = 256 one up to Nq = 4096 (causal
   // N1024-2048 +22-29 % with the dK/dV grid; at N8192 2 % slower)
-  const bool persist = (d == 128 && pq.nw == 8) || (d == 256 && pq.nw == 4 && pq.Nq <= 4096);
-  const unsigned grid = persist ? persistent_grid(pq.nwg) : 0;
+  // (the causal 4-wave d = 128 kernel fits two workgroups per CU and runs
+  // two per CU under the d = 256 rule)
+  const bool two = d == 128 && pq.nw == 4 && pq.causal && pq.Nq <= 4096;
+  const bool persist = (d == 128 && pq.nw == 8) || (d == 256 && pq.nw == 4 && pq.Nq <= 4096) || two;
+  const unsigned grid = persist ? persistent_grid(pq.nwg, two ? 2 : 1) : 0;
   if (grid > 0 && (long long)grid < pq.nwg) {
 #define FA_DQ_P(DD, CC, NN)                                                                                    \
   hipLaunchKernelGGL((fa_bwd_dq_persistent_kernel<DD, CC, NN>), dim3(grid), dim3(64 * NN), 0, stream,            \
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, (const __bf16*)dout, \
                      lse, ld, (__bf16*)dq, pq, c, scale)
-    if (d == 128) {
+    if (two) {
+      FA_DQ_P(128, true, 4);
+    } else if (d == 128) {
       if (pq.causal) FA_DQ_P(128, true, 8);
       else FA_DQ_P(128, false, 8);
     } else {

@@ -14,7 +14,8 @@ int queries_per_wave(int d, int f32);
 // Workgroups of a persistent launch whose kernel fits per_cu workgroups on
 // a CU (one: the forward at 8 waves and d = 128 or 4 waves and d = 256, the
 // dQ and dK/dV kernels of those shapes; two: the causal 4-wave forward at
-// d = 64 and 128): nwg, or per_cu per CU of the current device (the CU
+// d = 64 and 128, the causal 4-wave dQ kernel at d = 128, the 2-wave d = 64
+// dK/dV kernel): nwg, or per_cu per CU of the current device (the CU
 // count rounded down to a multiple of 8) when nwg is larger; the kernel then
 // takes its work items in rounds (fa_persistent_item).
 unsigned persistent_grid(long long nwg, int per_cu = 1);

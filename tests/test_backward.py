@@ -269,15 +269,18 @@ def test_backward_with_split_heads(api, case):
     check(api, w, (28, sum(case[:6])))
 
 
-@pytest.mark.parametrize("causal,n", [(True, 14600), (False, 7300)], ids=["causal_2061_items", "noncausal_1035_items"])
-def test_backward_persistent_dq_covers_every_row(api, causal, n):
+@pytest.mark.parametrize("B,Hq,Hkv,n,causal", [(1, 36, 9, 14600, True), (1, 36, 9, 7300, False), (8, 16, 16, 2048, True)],
+                         ids=["causal_2061_items", "noncausal_1035_items", "causal_4wave_2048_items"])
+def test_backward_persistent_dq_covers_every_row(api, B, Hq, Hkv, n, causal):
     """The dQ kernel of eight-wave d = 128 plans with more work items than CUs
-    runs as a persistent grid (one workgroup per CU, taking items in rounds).
-    At 2061 and 1035 items (not multiples of 8) dQ starts as NaN and must be
-    written everywhere.  Sampled rows of several heads match the oracle: a
-    row's dQ depends only on its own Q and dO rows and on the keys it sees, so
-    the oracle runs on that row and those keys alone."""
-    w = gen.workload(1, 36, 9, n, n, 128, causal=causal)
+    runs as a persistent grid (one workgroup per CU, taking items in rounds),
+    and so does the causal four-wave one up to 4096 rows, two workgroups per
+    CU.  At 2061 and 1035 items (not multiples of 8) and at 2048 four-wave
+    items dQ starts as NaN and must be written everywhere.  Sampled rows of
+    several heads match the oracle: a row's dQ depends only on its own Q and
+    dO rows and on the keys it sees, so the oracle runs on that row and those
+    keys alone."""
+    w = gen.workload(B, Hq, Hkv, n, n, 128, causal=causal)
     x = gen.make_inputs(w, (n, int(causal), 78))
     do_bits = gen.make_dout(w, (n, int(causal), 78))
     print(f"case: backward persistent dQ {w.name}", flush=True)
@@ -285,7 +288,7 @@ def test_backward_persistent_dq_covers_every_row(api, causal, n):
     do = to_device(do_bits, "bf16")
     o, lse = api.attention(q, k, v, causal=causal, scale=w.softmax_scale)
     dq = torch.full_like(q, float("nan"))
-    nbytes = api.bwd_workspace_size(1, 36, 9, n, n, 128, causal)
+    nbytes = api.bwd_workspace_size(B, Hq, Hkv, n, n, 128, causal)
     ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device="cuda")
     api.fa_bwd_dq(q, k, v, o, lse, do, dq, w.softmax_scale, causal, ws)
     torch.cuda.synchronize()
@@ -293,15 +296,16 @@ def test_backward_persistent_dq_covers_every_row(api, causal, n):
     dqf = out_to_f64(dq)
     rng = np.random.default_rng(n)
     got, ref = [], []
-    for h in (0, 13, 35):
-        hk = h // 4
+    b = B - 1
+    for h in (0, Hq // 3, Hq - 1):
+        hk = h // (Hq // Hkv)
         for i in [0, 63, 64, 255, 256, n // 2, n - 1] + [int(r) for r in rng.integers(0, n, 5)]:
             nk = i + 1 if causal else n
             rq, _, _ = attention_backward_fp64(
-                to_f64(x["q"][:, h:h + 1, i:i + 1], "bf16"), to_f64(x["k"][:, hk:hk + 1, :nk], "bf16"),
-                to_f64(x["v"][:, hk:hk + 1, :nk], "bf16"), to_f64(do_bits[:, h:h + 1, i:i + 1], "bf16"),
+                to_f64(x["q"][b:b + 1, h:h + 1, i:i + 1], "bf16"), to_f64(x["k"][b:b + 1, hk:hk + 1, :nk], "bf16"),
+                to_f64(x["v"][b:b + 1, hk:hk + 1, :nk], "bf16"), to_f64(do_bits[b:b + 1, h:h + 1, i:i + 1], "bf16"),
                 w.softmax_scale, False)
-            got.append(dqf[0, h, i])
+            got.append(dqf[b, h, i])
             ref.append(rq[0, 0, 0])
     compare_grad(np.array(got), np.array(ref), f"{w.name} dQ rows")
 
