@@ -558,6 +558,8 @@ FA_INST_DKDV_P(64, false, 4, 2)
 FA_INST_DKDV_P(64, true, 4, 2)
 FA_INST_DKDV_P(64, false, 2, 2)
 FA_INST_DKDV_P(64, true, 2, 2)
+FA_INST_DKDV_P(128, false, 4, 1)
+FA_INST_DKDV_P(128, true, 4, 1)
 #undef FA_INST_DKDV_P
 
 // ---------------------------------------------------------------- launchers
@@ -661,9 +663,10 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   // (d = 64, 128, 256; MHA and GQA; N 1024-4096); longer sequences and
   // partial second rounds keep one workgroup per item
   // workgroups per CU of the kernels with a persistent form: one for 8 waves
-  // at d = 128 (two waves per SIMD) and 4 waves at d = 256 and 64 (one wave
-  // per SIMD), two for 2 waves at d = 64
-  const int per_cu = ((d == 128 && pk.nw == 8) || (d == 256 && pk.nw == 4) || (d == 64 && pk.nw == 4)) ? 1
+  // at d = 128 (two waves per SIMD) and 4 waves at d = 128, 256 and 64 (one
+  // wave per SIMD), two for 2 waves at d = 64
+  const int per_cu = ((d == 128 && (pk.nw == 8 || pk.nw == 4)) || (d == 256 && pk.nw == 4) || (d == 64 && pk.nw == 4))
+                         ? 1
                      : (d == 64 && pk.nw == 2) ? 2 : 0;
   const unsigned grid = (per_cu > 0 && pk.Nq <= 4096) ? persistent_grid(pk.nwg, per_cu) : 0;
   if (grid > 0 && 2LL * grid <= pk.nwg) {
@@ -671,9 +674,12 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   hipLaunchKernelGGL((fa_bwd_dkdv_persistent_kernel<DD, CC, NN, KK>), dim3(grid), dim3(64 * NN), 0, stream,      \
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (const __bf16*)dout, ld, (__bf16*)dk, \
                      (__bf16*)dv, part, pk, c, scale)
-    if (d == 128) {
+    if (d == 128 && pk.nw == 8) {
       if (pk.causal) FA_DKDV_P(128, true, 8, 1);
       else FA_DKDV_P(128, false, 8, 1);
+    } else if (d == 128) {
+      if (pk.causal) FA_DKDV_P(128, true, 4, 1);
+      else FA_DKDV_P(128, false, 4, 1);
     } else if (d == 256) {
       if (pk.causal) FA_DKDV_P(256, true, 4, 1);
       else FA_DKDV_P(256, false, 4, 1);

@@ -312,12 +312,14 @@ def test_backward_persistent_dq_covers_every_row(api, B, Hq, Hkv, n, causal):
 
 @pytest.mark.parametrize("case", [(8, 32, 8, 2048, 128, True), (11, 28, 7, 1700, 128, False),
                                   (4, 16, 16, 2048, 256, True), (6, 16, 8, 1500, 256, False),
-                                  (4, 16, 16, 2048, 64, True), (2, 32, 8, 4096, 64, True)],
+                                  (4, 16, 16, 2048, 64, True), (2, 32, 8, 4096, 64, True),
+                                  (1, 32, 32, 2048, 128, True)],
                          ids=["d128_causal_512_items", "d128_noncausal_539_items", "d256_causal_1024_items",
-                              "d256_noncausal_576_items", "d64_causal_512_items", "d64_causal_2048_items_head_parts"])
+                              "d256_noncausal_576_items", "d64_causal_512_items", "d64_causal_2048_items_head_parts",
+                              "d128_4wave_causal_512_items"])
 def test_backward_persistent_dkdv_covers_every_key(api, case):
     """Up to 4096 query rows, the dK/dV kernels that fill a CU with one or two
-    workgroups (8 waves at d = 128, 4 at d = 256 and 64, 2 at d = 64) run as
+    workgroups (8 or 4 waves at d = 128, 4 at d = 256 and 64, 2 at d = 64) run as
     persistent grids when the plan has at least two key blocks per workgroup
     (here 512 to 2048 items, one count not a multiple of 8, one plan with the
     query heads split into parts); so do the dQ kernels at d = 128 and 256.
