@@ -3,8 +3,8 @@
 // probabilities from Q, K and the saved log-sum-exp instead of storing them.
 //
 // The pages report training speed-ups ("FlashAttention-4震撼发布",
-// FlashAttention-2 list; "FlashAttention (SV)", section "Prestanda och
-// fördelar") but print no backward algorithm.  What is computed is the
+// FlashAttention-2 list; "FlashAttention (SV)", section "Empiriska
+// resultat") but print no backward algorithm.  What is computed is the
 // derivative of the definition ("FlashAttention (SV)", section
 // "Problematik med standard-attention"), with P = softmax(scale Q K^T):
 //

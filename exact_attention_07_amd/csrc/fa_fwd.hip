@@ -50,6 +50,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -704,17 +705,23 @@ hipError_t launch_merge(const float* ows, const float* lws, void* o, float* lse,
 
 int queries_per_wave(int, int) { return 32; }
 
+// The CU count of each device, read once: 0 = not read yet, -1 = unknown.
+// Launching threads may race to fill an entry; each stores the same value,
+// and the atomic makes the race benign (no torn or stale-forever reads).
+static std::atomic<int> g_cus[64];
+
 unsigned persistent_grid(long long nwg, int per_cu) {
-  static int cus[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (unsigned)nwg;
-  if (cus[dev] == 0) {
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
-    cus[dev] = n >= 8 ? n / 8 * 8 : -1;
+    cus = n >= 8 ? n / 8 * 8 : -1;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
   }
-  const long long g = (long long)cus[dev] * per_cu;
-  return (cus[dev] > 0 && nwg > g) ? (unsigned)g : (unsigned)nwg;
+  const long long g = (long long)cus * per_cu;
+  return (cus > 0 && nwg > g) ? (unsigned)g : (unsigned)nwg;
 }
 
 // Workgroups of a bf16 forward launch: p.nwg, or a persistent grid for the

@@ -83,11 +83,16 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, void* stream);
 
 /*
- * float32 forward pass: q, k, v, o hold float32 values.  The kernel splits
- * every fp32 operand into a bf16 head and a bf16 tail (x = hi + lo, exact to
- * about 2^-16 relative) and forms each product from the three largest
- * partial products on bf16 MFMA, so scores and the output carry close to
- * fp32 accuracy.
+ * float32 forward pass: q, k, v, o hold float32 values.  The operation is
+ * fa_fwd's, the definition on "FlashAttention (SV)", section "Problematik
+ * med standard-attention", computed by the same tiled, fused, online-softmax
+ * method (sections "Tiling och blockbearbetning", "Online-beräkning av
+ * Softmax", "Sammanslagning av operationer"); only the operand precision
+ * differs.  The kernel splits every fp32 operand into a bf16 head and a bf16
+ * tail (x = hi + lo, exact to about 2^-16 relative) and forms each product
+ * from the three largest partial products on bf16 MFMA, so scores and the
+ * output carry close to fp32 accuracy.  Arguments, layouts, ownership and
+ * errors as for fa_fwd (16-byte aligned float32 tensors).
  */
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                      int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -153,8 +158,13 @@ fa_status fa_fp8_prepare(const void* q, const void* k, const void* v, void* q8, 
 
 /*
  * FP8 forward pass on the output of fa_fp8_prepare: O (bf16) and LSE (fp32)
- * of softmax(scale * Q K^T) V with Q, K, V represented by their codes and
- * scales.  Both products run on e4m3 MFMA with fp32 accumulation; the
+ * of softmax(scale * Q K^T) V ("FlashAttention (SV)", section "Problematik
+ * med standard-attention") with Q, K, V represented by their codes and
+ * scales, both products on 8-bit floating-point matrix instructions
+ * ("FlashAttention-3 — 闪电注意力-3", section on the Hopper GPU's new
+ * hardware features: FP8 at twice the FP16 rate; section on low precision
+ * and the reduction of quantisation error: Q and K rotated before
+ * quantisation, which leaves Q K^T unchanged).  Both products run on e4m3 MFMA with fp32 accumulation; the
  * probabilities multiply V as e4m3 values (unscaled, at most 2^8), while the
  * row sums and the LSE use the fp32 probabilities.  Conventions (GQA,
  * causal, errors) as for fa_fwd.
@@ -167,8 +177,8 @@ fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const floa
  * Backward pass (bfloat16): the gradients of L with respect to Q, K and V for
  * an upstream gradient dout = dL/dO of fa_fwd's output.  The pages report
  * the method's training speed-ups ("FlashAttention-4震撼发布",
- * FlashAttention-2 list; "FlashAttention (SV)", section "Prestanda och
- * fördelar") but print no backward algorithm; what is computed is the
+ * FlashAttention-2 list; "FlashAttention (SV)", section "Empiriska
+ * resultat") but print no backward algorithm; what is computed is the
  * derivative of the definition above, with P = softmax(scale Q K^T):
  *
  *     dV = P^T dO,   dP = dO V^T,   D_i = sum_c dO_ic O_ic,

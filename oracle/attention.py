@@ -21,8 +21,8 @@ Sources (the pages these functions restate):
     this for attention split over key ranges (each part keeps its own
     normalised output and log-sum-exp).
   * The pages report training results ("FlashAttention-4震撼发布",
-    FlashAttention-2 list; "FlashAttention (SV)", section "Prestanda och
-    fördelar") without a backward algorithm: attention_backward_fp64 is the
+    FlashAttention-2 list; "FlashAttention (SV)", section "Empiriska
+    resultat") without a backward algorithm: attention_backward_fp64 is the
     gradient of the definition above, written out.
 
 Layouts: q [B, Hq, Nq, d], k and v [B, Hkv, Nk, d]; outputs o [B, Hq, Nq, d]

@@ -420,3 +420,32 @@ def test_fp8_workload_sampled_rows(api):
     for rotate, r in report.items():
         check_lse_against_dequantised(*r["lse"], f"rotate={rotate}")
     assert report[True]["cos"] >= FP8_COSINE
+
+
+def test_fp8_workload_every_element(api):
+    """The fp8 workload's whole output, rotated and unrotated, against the
+    fp64 oracle on the unquantised bf16 source: cosine flattened over all
+    elements (the bar, for both runs), with RMSE and max |error| and the
+    unrotated/rotated RMSE ratio printed.  The oracle runs one (b, h) head per
+    task over the host's cores."""
+    from tests.full_compare import compare_all_heads, pool_size
+    w, x = gen.make_config(5)
+    print(f"case: {w.name} (every element, {pool_size()} host workers)", flush=True)
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    signs = torch.from_numpy(x["signs"]).cuda()
+    outs = {}
+    for rotate in (True, False):
+        o, lse, prep = api.attention_fp8(q, k, v, causal=False, scale=w.softmax_scale,
+                                         signs=signs if rotate else None)
+        torch.cuda.synchronize()
+        outs["rotated" if rotate else "unrotated"] = (o.view(torch.int16).cpu().numpy().view(np.uint16), None)
+        del o, lse, prep
+    del q, k, v
+    st = compare_all_heads(x["q"], x["k"], x["v"], w.softmax_scale, False, outs)
+    for nm, r in st.items():
+        print(f"fp8 {nm}: cosine {r['cosine']:.6f} rmse {r['rmse']:.4e} max|err| {r['max_abs']:.4e} "
+              f"mean|err| {r['mean_abs']:.4e} over {r['n']} elements", flush=True)
+    print(f"rmse ratio unrotated/rotated: {st['unrotated']['rmse'] / st['rotated']['rmse']:.4f}", flush=True)
+    for nm, r in st.items():
+        assert r["nonfinite"] == 0, nm
+        assert r["cosine"] >= FP8_COSINE, (nm, r)

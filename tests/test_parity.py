@@ -1,15 +1,16 @@
 """GPU parity: libfa.so (through its C ABI) against the fp64 oracle.
 
-Small and ragged shapes are compared element by element in full; the large
-standing workloads are compared on sampled rows the oracle computes one by
-one, in the launch configuration the benchmark uses.
+Small and ragged shapes are compared element by element in full.  The large
+standing workloads are compared in full too, in the launch configuration the
+benchmark uses, with the oracle computed one (b, h) head at a time over a
+pool of host processes; a quicker check on sampled rows is kept beside it.
 """
 import numpy as np
 import pytest
 
 from exact_attention_07_amd import gen
 from oracle import attention_fp64, attention_rows_fp64
-from tests.gpu_util import compare, out_to_f64, to_device, to_f64
+from tests.gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, LSE_ABS, compare, out_to_f64, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -73,6 +74,29 @@ def test_large_workloads_sampled(api, cfg):
     got_l = np.array([lse[b, h, i] for b, h, i in rows])
     compare(got_o, got_l, o_ref, lse_ref, what=w.name)
     assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("cfg", [3, 4])
+def test_large_workloads_every_element(api, cfg):
+    """The whole output of the standing workload against the oracle: max and
+    mean |dO| over all elements and max |dLSE| over all rows, with the oracle
+    computed one (b, h) head per task over the host's cores."""
+    from tests.full_compare import compare_all_heads, pool_size
+    w, x = gen.make_config(cfg)
+    print(f"case: {w.name} (every element, {pool_size()} host workers)", flush=True)
+    q, k, v = (to_device(x[t], w.dtype) for t in "qkv")
+    o, lse = api.attention(q, k, v, causal=w.causal, scale=w.softmax_scale)
+    torch.cuda.synchronize()
+    o_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    lse_h = lse.cpu().numpy()
+    del q, k, v, o, lse
+    st = compare_all_heads(x["q"], x["k"], x["v"], w.softmax_scale, w.causal, {"o": (o_bits, lse_h)})["o"]
+    print(f"{w.name}: max|dO| {st['max_abs']:.3e} mean|dO| {st['mean_abs']:.3e} rmse {st['rmse']:.3e} "
+          f"max|dLSE| {st['lse_max_abs']:.3e} over {st['n']} elements", flush=True)
+    assert st["nonfinite"] == 0 and st["lse_inf_mismatch"] == 0
+    assert st["max_abs"] <= BF16_MAX_ABS, st
+    assert st["mean_abs"] <= BF16_MEAN_ABS, st
+    assert st["lse_max_abs"] <= LSE_ABS, st
 
 
 # ---------------------------------------------------------------- ragged shapes and edge cases
@@ -227,3 +251,47 @@ def test_persistent_grid_covers_every_row(api, case):
     o_ref, lse_ref = attention_rows_fp64(qf, kf, vf, w.softmax_scale, causal, rows)
     compare(np.stack([of[b, h, i] for b, h, i in rows]), np.array([lf[b, h, i] for b, h, i in rows]),
             o_ref, lse_ref, what=w.name)
+
+
+def test_concurrent_host_threads_on_separate_streams(api):
+    """Several host threads call fa_fwd at once, each on its own stream, on
+    shapes that take persistent and one-item grids (the library keeps a
+    per-device CU-count cache that every launch reads); every result matches
+    the oracle."""
+    import threading
+    cases = [gen.workload(2, 8, 2, 640, 640, 128, causal=True),
+             gen.workload(1, 4, 4, 512, 700, 256),
+             gen.workload(2, 6, 3, 300, 300, 64, causal=True),
+             gen.workload(1, 16, 4, 1024, 1024, 128, causal=True),
+             gen.workload(3, 4, 1, 200, 520, 128)]
+    xs = [gen.make_inputs(w, (77, i)) for i, w in enumerate(cases)]
+    results, errors = [None] * len(cases), []
+    start = threading.Barrier(len(cases))
+
+    def work(i):
+        try:
+            w, x = cases[i], xs[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+                o = torch.empty_like(q)
+                lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+            s.synchronize()
+            start.wait(timeout=60)
+            for _ in range(4):
+                api.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, s)
+            s.synchronize()
+            results[i] = (out_to_f64(o), lse.cpu().numpy().astype(np.float64))
+        except Exception as e:  # noqa: BLE001
+            errors.append((i, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=90)
+    assert not errors, errors
+    for (w, x), (o, lse) in zip(zip(cases, xs), results):
+        q, k, v = (to_f64(x[t], "bf16") for t in "qkv")
+        o_ref, lse_ref = attention_fp64(q, k, v, w.softmax_scale, w.causal)
+        compare(o, lse, o_ref, lse_ref, what=w.name)
