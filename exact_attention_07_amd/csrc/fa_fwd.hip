@@ -394,7 +394,15 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
-  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
+  // lsum: row sum of the fp32 probabilities (the LSE).  At d = 256 also
+  // lsumq, the row sum of the bf16-rounded probabilities that multiply V,
+  // which normalises O: O is then a convex combination of V rows with
+  // exactly the weights applied, without the error (rounding of P) x |V| that
+  // dominates rows with one or two heavy keys.  It costs one dot2 per pair of
+  // probabilities: measured +1 % at d = 256, +4.6 % at d = 128, where O is
+  // normalised by lsum (see the error bound where the tolerance is stated).
+  constexpr bool QSUM = D == 256;
+  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f, lsumq = 0.f;
 
   // A range without key tiles (causal rows that see no key, or a key range
   // past every visible key of the workgroup's rows; uniform over the
@@ -449,13 +457,18 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
   for (int ps = 0; ps < PS; ++ps) pb.v[ps] = (u32x4){0u, 0u, 0u, 0u};
 
   // score sc = (kb, i) of s: exponential against mu, row-sum part, packed
-  // into the P dword of its pair (the odd member of a pair writes it)
-  auto score = [&](const Scores<D>& s, Probs& pf, int sc, float mu, float& part0, float& part1, float& even) {
+  // into the P dword of its pair (the odd member of a pair writes it and,
+  // with QSUM, adds the pair's two bf16 values to the rounded row sum)
+  const bf16x2 ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+  auto score = [&](const Scores<D>& s, Probs& pf, int sc, float mu, float& part0, float& part1, float& even,
+                   float& partq) {
     const int skb = sc / 16, si = sc % 16;
     const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s.v[skb][0][si], c, -mu));
     if (sc & 1) {
       part1 += pv;
-      pf.v[skb * 2 + si / 8][(si % 8) / 2] = pack_bf16(even, pv);
+      const unsigned pk = pack_bf16(even, pv);
+      pf.v[skb * 2 + si / 8][(si % 8) / 2] = pk;
+      if constexpr (QSUM) partq = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones2, partq, false);
     } else {
       part0 += pv;
       even = pv;
@@ -481,7 +494,7 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
     if (j0 + BC - 1 > kfull_w) mask_scores<D, CAUSAL>(s, j0, q_l, Nq, Nk, kend, lane);
 
     float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-    float part0 = 0.f, part1 = 0.f, even = 0.f;
+    float part0 = 0.f, part1 = 0.f, even = 0.f, partq = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sn.v[kb][0] = (f32x16){};
 #pragma unroll
@@ -500,7 +513,7 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
       }
       // scores [ch * NSC / NCH, (ch + 1) * NSC / NCH)
 #pragma unroll
-      for (int sc = ch * NSC / NCH; sc < (ch + 1) * NSC / NCH; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      for (int sc = ch * NSC / NCH; sc < (ch + 1) * NSC / NCH; ++sc) score(s, pf, sc, mu, part0, part1, even, partq);
       // copy instructions [ch * NCP / NCH, (ch + 1) * NCP / NCH): all NCP of them
 #pragma unroll
       for (int i = ch * NCP / NCH; i < (ch + 1) * NCP / NCH; ++i) copy_one(j, par, i);
@@ -524,17 +537,19 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
       if (__ballot(m_run > m_ref + TAU)) {
         const float alpha = (m_run == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_run);
         lsum *= alpha;
+        lsumq *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         m_ref = m_run;
       }
       mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-      part0 = part1 = 0.f;
+      part0 = part1 = partq = 0.f;
 #pragma unroll
-      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even, partq);
       part = part0 + part1;
     }
     lsum += part;
+    lsumq += partq;
   };
 
   // one code path for every iteration a wave takes part in (j <= ntw);
@@ -582,7 +597,8 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
   // range's partial result (fp32) goes to the workspace for the merge
   if (!live) return;
   const float lt = xhalf_sum(lsum);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  const float ltq = QSUM ? xhalf_sum(lsumq) : lt;
+  const float inv = ltq > 0.f ? 1.0f / ltq : 0.f;
   if (!valid_l) return;
   const float lse_row = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
   if (p.nsplit > 1) {

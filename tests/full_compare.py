@@ -110,3 +110,73 @@ def compare_all_heads(q, k, v, scale: float, causal: bool, outputs, workers: int
             agg["lse_inf_mismatch"] = sum(s["lse_inf_mismatch"] for s in sts)
         out[nm] = agg
     return out
+
+
+def _stats(o, r):
+    e = o - r
+    return np.array([(o * r).sum(), (o * o).sum(), (r * r).sum(), (e * e).sum(), np.abs(e).sum(), np.abs(e).max(),
+                     float((~np.isfinite(o)).sum())])
+
+
+def _fp8_head_task(args):
+    """Oracle on the unquantised source and on the dequantised codes of each
+    run, for one head; statistics of each run's GPU output against both, and
+    of the dequantised oracle against the source oracle."""
+    from oracle import attention_fp64
+    from oracle.formats import e4m3_decode
+    q, k, v, scale, runs = args
+    o_true, _ = attention_fp64(_decode(q)[None, None], _decode(k)[None, None], _decode(v)[None, None], scale, False)
+    o_true = o_true[0, 0]
+    res = []
+    for o_gpu, q8, k8, v8, sc in runs:
+        qq, kk, vv = (e4m3_decode(c) * s for c, s in zip((q8, k8, v8), sc))
+        o_deq, _ = attention_fp64(qq[None, None], kk[None, None], vv[None, None], scale, False)
+        o_deq = o_deq[0, 0]
+        o = _decode(o_gpu)
+        res.append({"gpu_true": _stats(o, o_true), "gpu_deq": _stats(o, o_deq), "deq_true": _stats(o_deq, o_true)})
+    return res
+
+
+def _agg(rows, n):
+    t = sum(rows)
+    return {"cosine": float(t[0] / math.sqrt(t[1] * t[2])) if t[1] > 0 and t[2] > 0 else float("nan"),
+            "rmse": math.sqrt(t[3] / n), "mean_abs": float(t[4] / n), "max_abs": float(max(r[5] for r in rows)),
+            "nonfinite": int(t[6]), "n": n}
+
+
+def compare_fp8_all_heads(q, k, v, scale: float, runs, workers: int | None = None):
+    """Non-causal fp8 attention outputs against the fp64 oracle on every element.
+
+    q, k, v: the bf16 source (uint16 bit patterns), [B, H, N, d] (MHA).
+    runs: {name: (o [B, H, N, d] bf16 bits, q8, k8, v8 (e4m3 codes; v8 in
+    [B, Hkv, Nk, d] key order), (s_q, s_k, s_v))}.
+    Returns {name: {"gpu_true", "gpu_deq", "deq_true"}}, each with cosine,
+    rmse, mean_abs, max_abs over all elements: the GPU output against the
+    oracle on the source (the accuracy of the fp8 path), against the oracle on
+    the dequantised codes (the kernel's own error), and the dequantised oracle
+    against the source oracle (the error of the format alone).
+    """
+    B, H = q.shape[:2]
+    Hkv = k.shape[1]
+    g = H // Hkv
+    names = list(runs)
+    tasks = []
+    for b in range(B):
+        for h in range(H):
+            hk = h // g
+            rr = []
+            for nm in names:
+                o, q8, k8, v8, sc = runs[nm]
+                rr.append((np.ascontiguousarray(o[b, h]), np.ascontiguousarray(q8[b, h]),
+                           np.ascontiguousarray(k8[b, hk]), np.ascontiguousarray(v8[b, hk]), tuple(map(float, sc))))
+            tasks.append((np.ascontiguousarray(q[b, h]), np.ascontiguousarray(k[b, hk]), np.ascontiguousarray(v[b, hk]),
+                          scale, rr))
+    workers = workers or pool_size()
+    if workers == 1:
+        per_head = [_fp8_head_task(t) for t in tasks]
+    else:
+        with mp.get_context("spawn").Pool(workers, initializer=_init_worker) as pool:
+            per_head = pool.map(_fp8_head_task, tasks, chunksize=1)
+    n = q[..., 0].size * runs[names[0]][0].shape[-1]
+    return {nm: {key: _agg([ph[i][key] for ph in per_head], n) for key in ("gpu_true", "gpu_deq", "deq_true")}
+            for i, nm in enumerate(names)}
