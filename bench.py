@@ -13,11 +13,18 @@ on the stream the kernels run on.  Prints one JSON line on stdout
 
   value     attention forward TFLOP/s = 4*B*Hq*Nq*Nk*d (halved when causal) / step time
   roofline  the attention kernel (its own launch time, from events around
-            each launch) against the MI355X dense MFMA peak for its dtype, and
-            the HBM traffic measured by rocprofv3 counters for the same kernel
-            source (null when the source changed since the counters were taken)
+            each launch: mean, median and min over the K launches) against
+            the MI355X dense MFMA peak for its dtype; the HBM traffic, the
+            sustained clock and the MFMA-busy share measured by rocprofv3
+            counters on the same kernel source (profiles/counters_config<N>.txt;
+            omitted or null when the source changed since they were taken),
+            with the fraction of the peak at that clock; and the measured MFMA
+            ceiling (fa_mfma_ceiling, a loop of the same matrix instruction on
+            toggling operands, timed right after the steps) with the fraction
+            of it reached
   cpu_baseline  the fp64 oracle timed on this host's cores over a bounded
-            sample of the same workload (whole heads), as a reported baseline
+            sample of the same workload (whole (b, h) heads, one per task over
+            a pool of processes), with the CPU model, as a reported baseline
 
 --config backward measures the backward pass (fa_bwd_dq then fa_bwd_dkdv:
 dQ, dK, dV for a seeded upstream gradient dO, probabilities recomputed from
@@ -36,7 +43,6 @@ once) against the 8 TB/s of HBM3E; the step includes the merge kernel.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -47,38 +53,31 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from exact_attention_07_amd import profsum  # noqa: E402  (reads profiler summaries; no GPU, no oracle)
+
 METRIC = "attention fwd TFLOP/s + % of MFMA peak (bf16, causal GQA, N=8K, d=128)"
 # MI355X published dense peaks (no sparsity), TFLOP/s
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0, "fp8": 5000.0}
-# sources of the attention kernel of each dtype (the traffic summary is valid
-# only for the sources it was measured on)
-_CSRC = "exact_attention_07_amd/csrc/"
-KERNEL_SOURCES = {
-    "bf16": [_CSRC + f for f in ("fa_fwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
-    "f32": [_CSRC + f for f in ("fa_fwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
-    "fp8": [_CSRC + f for f in ("fa_fwd_fp8.hip", "fa_device.h", "plan.h")],
-    "bwd": [_CSRC + f for f in ("fa_bwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
-}
-KERNEL_NAME = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel",
-               "bwd": "fa_bwd_dkdv_kernel"}
+NOMINAL_CLOCK_GHZ = 2.4  # the clock the published peaks assume
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(dtype: str) -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES[dtype]:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def load_counters(config):
+    """The committed rocprofv3 counter summary of this workload's attention
+    kernel (profiles/counters_config<N>.txt, counters_decode.txt,
+    counters_backward.txt), if taken on the current kernel sources; else None."""
+    return profsum.load(config, ROOT)
 
 
-def load_traffic(tag: str, dtype: str):
-    """HBM bytes per launch of the measured kernel from the committed
-    rocprofv3 counter summary profiles/traffic_<tag>.txt, if it was taken on
-    the current kernel source."""
+def load_traffic(tag: str, dtype: str, counters=None):
+    """HBM bytes per launch of the measured kernel: from the counter summary
+    of the workload, or from profiles/traffic_<tag>.txt, if taken on the
+    current kernel sources; else None."""
+    if counters and "hbm_bytes_per_launch" in counters:
+        return float(counters["hbm_bytes_per_launch"])
     path = os.path.join(ROOT, "profiles", f"traffic_{tag}.txt")
     if not os.path.exists(path):
         return None
@@ -87,7 +86,7 @@ def load_traffic(tag: str, dtype: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != source_hash(dtype):
+    if fields.get("kernel_source_sha256") != profsum.source_hash(dtype):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -95,63 +94,79 @@ def load_traffic(tag: str, dtype: str):
         return None
 
 
-def cpu_baseline(w, x, budget_s: float):
-    """Time the fp64 oracle on whole (b, h) heads of the workload until budget_s elapsed."""
-    from oracle import attention_fp64
-    from oracle.formats import bf16_bits_to_f64
+def cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
-    g = w.Hq // w.Hkv
-    done, flops, t_total = 0, 0.0, 0.0
-    heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    for b, h in heads:
-        q = bf16_bits_to_f64(x["q"][b:b + 1, h:h + 1])
-        k = bf16_bits_to_f64(x["k"][b:b + 1, h // g:h // g + 1])
-        v = bf16_bits_to_f64(x["v"][b:b + 1, h // g:h // g + 1])
-        t0 = time.perf_counter()
-        attention_fp64(q, k, v, w.softmax_scale, w.causal)
-        t_total += time.perf_counter() - t0
-        done += 1
-        f = 4.0 * w.Nq * w.Nk * w.d
-        flops += f / 2 if w.causal else f
-        if t_total >= budget_s:
-            break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, fp64 two-pass oracle "
-                      f"(S and P materialised), {t_total:.1f} s"}
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
-def cpu_baseline_backward(w, x, dout, budget_s: float):
-    """Time the fp64 gradient oracle on whole (b, h) heads until budget_s elapsed."""
-    from oracle import attention_backward_fp64
-    from oracle.formats import bf16_bits_to_f64
+def host_cores() -> int:
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _pool_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
     except Exception:  # noqa: BLE001
-        threads = os.cpu_count() or 1
+        pass
+
+
+def _oracle_head(args):
+    """One (b, h) head of the fp64 oracle (forward, or its gradient when dO is given)."""
+    import time as _t
+    from oracle import attention_backward_fp64, attention_fp64
+    from oracle.formats import bf16_bits_to_f64
+    q, k, v, do, scale, causal = args
+    q, k, v = (bf16_bits_to_f64(a)[None, None] for a in (q, k, v))
+    t0 = _t.perf_counter()
+    if do is None:
+        attention_fp64(q, k, v, scale, causal)
+    else:
+        attention_backward_fp64(q, k, v, bf16_bits_to_f64(do)[None, None], scale, causal)
+    return _t.perf_counter() - t0
+
+
+def cpu_baseline_pool(w, x, budget_s: float, dout=None):
+    """The fp64 oracle timed on this host: whole (b, h) heads of the workload,
+    one per task over a pool of host processes (one BLAS thread each), until
+    budget_s of wall time has passed; value = oracle flops of the finished
+    heads / wall time."""
+    import multiprocessing as mp
+    cores = host_cores()
     g = w.Hq // w.Hkv
-    done, flops, t_total = 0, 0.0, 0.0
     heads = [(b, h) for b in range(w.B) for h in range(w.Hq)]
-    for b, h in heads:
-        q = bf16_bits_to_f64(x["q"][b:b + 1, h:h + 1])
-        k = bf16_bits_to_f64(x["k"][b:b + 1, h // g:h // g + 1])
-        v = bf16_bits_to_f64(x["v"][b:b + 1, h // g:h // g + 1])
-        do = bf16_bits_to_f64(dout[b:b + 1, h:h + 1])
+    per_head = (10.0 if dout is not None else 4.0) * w.Nq * w.Nk * w.d / (2 if w.causal else 1)
+    tasks = [(x["q"][b, h], x["k"][b, h // g], x["v"][b, h // g], None if dout is None else dout[b, h],
+              w.softmax_scale, w.causal) for b, h in heads]
+    pool = mp.get_context("spawn").Pool(cores, initializer=_pool_init)
+    try:
+        pool.map(abs, range(cores))  # workers started before the clock runs
         t0 = time.perf_counter()
-        attention_backward_fp64(q, k, v, do, w.softmax_scale, w.causal)
-        t_total += time.perf_counter() - t0
-        done += 1
-        f = 10.0 * w.Nq * w.Nk * w.d
-        flops += f / 2 if w.causal else f
-        if t_total >= budget_s:
-            break
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, fp64 gradient oracle "
-                      f"(P, dP, dS materialised), {t_total:.1f} s"}
+        done, t_last = 0, t0
+        for _ in pool.imap_unordered(_oracle_head, tasks):
+            done += 1
+            t_last = time.perf_counter()
+            if t_last - t0 >= budget_s:
+                break
+    finally:
+        pool.terminate()
+        pool.join()
+    wall = t_last - t0
+    what = "fp64 gradient oracle (P, dP, dS materialised)" if dout is not None else \
+        "fp64 two-pass oracle (S and P materialised)"
+    return {"value": done * per_head / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, {what}, one head per task on "
+                      f"{cores} processes with one BLAS thread each, {wall:.1f} s wall"}
 
 
 def bench_backward(args, torch, api, gen):
@@ -233,7 +248,7 @@ def bench_backward(args, torch, api, gen):
         log(f"check dQ of head ({b_},{h_}): rms err / rms ref = "
             f"{np.sqrt((err ** 2).mean()) / np.sqrt((rq ** 2).mean()):.2e}")
 
-    traffic = load_traffic("backward", "bwd")
+    traffic = load_traffic("backward", "bwd", load_counters("backward"))
     line = {
         "metric": "attention bwd TFLOP/s + % of MFMA peak (bf16, causal GQA, N=8K, d=128)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -241,7 +256,7 @@ def bench_backward(args, torch, api, gen):
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q, K, V, dO; O and LSE from fa_fwd; resident in HBM before timing)",
         "config": {"workload": "backward of " + w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk,
-                   "d": w.d, "causal": w.causal, "kernel": KERNEL_NAME["bwd"],
+                   "d": w.d, "causal": w.causal, "kernel": "fa_bwd_dkdv_kernel",
                    "steps_in_a_step": "fa_bwd_dq (dQ, D, LSE log2 e) + fa_bwd_dkdv (dK, dV)"},
         "roofline": {"bound": "mfma", "achieved": round(dkdv_tflops, 2), "peak": PEAK_TFLOPS["bf16"],
                      "unit": "TFLOP/s", "frac": round(dkdv_tflops / PEAK_TFLOPS["bf16"], 4), "traffic": traffic,
@@ -250,8 +265,42 @@ def bench_backward(args, torch, api, gen):
                       "algorithmic_tflops": round(0.5 * fwd_flops / (dq_ms * 1e-3) / 1e12, 2)},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_backward(w, x, dout, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline_pool(w, x, args.cpu_budget, dout)
     print(json.dumps(line), flush=True)
+
+
+def measured_ceiling(torch, api, fp8: bool, stream, span_ms: float):
+    """Time the MFMA-only loop (fa_mfma_ceiling: the attention kernels' matrix
+    instruction, two waves per SIMD, operands toggling like random data) for
+    about as long as the attention launches ran, right after them: the rate
+    the chip sustains for pure matrix work at that moment."""
+    out = torch.empty(api.mfma_ceiling_out_bytes() // 4, dtype=torch.float32, device="cuda")
+    iters = 250 if fp8 else 500
+    for _ in range(3):
+        api.mfma_ceiling(out, fp8, iters, True, stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 4
+    a.record(stream)
+    for _ in range(n):
+        api.mfma_ceiling(out, fp8, iters, True, stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    one = a.elapsed_time(b) / n
+    n = max(10, int(span_ms / max(one, 1e-3)))
+    launches = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in launches:
+        a.record(stream)
+        api.mfma_ceiling(out, fp8, iters, True, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = float(np.median([a.elapsed_time(b) for a, b in launches]))
+    tf = api.mfma_ceiling_flops(fp8, iters) / (t * 1e-3) / 1e12
+    log(f"measured MFMA ceiling ({'fp8' if fp8 else 'bf16'}, random operands): {tf:.1f} TFLOP/s "
+        f"({n} launches of {t:.3f} ms)")
+    return {"tflops": round(tf, 1),
+            "what": f"fa_mfma_ceiling: {'v_mfma_f32_32x32x64_f8f6f4' if fp8 else 'v_mfma_f32_32x32x16_bf16'} only, "
+                    f"two waves per SIMD, toggling operands, median of {n} launches right after the timed steps"}
 
 
 def main():
@@ -263,6 +312,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--check", action="store_true", help="compare sampled rows with the oracle (stderr)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the measured MFMA ceiling (profiling runs)")
+    ap.add_argument("--no-compare", action="store_true",
+                    help="decode: skip the comparison run without the key split (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -348,7 +400,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
-    kernel_ms = sum(a.elapsed_time(b) for a, b in marks) / args.steps
+    launch_ms = [a.elapsed_time(b) for a, b in marks]
+    kernel_ms = sum(launch_ms) / args.steps
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     kernel_tflops = flops / (kernel_ms * 1e-3) / 1e12
@@ -375,7 +428,7 @@ def main():
         lerr = max(abs(float(ll[b, h, i]) - l_ref[r]) for r, (b, h, i) in enumerate(rows))
         log(f"check on {len(rows)} rows: max|O err|={err:.2e} max|LSE err|={lerr:.2e}")
 
-    if decode:
+    if decode and not args.no_compare:
         # the same step without the split, for comparison (stderr)
         for _ in range(3):
             api.fa_fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
@@ -386,6 +439,7 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         log(f"without the key split (fa_fwd): {a.elapsed_time(b) / args.steps:.4f} ms/step")
+    if decode:
         nbytes = 2 * (q.numel() + k.numel() + v.numel() + o.numel()) + 4 * lse.numel()
         gbs = nbytes / (ms * 1e-3) / 1e9
         log(f"key split: {ws_bytes / 4 / (w.B * w.Hq * w.Nq * (w.d + 1)):.0f} ranges, {gbs:.0f} GB/s")
@@ -400,14 +454,17 @@ def main():
             # over the key ranges + the merge, one library call); traffic: HBM
             # bytes of the attention kernel (rocprofv3 counters)
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": 8000.0, "unit": "GB/s",
-                         "frac": round(gbs / 8000.0, 4), "traffic": load_traffic("decode", "bf16"),
+                         "frac": round(gbs / 8000.0, 4), "traffic": load_traffic("decode", "bf16", load_counters("decode")),
                          "step_ms": round(ms, 5), "call_ms": round(kernel_ms, 5), "tflops": round(tflops, 2)},
         }
         print(json.dumps(line), flush=True)
         return
 
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = load_traffic(f"config{args.config}", w.dtype)
+    counters = load_counters(args.config)
+    traffic = load_traffic(f"config{args.config}", w.dtype, counters)
+    ceiling = None if args.no_ceiling else measured_ceiling(torch, api, w.dtype == "fp8", stream,
+                                                            args.steps * kernel_ms)
     data = "synthetic (seeded N(0,1), generated on the host, resident in HBM before timing)"
     if w.dtype == "fp8":
         data = ("synthetic (seeded N(0,1) bf16, Q and K with +-50 outliers at p=0.001; quantised to e4m3 "
@@ -426,16 +483,32 @@ def main():
         "dtype": w.dtype,
         "data": data,
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
-                   "causal": w.causal, "kernel": KERNEL_NAME[w.dtype]},
+                   "causal": w.causal, "kernel": {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel"}[w.dtype]},
         "roofline": {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(kernel_tflops / peak, 4), "traffic": traffic,
-                     "kernel_ms": round(kernel_ms, 5)},
+                     "kernel_ms": round(kernel_ms, 5),
+                     "kernel_ms_median": round(float(np.median(launch_ms)), 5),
+                     "kernel_ms_min": round(float(np.min(launch_ms)), 5), "launches": len(launch_ms)},
     }
+    if counters:
+        # the same kernel under rocprofv3 counters: the clock it sustains and
+        # the share of SIMD cycles its matrix pipe was busy
+        clk = float(counters.get("sustained_clock_ghz", "nan"))
+        peak_clk = peak * clk / NOMINAL_CLOCK_GHZ
+        line["roofline"].update({
+            "sustained_clock_ghz": round(clk, 4), "mfma_busy": float(counters.get("mfma_busy", "nan")),
+            "peak_at_sustained_clock": round(peak_clk, 1),
+            "frac_at_sustained_clock": round(kernel_tflops / peak_clk, 4),
+            "counters": "profiles/" + profsum.summary_name(args.config)})
+    if ceiling:
+        line["roofline"].update({"measured_mfma_ceiling": ceiling["tflops"],
+                                 "frac_of_measured_ceiling": round(kernel_tflops / ceiling["tflops"], 4),
+                                 "ceiling_measurement": ceiling["what"]})
     if w.dtype == "fp8":
         line["config"]["steps_in_a_step"] = "fa_fp8_prepare (rotation, scales, e4m3) + fa_fwd_fp8"
         line["prepare_ms"] = round(ms - kernel_ms, 5)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+        line["cpu_baseline"] = cpu_baseline_pool(w, x, args.cpu_budget)
     print(json.dumps(line), flush=True)
 
 

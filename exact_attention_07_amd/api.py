@@ -56,6 +56,12 @@ def lib() -> ctypes.CDLL:
     L.fa_bwd_dkdv.restype = ctypes.c_int
     L.fa_bwd_workspace_size.argtypes = [i] * 7
     L.fa_bwd_workspace_size.restype = ctypes.c_size_t
+    L.fa_mfma_ceiling_out_bytes.argtypes = []
+    L.fa_mfma_ceiling_out_bytes.restype = ctypes.c_size_t
+    L.fa_mfma_ceiling_flops.argtypes = [i, i]
+    L.fa_mfma_ceiling_flops.restype = ctypes.c_double
+    L.fa_mfma_ceiling.argtypes = [vp, ctypes.c_size_t, i, i, i, vp]
+    L.fa_mfma_ceiling.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_abi_version.argtypes = []
@@ -304,3 +310,22 @@ def attention_backward(q, k, v, o, lse, do, causal: bool = False, scale: float |
     ws = torch.empty((nbytes + 15) // 16 * 4, dtype=torch.float32, device=q.device)
     fa_bwd(q, k, v, o, lse, do, dq, dk, dv, scale, causal, ws, stream)
     return dq, dk, dv
+
+
+def mfma_ceiling_out_bytes() -> int:
+    """Bytes of device memory fa_mfma_ceiling's `out` must hold."""
+    return int(lib().fa_mfma_ceiling_out_bytes())
+
+
+def mfma_ceiling_flops(fp8: bool, iters: int) -> float:
+    """Matrix flops of one fa_mfma_ceiling launch."""
+    return float(lib().fa_mfma_ceiling_flops(int(bool(fp8)), int(iters)))
+
+
+def mfma_ceiling(out, fp8: bool, iters: int, random: bool = True, stream=None) -> None:
+    """Enqueue the MFMA-only loop (the measured ceiling) into `out` (a float32 GPU tensor)."""
+    import torch
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 GPU tensor")
+    _check(lib().fa_mfma_ceiling(_ptr(out), out.numel() * 4, int(bool(fp8)), int(iters), int(bool(random)),
+                                 _stream(stream)), "fa_mfma_ceiling")

@@ -360,4 +360,17 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
   return bwd_dkdv(q, k, v, dout, dk, dv, B, Hq, Hkv, Nq, Nk, d, scale, causal, workspace, workspace_bytes, stream);
 }
 
+size_t fa_mfma_ceiling_out_bytes(void) { return (size_t)fa::mfma_ceiling_workgroups() * 256 * sizeof(float); }
+
+double fa_mfma_ceiling_flops(int fp8, int iters) { return iters < 1 ? 0.0 : fa::mfma_ceiling_flops(fp8 != 0, iters); }
+
+fa_status fa_mfma_ceiling(float* out, size_t out_bytes, int fp8, int iters, int random, void* stream) {
+  if (!out) return FA_ERR_NULL;
+  if ((fp8 != 0 && fp8 != 1) || (random != 0 && random != 1)) return FA_ERR_FLAG;
+  if (iters < 1) return FA_ERR_SHAPE;
+  if (!aligned4(out) || out_bytes < fa_mfma_ceiling_out_bytes()) return FA_ERR_WORKSPACE;
+  const hipError_t e = fa::launch_mfma_ceiling(out, fp8, iters, random, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

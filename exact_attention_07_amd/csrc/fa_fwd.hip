@@ -726,9 +726,9 @@ int queries_per_wave(int, int) { return 32; }
 // and the atomic makes the race benign (no torn or stale-forever reads).
 static std::atomic<int> g_cus[64];
 
-unsigned persistent_grid(long long nwg, int per_cu) {
+int cu_count() {
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return (unsigned)nwg;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   int cus = g_cus[dev].load(std::memory_order_relaxed);
   if (cus == 0) {
     int n = 0;
@@ -736,6 +736,11 @@ unsigned persistent_grid(long long nwg, int per_cu) {
     cus = n >= 8 ? n / 8 * 8 : -1;
     g_cus[dev].store(cus, std::memory_order_relaxed);
   }
+  return cus > 0 ? cus : 0;
+}
+
+unsigned persistent_grid(long long nwg, int per_cu) {
+  const int cus = cu_count();
   const long long g = (long long)cus * per_cu;
   return (cus > 0 && nwg > g) ? (unsigned)g : (unsigned)nwg;
 }

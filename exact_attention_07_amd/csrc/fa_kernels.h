@@ -20,6 +20,19 @@ int queries_per_wave(int d, int f32);
 // takes its work items in rounds (fa_persistent_item).
 unsigned persistent_grid(long long nwg, int per_cu = 1);
 
+// CUs of the current device, rounded down to a multiple of 8 (one per XCD
+// share); 0 if the runtime cannot say.  Read once per device.
+int cu_count();
+
+// The measured MFMA ceiling (fa_ceiling.hip): workgroups of the loop kernel
+// (two per CU, four waves each), its matrix flops for `iters` rounds, and
+// the launch (fp8: the e4m3 instruction; random: operands that change from
+// instruction to instruction, else constant).  out: one float per thread,
+// mfma_ceiling_workgroups() * 256 of them.
+unsigned mfma_ceiling_workgroups();
+double mfma_ceiling_flops(int fp8, int iters);
+hipError_t launch_mfma_ceiling(float* out, int fp8, int iters, int random, hipStream_t stream);
+
 // Enqueue the forward kernel.  c = scale * log2(e).  f32 selects fp32
 // operands (split into bf16 hi/lo parts inside the kernel).  With a key
 // split (p.nsplit > 1, bf16 only) the kernel writes the partial results of

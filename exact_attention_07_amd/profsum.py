@@ -1,0 +1,183 @@
+"""Summaries of rocprofv3 counter runs of the attention kernels.
+
+    python -m exact_attention_07_amd.profsum --config 3 --out profiles/counters_config3.txt \\
+        --cmd "<command of pass 1>" ... DIR [DIR ...]
+
+Each DIR is the output directory of one `rocprofv3 --pmc ... --output-format
+csv` run of `bench.py --config N` (one counter pass).  The summary averages
+every counter over the dispatches of the workload's attention kernel, derives
+the quantities the measurement reports, and records the sha256 of the
+kernel's sources, so that bench.py uses it only while it describes the
+current code:
+
+  sustained_clock_ghz   GRBM_GUI_ACTIVE / 8 XCDs / kernel duration (the
+                        counter sums the busy clocks of the 8 XCDs)
+  mfma_busy             SQ_VALU_MFMA_BUSY_CYCLES / (clocks * 4 SIMDs * CUs):
+                        the share of SIMD cycles the matrix pipe was busy
+  mfma_flops_executed   512 * SQ_INSTS_VALU_MFMA_MOPS_* (one MOP = 512 flops)
+  mfma_peak_at_clock    CUs * 4 SIMDs * flops per clock per SIMD (1024 bf16,
+                        2048 fp8) * sustained clock
+  trans_share           SQ_INSTS_VALU_TRANS_F32 / non-matrix VALU instructions
+  lds_bank_conflict_rate SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (cycles)
+  hbm_bytes_per_launch  FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+                        scaled by true bytes / counted bytes of the 1 GiB
+                        device copy bench.py --copy-calibration runs
+
+Measurement tooling: it reads profiler output only and computes nothing of
+the attention.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+_CSRC = "exact_attention_07_amd/csrc/"
+# sources of the attention kernel of each dtype
+KERNEL_SOURCES = {
+    "bf16": [_CSRC + f for f in ("fa_fwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
+    "f32": [_CSRC + f for f in ("fa_fwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
+    "fp8": [_CSRC + f for f in ("fa_fwd_fp8.hip", "fa_device.h", "plan.h")],
+    "bwd": [_CSRC + f for f in ("fa_bwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
+}
+KERNEL_NAME = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel",
+               "bwd": "fa_bwd_dkdv_kernel"}
+CONFIG_DTYPE = {1: "f32", 2: "bf16", 3: "bf16", 4: "bf16", 5: "fp8", "decode": "bf16", "backward": "bwd"}
+N_XCD = 8
+N_CU = 256
+COPY_BYTES = 1 << 30
+
+
+def source_hash(dtype: str) -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES[dtype]:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _dispatch_counters(path: str, name_part: str):
+    """{dispatch id: {counter: value, "_ns": duration}} of the dispatches whose
+    kernel name contains name_part, summed over the counter's dimensions."""
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if name_part not in r["Kernel_Name"]:
+            continue
+        d = out.setdefault(r["Dispatch_Id"], {"_ns": int(r["End_Timestamp"]) - int(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return out
+
+
+def _mean(rows, key):
+    vals = [r[key] for r in rows if key in r]
+    return sum(vals) / len(vals) if vals else None
+
+
+def summarize(config, dirs, commands, out_path):
+    dtype = CONFIG_DTYPE[config]
+    kname = KERNEL_NAME[dtype]
+    fields = {}
+    copy = {}
+    durations = []
+    clocks = []
+    busy = None
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        rows = list(_dispatch_counters(files[0], kname).values())
+        if not rows:
+            raise SystemExit(f"no dispatch of {kname} in {files[0]}")
+        for key in rows[0]:
+            if key != "_ns":
+                fields[key] = _mean(rows, key)
+        durations += [r["_ns"] for r in rows]
+        # clock and matrix-pipe share from the dispatches of the same pass
+        if "GRBM_GUI_ACTIVE" in rows[0]:
+            clocks += [r["GRBM_GUI_ACTIVE"] / N_XCD / r["_ns"] for r in rows]
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in rows[0]:
+                busy = sum(r["SQ_VALU_MFMA_BUSY_CYCLES"] / (r["GRBM_GUI_ACTIVE"] / N_XCD * 4 * N_CU)
+                           for r in rows) / len(rows)
+        for r in _dispatch_counters(files[0], "copyBuffer").values():
+            for key in ("FETCH_SIZE", "WRITE_SIZE"):
+                if key in r:
+                    copy[key] = r[key]
+    ns = sum(durations) / len(durations)
+    lines = [f"# rocprofv3 counters of {kname}: workload config {config}",
+             "# commands (from the repository root on the MI355X box), one counter pass each:"]
+    lines += [f"#   {c}" for c in commands]
+    lines += ["# values: mean per dispatch of the attention kernel over the profiled launches",
+              f"kernel: {kname}", f"dispatches_per_pass: {len(durations) // max(1, len(dirs))}",
+              f"kernel_ns_under_counters: {ns:.0f}"]
+    for key in sorted(fields):
+        lines.append(f"{key}: {fields[key]:.0f}")
+    if clocks:
+        clk = sum(clocks) / len(clocks)  # GHz
+        lines.append(f"sustained_clock_ghz: {clk:.4f}")
+        per_simd = 1024.0 * (2 if dtype == "fp8" else 1)
+        lines.append(f"mfma_peak_at_clock_tflops: {N_CU * 4 * per_simd * clk * 1e9 / 1e12:.1f}")
+    if busy is not None:
+        lines.append(f"mfma_busy: {busy:.4f}")
+    mops = fields.get("SQ_INSTS_VALU_MFMA_MOPS_F8" if dtype == "fp8" else "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+    if mops:
+        lines.append(f"mfma_flops_executed: {512.0 * mops:.4e}")
+        lines.append(f"mfma_tflops_executed_under_counters: {512.0 * mops / ns / 1e3:.1f}")
+    valu, mfma, trans = (fields.get(k) for k in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32"))
+    if valu and mfma and trans is not None:
+        lines.append(f"valu_insts_per_mfma: {(valu - mfma) / mfma:.3f}")
+        lines.append(f"trans_share: {trans / (valu - mfma):.4f}")
+    if fields.get("SQ_ACTIVE_INST_LDS"):
+        lines.append(f"lds_bank_conflict_rate: {fields.get('SQ_LDS_BANK_CONFLICT', 0.0) / fields['SQ_ACTIVE_INST_LDS']:.5f}")
+    if "FETCH_SIZE" in fields and "WRITE_SIZE" in fields and "FETCH_SIZE" in copy and "WRITE_SIZE" in copy:
+        fs = COPY_BYTES / (copy["FETCH_SIZE"] * 1024.0)
+        ws = COPY_BYTES / (copy["WRITE_SIZE"] * 1024.0)
+        fb = fields["FETCH_SIZE"] * 1024.0 * fs
+        wb = fields["WRITE_SIZE"] * 1024.0 * ws
+        lines += [f"copy_fetch_kib_raw: {copy['FETCH_SIZE']:.1f}", f"copy_write_kib_raw: {copy['WRITE_SIZE']:.1f}",
+                  f"fetch_scale: {fs:.4f}", f"write_scale: {ws:.4f}",
+                  f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
+                  f"hbm_bytes_per_launch: {fb + wb:.0f}"]
+    lines.append(f"kernel_source_sha256: {source_hash(dtype)}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
+
+
+def summary_name(config) -> str:
+    """File name of a workload's counter summary under profiles/."""
+    return f"counters_config{config}.txt" if isinstance(config, int) else f"counters_{config}.txt"
+
+
+def load(config, root=ROOT):
+    """Fields of the workload's counter summary under profiles/ if it
+    describes the current kernel sources, else None."""
+    path = os.path.join(root, "profiles", summary_name(config))
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != source_hash(CONFIG_DTYPE[config]):
+        return None
+    return fields
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--config", required=True)
+    ap.add_argument("--out", required=True)
+    ap.add_argument("--cmd", action="append", default=[], help="command of a pass (repeat, in order)")
+    ap.add_argument("dirs", nargs="+")
+    a = ap.parse_args(argv)
+    cfg = int(a.config) if a.config.isdigit() else a.config
+    print(summarize(cfg, a.dirs, a.cmd, a.out))
+
+
+if __name__ == "__main__":
+    sys.exit(main())

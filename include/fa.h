@@ -233,6 +233,36 @@ fa_status fa_bwd_dkdv(const void* q, const void* k, const void* v, const void* d
                       int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement helper, not part of the attention computation: the measured
+ * MFMA ceiling.  The pages state attention throughput as a share of the
+ * GPU's peak matrix rate ("FlashAttention-3 — 闪电注意力-3", section
+ * "性能与意义": 75-85 % of H100's peak; "FlashAttention (SV)", section
+ * "FlashAttention-2 (2023)": 50-73 % of A100's).  On MI355X the sustained
+ * clock under a dense matrix load is set by the power limit and by how much
+ * the operand bits toggle, so the nominal peak is not reachable by any
+ * kernel; this call runs a loop of nothing but the matrix instructions the
+ * attention kernels use (v_mfma_f32_32x32x16_bf16, or with fp8 = 1
+ * v_mfma_f32_32x32x64_f8f6f4), two waves per SIMD on every CU, so that the
+ * rate it reaches, timed by the caller, is the ceiling for matrix work at
+ * the clock the chip sustains at that moment.
+ *
+ *   out        device memory for one float per thread of the loop, at least
+ *              fa_mfma_ceiling_out_bytes() bytes, 4-byte aligned (the sums are
+ *              stored only so that no work is optimised away)
+ *   fp8        0: bf16 instruction, 1: e4m3 instruction
+ *   iters      rounds of 16 matrix instructions per wave, >= 1
+ *   random     1: operands that change from instruction to instruction
+ *              (pseudo-random values, the toggling of real data); 0: constant
+ *   fa_mfma_ceiling_flops(fp8, iters) gives the matrix flops of one launch.
+ * Errors: FA_ERR_NULL (out), FA_ERR_WORKSPACE (out_bytes too small or out
+ * misaligned), FA_ERR_SHAPE (iters < 1), FA_ERR_FLAG (fp8 or random not 0/1),
+ * FA_ERR_HIP (launch).
+ */
+size_t fa_mfma_ceiling_out_bytes(void);
+double fa_mfma_ceiling_flops(int fp8, int iters);
+fa_status fa_mfma_ceiling(float* out, size_t out_bytes, int fp8, int iters, int random, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

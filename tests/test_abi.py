@@ -217,3 +217,12 @@ def test_bwd_dkdv_rejects_invalid_arguments(lib, kw, status):
     assert lib.fa_bwd_dkdv(a["q"], a["k"], a["v"], a["do"], a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
                            a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], a["ws"],
                            ctypes.c_size_t(a["wsb"]), None) == status
+
+
+def test_mfma_ceiling_rejects_arguments_on_the_host(lib):
+    f = lib.fa_mfma_ceiling
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 1 << 20, 0, 10, 1, None) == 1         # FA_ERR_NULL
+    assert f(P, 1 << 20, 2, 10, 1, None) == 8            # FA_ERR_FLAG (fp8)
+    assert f(P, 1 << 20, 0, 10, 3, None) == 8            # FA_ERR_FLAG (random)
+    assert f(P, 1 << 20, 0, 0, 1, None) == 2             # FA_ERR_SHAPE (iters)
