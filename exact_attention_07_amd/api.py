@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM", 4: "FA_ERR_GQA_RATIO",
-             5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_HIP", 8: "FA_ERR_FLAG", 9: "FA_ERR_WORKSPACE"}
+             5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_HIP", 8: "FA_ERR_FLAG", 9: "FA_ERR_WORKSPACE",
+             10: "FA_ERR_SCRATCH_LIMIT"}
 
 _lib = None
 
@@ -46,6 +47,8 @@ def lib() -> ctypes.CDLL:
     L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_fwd_splitkv.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, vp, ctypes.c_size_t, vp]
     L.fa_fwd_splitkv.restype = ctypes.c_int
+    L.fa_fwd_splitkv_noalloc.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, vp]
+    L.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
     L.fa_fwd_splitkv_workspace_size.argtypes = [i] * 8
     L.fa_fwd_splitkv_workspace_size.restype = ctypes.c_size_t
     L.fa_bwd.argtypes = [vp] * 9 + [i] * 6 + [f, i, vp, ctypes.c_size_t, vp]
@@ -329,3 +332,17 @@ def mfma_ceiling(out, fp8: bool, iters: int, random: bool = True, stream=None) -
         raise ValueError("out must be a contiguous float32 GPU tensor")
     _check(lib().fa_mfma_ceiling(_ptr(out), out.numel() * 4, int(bool(fp8)), int(iters), int(bool(random)),
                                  _stream(stream)), "fa_mfma_ceiling")
+
+
+def fa_fwd_splitkv_noalloc(q, k, v, o, lse, scale: float, causal: bool, nsplit: int = 0, stream=None) -> None:
+    """fa_fwd_splitkv with the parts in the library's fixed per-GPU scratch (no workspace argument)."""
+    import torch
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v, o, lse)
+    for t in (q, k, v, o):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("fa_fwd_splitkv_noalloc takes bfloat16 q, k, v, o")
+    if lse is not None and lse.dtype != torch.float32:
+        raise TypeError("lse must be float32")
+    _check(lib().fa_fwd_splitkv_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                        float(scale), int(bool(causal)), int(nsplit), _stream(stream)),
+           "fa_fwd_splitkv_noalloc")

@@ -188,6 +188,14 @@ size_t bwd_workspace_bytes(int B, int Hq, int Hkv, int Nq, int Nk, int d, int ca
 
 }  // namespace
 
+namespace fa {
+// The forward entry points' host-side argument checks, for fa_noalloc.hip.
+fa_status validate_forward(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int Hq,
+                           int Hkv, int Nq, int Nk, int d, float scale, int causal) {
+  return validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+}
+}  // namespace fa
+
 extern "C" {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
@@ -204,6 +212,7 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_HIP: return "HIP launch failed";
     case FA_ERR_FLAG: return "causal must be 0 or 1";
     case FA_ERR_WORKSPACE: return "workspace missing, too small or not 16-byte aligned";
+    case FA_ERR_SCRATCH_LIMIT: return "the call needs more than the library's fixed scratch";
   }
   return "unknown status";
 }

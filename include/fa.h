@@ -63,7 +63,8 @@ typedef enum fa_status {
   FA_ERR_SCALE = 6,      /* scale not finite or not > 0 */
   FA_ERR_HIP = 7,        /* the HIP runtime refused the launch */
   FA_ERR_FLAG = 8,       /* causal not 0 or 1 */
-  FA_ERR_WORKSPACE = 9   /* workspace missing, too small or not 16-byte aligned */
+  FA_ERR_WORKSPACE = 9,  /* workspace missing, too small or not 16-byte aligned */
+  FA_ERR_SCRATCH_LIMIT = 10 /* the call needs more than the library's fixed scratch */
 } fa_status;
 
 /* Version of this interface; bumped on any incompatible change. */
@@ -126,6 +127,24 @@ size_t fa_fwd_splitkv_workspace_size(int B, int Hq, int Hkv, int Nq, int Nk, int
 fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                          int nsplit, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The parts live in a fixed array of
+ * FA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; the call itself allocates and frees nothing.
+ * Arguments, layouts, result and errors as for fa_fwd_splitkv, plus
+ * FA_ERR_SCRATCH_LIMIT when fa_fwd_splitkv_workspace_size(...) for the same
+ * arguments exceeds FA_NOALLOC_SCRATCH_BYTES (ask for fewer ranges, or use
+ * fa_fwd_splitkv with a workspace).  Every call on one GPU uses that GPU's
+ * array: calls that overlap on one GPU (on other streams or from other host
+ * threads) race on it, so the caller orders them.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (32 * 1024 * 1024)
+fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                                 int nsplit, void* stream);
 
 /*
  * FP8 preparation ("FlashAttention-3 — 闪电注意力-3", section on low

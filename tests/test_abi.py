@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_status_strings(lib):
     assert lib.fa_abi_version() == 1
-    for s in range(10):
+    for s in range(11):
         assert len(lib.fa_status_string(s)) > 0
     assert lib.fa_status_string(123) == b"unknown status"
 
@@ -226,3 +226,19 @@ def test_mfma_ceiling_rejects_arguments_on_the_host(lib):
     assert f(P, 1 << 20, 2, 10, 1, None) == 8            # FA_ERR_FLAG (fp8)
     assert f(P, 1 << 20, 0, 10, 3, None) == 8            # FA_ERR_FLAG (random)
     assert f(P, 1 << 20, 0, 0, 1, None) == 2             # FA_ERR_SHAPE (iters)
+
+
+def test_noalloc_refuses_a_call_beyond_its_scratch_on_the_host(lib):
+    """More parts than the fixed scratch holds: FA_ERR_SCRATCH_LIMIT before any
+    HIP call (fake, never dereferenced pointers)."""
+    f = lib.fa_fwd_splitkv_noalloc
+    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int] * 6 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                                ctypes.c_void_p]
+    ws = lib.fa_fwd_splitkv_workspace_size
+    ws.argtypes = [ctypes.c_int] * 8
+    ws.restype = ctypes.c_size_t
+    assert ws(1, 64, 64, 1024, 65536, 256, 0, 64) > 32 * 1024 * 1024
+    assert f(P, P, P, P, P, 1, 64, 64, 1024, 65536, 256, ctypes.c_float(0.1), 0, 64, None) == 10
+    assert f(P, P, P, P, P, 1, 64, 64, 1024, 65536, 256, ctypes.c_float(0.1), 0, -1, None) == 2
+    assert f(None, P, P, P, P, 1, 4, 2, 10, 10, 128, ctypes.c_float(0.1), 0, 0, None) == 1
+    assert f(P, P, P, P, P, 1, 4, 2, 10, 10, 128, ctypes.c_float(-1.0), 0, 0, None) == 6
