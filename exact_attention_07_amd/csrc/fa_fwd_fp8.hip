@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "plan.h"
@@ -65,17 +67,33 @@ struct TileCopy {
       goff[i] = (ins < INS && pp < CPR) ? (unsigned)(r * row_stride + pp * 16) : OUT_OF_RANGE;
     }
   }
+  // copy instruction i of this wave for the tile at byte offset soff
+  // (instructions past the tile, when NW does not divide INS, write into the
+  // 1 KB block `spare`)
+  __device__ __forceinline__ void issue_one(const __amdgpu_buffer_rsrc_t& rs, int soff, LDS_AS char* tile,
+                                            LDS_AS char* spare, int wave, int i) const {
+    const int ins = i * NW + wave;
+    LDS_AS char* dst = (INS % NW == 0 || ins < INS) ? tile + ins * 1024 : spare;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], soff, 0, 0);
+  }
   __device__ __forceinline__ void issue_all(const __amdgpu_buffer_rsrc_t& rs, int soff, LDS_AS char* tile,
                                             LDS_AS char* spare, int wave) const {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int ins = i * NW + wave;
-      LDS_AS char* dst = (INS % NW == 0 || ins < INS) ? tile + ins * 1024 : spare;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)dst, 16, goff[i], soff, 0, 0);
-    }
+    for (int i = 0; i < MI; ++i) issue_one(rs, soff, tile, spare, wave, i);
   }
 };
 
+// Iteration j of a wave interleaves three independent streams, one MFMA per
+// chunk: the MFMAs of S_{j+1} = K_{j+1} Q^T, the exponentials (and e4m3
+// packing) of tile j, and the MFMAs of O^T += V_{j-1}^T P_{j-1}^T.  Every
+// chunk thus carries both matrix and vector work, so the matrix pipe of a
+// SIMD is fed while its two waves take exponentials, instead of both waves
+// taking all their exponentials, then all their products, in step.  The lazy
+// rescale of tile j runs after P_{j-1} V_{j-1} has entered O, so O and P_j
+// always refer to the same reference maximum.
+// LDS ring (two slots each): iteration j reads K_{j+1} and V_{j-1} and
+// refills the slots of K_j and V_{j-2} with K_{j+2} and V_j; each copy has
+// one iteration to land before the barrier that publishes it.
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
@@ -85,16 +103,32 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
   constexpr int KS = D / 64;       // k-steps of S^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
   constexpr int NMF = KB * KS;     // S^T MFMAs per tile
-  constexpr int SPS = KB * 16 / NMF;  // exponentials per S^T MFMA
+  constexpr int NPV = DB;          // P V MFMAs per tile (one per block covers the 64 keys)
+  static_assert(NMF == NPV, "S and P V streams alternate");
+  constexpr int NCH = NMF + NPV;   // chunks of the fused phase
+  constexpr int NSC = KB * 16;     // scores per lane per tile
+  constexpr int SPC = NSC / NCH;   // scores per chunk
+  static_assert(NSC % NCH == 0 && SPC % 2 == 0, "whole pairs of scores per chunk");
+  constexpr int KPF = 2, VPF = 2;  // LDS fragment reads in flight per stream
   constexpr int RSK = D + 16;      // K8 LDS row stride (conflict-free for 16 consecutive keys)
   constexpr int RSV = 80;          // V8^T LDS row stride: 64 keys + 16 bytes
   constexpr int KTILE = BC * RSK, VTILE = D * RSV;
   using KCopy = TileCopy<BC, D / 16, D / 16 + 1, NW>;
   using VCopy = TileCopy<D, 4, 5, NW>;
-  constexpr int MIK = KCopy::MI, MIV = VCopy::MI;
-  __shared__ __attribute__((aligned(1024))) char smem_[2 * KTILE + 2 * VTILE + 1024];
-  LDS_AS char* const smem = (LDS_AS char*)smem_;
-  LDS_AS char* const spare = smem + 2 * KTILE + 2 * VTILE;
+  constexpr int NCP = KCopy::MI + VCopy::MI;
+  // every ring slot is an array of its own, so that a copy into one slot
+  // provably does not alias the reads of the other (the compiler then does
+  // not wait for copies in flight before those reads)
+  __shared__ __attribute__((aligned(1024))) char lk0_[KTILE];
+  __shared__ __attribute__((aligned(1024))) char lk1_[KTILE];
+  __shared__ __attribute__((aligned(1024))) char lv0_[VTILE];
+  __shared__ __attribute__((aligned(1024))) char lv1_[VTILE];
+  __shared__ __attribute__((aligned(1024))) char lsp_[1024];
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  auto kslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lk0_ : lk1_); };
+  auto vslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lv0_ : lv1_); };
+  LDS_AS char* const spare = (LDS_AS char*)lsp_;
 
   const fa_work_t w = fa_decode(p, blockIdx.x);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -107,6 +141,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
   const int qlast_w = min(Nq - 1, q0w + 31);
   const int klast_w = CAUSAL ? min(Nk - 1, qlast_w + Nk - Nq) : Nk - 1;
   const int kfull_w = CAUSAL ? min(Nk - 1, q0w + Nk - Nq) : Nk - 1;
+  // tiles this wave computes (0 .. ntw - 1)
   const int ntw = (live && klast_w >= 0) ? min(nt, klast_w / BC + 1) : 0;
   const float sq = descale[0], sk = descale[1], sv = descale[2];
   const float c = c0 * sq * sk;
@@ -115,6 +150,14 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
   const size_t koff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
   const size_t voff = (size_t)(w.b * p.Hkv + w.hkv) * D * Nkp;
 
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
+  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
+
+  // A workgroup without key tiles (causal rows that see no key) loads and
+  // copies nothing: the epilogue writes O = 0 and LSE = -inf straight away.
+  if (nt > 0) {
   // resident Q fragments: query lane%32, bytes ks*64 + (lane/32)*32 .. +31
   i32x8 qf[KS];
   {
@@ -126,10 +169,6 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
       qf[ks] = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   }
-  f32x16 o[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) o[db] = (f32x16){};
-  float m_ref = NEG_INF, m_run = NEG_INF, lsum = 0.f;
 
   const int koff_l = (lane & 31) * RSK + (lane >> 5) * 32;
   const int voff_l = (lane & 31) * RSV + (lane >> 5) * 32;
@@ -139,48 +178,67 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
   vc.init(wave, lane, Nkp);
   const __amdgpu_buffer_rsrc_t kres = __builtin_amdgcn_make_buffer_rsrc((void*)(K8 + koff), (short)0, Nk * D, 0x00020000);
   const __amdgpu_buffer_rsrc_t vres = __builtin_amdgcn_make_buffer_rsrc((void*)(V8T + voff), (short)0, D * Nkp, 0x00020000);
-  auto opaque = [](int x) {
-    asm volatile("" : "+s"(x));
-    return x;
+  // byte offsets of tile t (past the last tile: past the buffer, reads zeros)
+  auto tile_k = [&](int t) { return t < nt ? t * BC * D : Nk * D; };
+  auto tile_v = [&](int t) { return t < nt ? t * BC : D * Nkp; };
+  // copy instruction i of this wave in iteration j (of parity par): K_{j+2}
+  // into K slot par, then V_j into V slot par
+  auto copy_one = [&](int j, auto par, int i) {
+    if (i < KCopy::MI) kc.issue_one(kres, tile_k(j + 2), kslot(par), spare, wave, i);
+    else vc.issue_one(vres, tile_v(j), vslot(par), spare, wave, i - KCopy::MI);
   };
-  auto kslot = [&](int t) { return smem + (t & 1) * KTILE; };
-  auto vslot = [&](int t) { return smem + 2 * KTILE + (t & 1) * VTILE; };
-  auto copy_k = [&](int t) {
-    kc.issue_all(kres, t < nt ? t * BC * D : Nk * D, smem + opaque((t & 1) * KTILE), spare, wave);
-  };
-  auto copy_v = [&](int t) {
-    vc.issue_all(vres, t < nt ? t * BC : D * Nkp, smem + opaque(2 * KTILE + (t & 1) * VTILE), spare, wave);
+  auto copy_all = [&](int j, auto par) {
+    kc.issue_all(kres, tile_k(j + 2), kslot(par), spare, wave);
+    vc.issue_all(vres, tile_v(j), vslot(par), spare, wave);
   };
 
-  // prologue: K_0, V_0, K_1 complete; S_0
-  copy_k(0);
-  copy_k(1);
-  copy_v(0);
+  // prologue: K_0, K_1, zeros into V slot 1, which iteration 0 reads (its
+  // P V product then adds 0 x 0); S_0
+  kc.issue_all(kres, tile_k(0), kslot(P0{}), spare, wave);
+  kc.issue_all(kres, tile_k(1), kslot(P1{}), spare, wave);
+  vc.issue_all(vres, D * Nkp, vslot(P1{}), spare, wave);
   vm_wait<0>();
   __syncthreads();
   f32x16 sa[KB], sb[KB];
-  auto scores = [&](f32x16 (&sv_)[KB], LDS_AS const char* kt) {
+  if (ntw > 0) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sv_[kb] = (f32x16){};
+    for (int kb = 0; kb < KB; ++kb) sa[kb] = (f32x16){};
 #pragma unroll
-    for (int t = 0; t < NMF; ++t) {
-      const int ks = t / KB, kb = t % KB;
-      sv_[kb] = mfma_fp8(lds_b256(kt + koff_l + kb * 32 * RSK + ks * 64), qf[ks], sv_[kb]);
+    for (int t = 0; t < NMF; ++t)
+      sa[t % KB] = mfma_fp8(lds_b256(kslot(P0{}) + koff_l + (t % KB) * 32 * RSK + (t / KB) * 64), qf[t / KB], sa[t % KB]);
+  }
+  i32x8 pa, pb;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) pb[i] = 0;
+
+  // score sc of s: exponential against mu, row-sum part; byte sc of the P
+  // fragment (the odd member of a pair packs the pair into its half-dword)
+  auto score = [&](const f32x16 (&s)[KB], i32x8& pf, int sc, float mu, float& part0, float& part1, float& even) {
+    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sc / 16][sc % 16], c, -mu));
+    if (sc & 1) {
+      part1 += pv;
+      const int pp = sc / 2;
+      if (pp & 1) pf[pp / 2] = __builtin_amdgcn_cvt_pk_fp8_f32(even, pv, pf[pp / 2], true);
+      else pf[pp / 2] = __builtin_amdgcn_cvt_pk_fp8_f32(even, pv, 0, false);
+    } else {
+      part0 += pv;
+      even = pv;
     }
   };
-  if (ntw > 0) scores(sa, kslot(0));
 
-  auto step = [&](int j, f32x16 (&s)[KB], f32x16 (&sn)[KB]) {
+  // the exponentials of tile j (scores in s, probabilities into pf), the
+  // MFMAs of S_{j+1} (into sn) and of O += V_{j-1} P_{j-1} (pprev).  At the
+  // wave's tile ntw, past its last key, the mask turns every score into -inf.
+  auto fused = [&](int j, auto par, f32x16 (&s)[KB], f32x16 (&sn)[KB], i32x8& pf, const i32x8& pprev) {
+    using other = std::integral_constant<int, 1 - decltype(par)::value>;
     const int j0 = j * BC;
-    vm_wait<0>();
-    __syncthreads();
-    if (j + 2 < nt) copy_k(j + 2);
-    if (j + 1 < nt) copy_v(j + 1);
-    if (j >= ntw) return;
-    LDS_AS const char* knext = kslot(j + 1) + koff_l;
-    LDS_AS const char* vlane = vslot(j) + voff_l;
-    i32x8 kbuf = lds_b256(knext);
-
+    LDS_AS const char* knext = kslot(other{}) + koff_l;
+    LDS_AS const char* vprev = vslot(other{}) + voff_l;
+    i32x8 kbuf[KPF], vbuf[VPF];
+#pragma unroll
+    for (int t = 0; t < KPF; ++t) kbuf[t] = lds_b256(knext + (t % KB) * 32 * RSK + (t / KB) * 64);
+#pragma unroll
+    for (int t = 0; t < VPF; ++t) vbuf[t] = lds_b256(vprev + t * 32 * RSV);
     if (j0 + BC - 1 > kfull_w) {
       const int query = q0w + (lane & 31);
 #pragma unroll
@@ -191,29 +249,38 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
           if ((i >> 2) * 8 + (i & 3) > kmax) s[kb][i] = NEG_INF;
       }
     }
-
     float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-    float part0 = 0.f, part1 = 0.f;
-    float pfl[KB * 16];
+    float part0 = 0.f, part1 = 0.f, even = 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sn[kb] = (f32x16){};
 #pragma unroll
-    for (int t = 0; t < NMF; ++t) {
-      const int ks = t / KB, kb = t % KB;
-      const i32x8 kf = kbuf;
-      if (t + 1 < NMF) kbuf = lds_b256(knext + ((t + 1) % KB) * 32 * RSK + ((t + 1) / KB) * 64);
-      sn[kb] = mfma_fp8(kf, qf[ks], sn[kb]);
-#pragma unroll
-      for (int u = 0; u < SPS; ++u) {
-        const int sc = t * SPS + u;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sc / 16][sc % 16], c, -mu));
-        if (sc & 1) part1 += pv;
-        else part0 += pv;
-        pfl[sc] = pv;
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int m = ch / 2;
+      if (ch % 2 == 0) {
+        // S_{j+1}: MFMA m (k-step m / KB, key block m % KB)
+        sn[m % KB] = mfma_fp8(kbuf[m % KPF], qf[m / KB], sn[m % KB]);
+        if (m + KPF < NMF)
+          kbuf[m % KPF] = lds_b256(knext + ((m + KPF) % KB) * 32 * RSK + ((m + KPF) / KB) * 64);
+      } else {
+        // O += V_{j-1} P_{j-1}: MFMA m (d-block m)
+        o[m] = mfma_fp8(vbuf[m % VPF], pprev, o[m]);
+        if (m + VPF < NPV) vbuf[m % VPF] = lds_b256(vprev + (m + VPF) * 32 * RSV);
       }
+#pragma unroll
+      for (int sc = ch * SPC; sc < (ch + 1) * SPC; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      // the copy instructions over the first half of the chunks: each then
+      // has more than half an iteration to land (measured 1-2 % faster than
+      // spreading them over all chunks)
+#pragma unroll
+      for (int i = 0; i < NCP; ++i)
+        if (ch == i * (NCH / 2) / NCP) copy_one(j, par, i);
       __builtin_amdgcn_sched_barrier(0);
     }
     float part = part0 + part1;
+    // slow path, as in the bf16 kernel: if some probability may exceed
+    // 2^TAU (a lane's partial row sum does) or a row has no reference yet,
+    // form the row maximum, rescale O (which already holds P_{j-1} V_{j-1})
+    // and l when it grew by more than TAU, and redo the exponentials
     if (__ballot(!(part <= TAU_EXP2) || m_ref == NEG_INF)) {
       float mx = NEG_INF;
 #pragma unroll
@@ -229,39 +296,38 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
         m_ref = m_run;
       }
       mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-      part = 0.f;
+      part0 = part1 = 0.f;
 #pragma unroll
-      for (int sc = 0; sc < KB * 16; ++sc) {
-        pfl[sc] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sc / 16][sc % 16], c, -mu));
-        part += pfl[sc];
-      }
+      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      part = part0 + part1;
     }
     lsum += part;
-    // P -> e4m3, byte j = score j (block j/16, register j%16)
-    i32x8 p8;
-#pragma unroll
-    for (int wd = 0; wd < 8; ++wd) {
-      int v = __builtin_amdgcn_cvt_pk_fp8_f32(pfl[4 * wd], pfl[4 * wd + 1], 0, false);
-      p8[wd] = __builtin_amdgcn_cvt_pk_fp8_f32(pfl[4 * wd + 2], pfl[4 * wd + 3], v, true);
-    }
-    // O^T += V^T P^T: one MFMA per 32-row block of d covers the 64 keys
-    i32x8 vbuf = lds_b256(vlane);
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const i32x8 vf = vbuf;
-      if (db + 1 < DB) vbuf = lds_b256(vlane + (db + 1) * 32 * RSV);
-      o[db] = mfma_fp8(vf, p8, o[db]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
   };
-  for (int j = 0; j < nt; j += 2) {
-    step(j, sa, sb);
-    if (j + 1 < nt) step(j + 1, sb, sa);
+
+  // one code path for every iteration a wave takes part in (j <= ntw);
+  // waves past their last tile only keep the barriers and copies going
+  auto iteration = [&](int j, auto par, f32x16 (&s)[KB], f32x16 (&sn)[KB], i32x8& pf, i32x8& pprev) {
+    vm_wait<0>();
+    __syncthreads();
+    if (j <= ntw && ntw > 0) fused(j, par, s, sn, pf, pprev);
+    else copy_all(j, par);
+  };
+  for (int j = 0; j <= nt - 1; j += 2) {
+    iteration(j, P0{}, sa, sb, pa, pb);
+    if (j + 1 <= nt - 1) iteration(j + 1, P1{}, sb, sa, pb, pa);
   }
-  (void)vslot;
-  // the last copies (zeros past the final tile) land before the workgroup's
-  // LDS can pass to another workgroup
+  // iteration nt only adds O += V_{nt-1} P_{nt-1}; it also waits for the
+  // last copies (zeros past the final tile), which must land before the
+  // workgroup's LDS can pass to another workgroup
   vm_wait<0>();
+  __syncthreads();
+  if (nt <= ntw) {
+    LDS_AS const char* vprev = ((nt & 1) ? (LDS_AS const char*)lv0_ : (LDS_AS const char*)lv1_) + voff_l;
+    const i32x8 pp = (nt & 1) ? pa : pb;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) o[db] = mfma_fp8(lds_b256(vprev + db * 32 * RSV), pp, o[db]);
+  }
+  }  // nt > 0
 
   if (!live) return;
   const float lt = xhalf_sum(lsum);
