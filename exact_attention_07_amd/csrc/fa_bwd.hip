@@ -526,12 +526,15 @@ void fa_bwd_dkdv_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
   bwd_dkdv_item<D, CAUSAL, NW, KBW>(Q, K, V, dO, LD, dK, dV, PART, p, c, scale, blockIdx.x);
 }
 
-// The kernels that hold a whole CU per workgroup (8 waves at d = 128, 4 at
-// d = 256) as a persistent grid of fewer workgroups than items
+// The dK/dV kernels as a persistent grid of fewer workgroups than items
 // (fa_persistent_item over the key-block order): the snake gives every
-// workgroup heavy and light causal key blocks alike.  A kernel of its own:
-// the loop around the item slows the one-item kernel's inner loop by 3-5 %
-// where that is kept (Nq > 4096).
+// workgroup heavy and light causal key blocks alike.  Forms (launch_bwd_dkdv
+// picks them up to Nq = 4096 with at least two items per workgroup), with
+// the workgroups each CU holds: 8 waves at d = 128 (one per CU), 4 waves at
+// d = 128, 256 and 64 (one per CU), 2 waves at d = 64, causal only (two per
+// CU; non-causal 2-wave d = 64 plans never reach two items per workgroup).
+// A kernel of its own: the loop around the item slows the one-item kernel's
+// inner loop by 3-5 % where that is kept (Nq > 4096).
 template <int D, bool CAUSAL, int NW, int KBW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1)))
 void fa_bwd_dkdv_persistent_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
@@ -556,7 +559,6 @@ FA_INST_DKDV_P(256, false, 4, 1)
 FA_INST_DKDV_P(256, true, 4, 1)
 FA_INST_DKDV_P(64, false, 4, 2)
 FA_INST_DKDV_P(64, true, 4, 2)
-FA_INST_DKDV_P(64, false, 2, 2)
 FA_INST_DKDV_P(64, true, 2, 2)
 FA_INST_DKDV_P(128, false, 4, 1)
 FA_INST_DKDV_P(128, true, 4, 1)
@@ -667,7 +669,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
   // wave per SIMD), two for 2 waves at d = 64
   const int per_cu = ((d == 128 && (pk.nw == 8 || pk.nw == 4)) || (d == 256 && pk.nw == 4) || (d == 64 && pk.nw == 4))
                          ? 1
-                     : (d == 64 && pk.nw == 2) ? 2 : 0;
+                     : (d == 64 && pk.nw == 2 && pk.causal) ? 2 : 0;
   const unsigned grid = (per_cu > 0 && pk.Nq <= 4096) ? persistent_grid(pk.nwg, per_cu) : 0;
   if (grid > 0 && 2LL * grid <= pk.nwg) {
 #define FA_DKDV_P(DD, CC, NN, KK)                                                                              \
@@ -687,8 +689,7 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const vo
       if (pk.causal) FA_DKDV_P(64, true, 4, 2);
       else FA_DKDV_P(64, false, 4, 2);
     } else {
-      if (pk.causal) FA_DKDV_P(64, true, 2, 2);
-      else FA_DKDV_P(64, false, 2, 2);
+      FA_DKDV_P(64, true, 2, 2);  // per_cu > 0 at d = 64 with 2 waves only if causal
     }
 #undef FA_DKDV_P
     e = hipGetLastError();

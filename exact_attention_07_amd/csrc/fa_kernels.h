@@ -12,12 +12,17 @@ namespace fa {
 int queries_per_wave(int d, int f32);
 
 // Workgroups of a persistent launch whose kernel fits per_cu workgroups on
-// a CU (one: the forward at 8 waves and d = 128 or 4 waves and d = 256, the
-// dQ and dK/dV kernels of those shapes; two: the causal 4-wave forward at
-// d = 64 and 128, the causal 4-wave dQ kernel at d = 128, the 2-wave d = 64
-// dK/dV kernel): nwg, or per_cu per CU of the current device (the CU
-// count rounded down to a multiple of 8) when nwg is larger; the kernel then
-// takes its work items in rounds (fa_persistent_item).
+// a CU: nwg, or per_cu per CU of the current device (the CU count rounded
+// down to a multiple of 8) when nwg is larger; the kernel then takes its
+// work items in rounds (fa_persistent_item).  The persistent forms and
+// their workgroups per CU:
+//   forward: 8 waves at d = 128 and 4 at d = 256 (one); causal 4 waves at
+//     d = 64 and 128 (two);
+//   dQ: 8 waves at d = 128, 4 at d = 256 up to Nq = 4096 (one); causal
+//     4 waves at d = 128 up to Nq = 4096 (two);
+//   dK/dV, up to Nq = 4096 with two items per workgroup: 8 waves at
+//     d = 128, 4 waves at d = 64, 128 and 256 (one); causal 2 waves at
+//     d = 64 (two).
 unsigned persistent_grid(long long nwg, int per_cu = 1);
 
 // CUs of the current device, rounded down to a multiple of 8 (one per XCD
