@@ -364,10 +364,10 @@ def main():
         amax_ws = torch.empty(3, dtype=torch.int32, device=dev)
 
         def prepare():
-            api.fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, stream)
+            api.fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, w.softmax_scale, stream)
 
         def attend():
-            api.fa_fwd_fp8(q8, k8, v8t, descale, o, lse, w.softmax_scale, w.causal, stream)
+            api.fa_fwd_fp8(q8, k8, v8t, descale, o, lse, w.causal, stream)
     else:
         fwd = api.fa_fwd if w.dtype == "bf16" else api.fa_fwd_f32
 

@@ -41,9 +41,9 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = fwd_args
         fn.restype = ctypes.c_int
-    L.fa_fp8_prepare.argtypes = [vp] * 9 + [i] * 6 + [vp]
+    L.fa_fp8_prepare.argtypes = [vp] * 9 + [f] + [i] * 6 + [vp]
     L.fa_fp8_prepare.restype = ctypes.c_int
-    L.fa_fwd_fp8.argtypes = [vp] * 6 + [i] * 6 + [f, i, vp]
+    L.fa_fwd_fp8.argtypes = [vp] * 6 + [i] * 6 + [i, vp]
     L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_fwd_splitkv.argtypes = [vp] * 5 + [i] * 6 + [f, i, i, vp, ctypes.c_size_t, vp]
     L.fa_fwd_splitkv.restype = ctypes.c_int
@@ -148,8 +148,10 @@ def padded_keys(nk: int) -> int:
     return (nk + 63) // 64 * 64
 
 
-def fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs=None, stream=None) -> None:
-    """Rotate (if signs is given) and quantise bf16 q, k, v into e4m3 codes (uint8 tensors)."""
+def fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs=None, scale: float | None = None,
+                   stream=None) -> None:
+    """Rotate (if signs is given) and quantise bf16 q, k, v into e4m3 codes (uint8 tensors) for the
+    softmax scale `scale` (default 1/sqrt(d)), which the Q codes carry."""
     import torch
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
@@ -168,13 +170,16 @@ def fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs=None, stream=No
             raise ValueError("tensors must be contiguous GPU tensors")
     if signs is not None and (signs.numel() != d or signs.dtype != torch.float32):
         raise ValueError("signs: d float32 values")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
     _check(lib().fa_fp8_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(q8), _ptr(k8), _ptr(v8t), _ptr(descale),
-                                _ptr(amax_ws), _ptr(signs), B, Hq, Hkv, Nq, Nk, d, _stream(stream)),
+                                _ptr(amax_ws), _ptr(signs), float(scale), B, Hq, Hkv, Nq, Nk, d, _stream(stream)),
            "fa_fp8_prepare")
 
 
-def fa_fwd_fp8(q8, k8, v8t, descale, o, lse, scale: float, causal: bool, stream=None) -> None:
-    """fp8 forward pass on codes from fa_fp8_prepare into o (bf16) and lse (fp32 or None)."""
+def fa_fwd_fp8(q8, k8, v8t, descale, o, lse, causal: bool, stream=None) -> None:
+    """fp8 forward pass on codes from fa_fp8_prepare (which fixed the softmax scale) into o (bf16) and lse
+    (fp32 or None)."""
     import torch
     B, Hq, Nq, d = q8.shape
     _, Hkv, Nk, _ = k8.shape
@@ -188,7 +193,7 @@ def fa_fwd_fp8(q8, k8, v8t, descale, o, lse, scale: float, causal: bool, stream=
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous GPU tensors")
     _check(lib().fa_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8t), _ptr(descale), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk,
-                            d, float(scale), int(bool(causal)), _stream(stream)), "fa_fwd_fp8")
+                            d, int(bool(causal)), _stream(stream)), "fa_fwd_fp8")
 
 
 def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None, signs=None, stream=None):
@@ -207,10 +212,10 @@ def attention_fp8(q, k, v, causal: bool = False, scale: float | None = None, sig
     v8t = torch.empty((B, Hkv, d, padded_keys(Nk)), dtype=torch.uint8, device=dev)
     descale = torch.empty(3, dtype=torch.float32, device=dev)
     amax_ws = torch.empty(3, dtype=torch.int32, device=dev)
-    fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, stream)
+    fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, scale, stream)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev)
-    fa_fwd_fp8(q8, k8, v8t, descale, o, lse, scale, causal, stream)
+    fa_fwd_fp8(q8, k8, v8t, descale, o, lse, causal, stream)
     return o, lse, {"q8": q8, "k8": k8, "v8t": v8t, "descale": descale}
 
 

@@ -228,8 +228,8 @@ fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, f
 }
 
 fa_status fa_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t, float* descale,
-                         unsigned* amax_ws, const float* signs, int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                         void* stream) {
+                         unsigned* amax_ws, const float* signs, float scale, int B, int Hq, int Hkv, int Nq, int Nk,
+                         int d, void* stream) {
   if (!q || !k || !v || !q8 || !k8 || !v8t || !descale || !amax_ws) return FA_ERR_NULL;
   const fa_status st = validate_shape(B, Hq, Hkv, Nq, Nk, d);
   if (st != FA_OK) return st;
@@ -237,25 +237,25 @@ fa_status fa_fp8_prepare(const void* q, const void* k, const void* v, void* q8, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q8) || !aligned16(k8) || !aligned16(v8t) ||
       !aligned4(descale) || !aligned4(amax_ws) || (signs && !aligned4(signs)))
     return FA_ERR_ALIGN;
-  const hipError_t e =
-      fa::launch_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, B, Hq, Hkv, Nq, Nk, d, (hipStream_t)stream);
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
+  const float c0 = (float)((double)scale * LOG2E);
+  const hipError_t e = fa::launch_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, c0, B, Hq, Hkv, Nq, Nk,
+                                              d, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale, void* o, float* lse, int B,
-                     int Hq, int Hkv, int Nq, int Nk, int d, float scale, int causal, void* stream) {
+                     int Hq, int Hkv, int Nq, int Nk, int d, int causal, void* stream) {
   if (!q8 || !k8 || !v8t || !descale || !o) return FA_ERR_NULL;
   const fa_status st = validate_shape(B, Hq, Hkv, Nq, Nk, d);
   if (st != FA_OK) return st;
   if (!aligned16(q8) || !aligned16(k8) || !aligned16(v8t) || !aligned16(o) || (lse && !aligned16(lse)) ||
       !aligned4(descale))
     return FA_ERR_ALIGN;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_SCALE;
   if (causal != 0 && causal != 1) return FA_ERR_FLAG;
   const fa_plan_t p = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, KIND_FP8);
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
-  const hipError_t e =
-      fa::launch_fwd_fp8(q8, k8, v8t, descale, o, lse, p, d, (float)((double)scale * LOG2E), (hipStream_t)stream);
+  const hipError_t e = fa::launch_fwd_fp8(q8, k8, v8t, descale, o, lse, p, d, (hipStream_t)stream);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

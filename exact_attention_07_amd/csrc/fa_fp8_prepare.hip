@@ -9,8 +9,14 @@
 //     applied on the right, x -> x M, to every row of Q and K; V is not
 //     rotated; signs == NULL skips the rotation.  x M is computed as a fast
 //     Walsh-Hadamard transform of (x * signs) scaled by 1/sqrt(d), in fp32.
-//   * one scale per tensor: s = amax|x| / 448 (s = 1 for an all-zero
-//     tensor); codes = e4m3(x / s), rounded to nearest even by
+//   * Q is multiplied by c0 = softmax scale * log2(e) before it is
+//     quantised, so that the attention kernel's score products come out in
+//     the log2 units its exponentials take;
+//   * one scale per tensor: for Q and K the smallest power of two s with
+//     amax|x| / s <= 448 (x = c0 * rotated Q, rotated K), so that the
+//     attention kernel applies s_q s_k exactly through the matrix core's
+//     power-of-two scale operands; for V s = amax|V| / 448; s = 1 for an
+//     all-zero tensor; codes = e4m3(x / s), rounded to nearest even by
 //     v_cvt_pk_fp8_f32 (OCP E4M3, largest finite 448).
 //   * V is written transposed, [B][Hkv][d][Nkp] with Nkp = Nk rounded up to
 //     a multiple of 64; within each block of 64 keys the keys are stored in
@@ -105,6 +111,16 @@ __device__ __forceinline__ float scale_of(unsigned amax_bits) {
   return a > 0.f ? a / E4M3_MAX : 1.0f;
 }
 
+// the smallest power of two >= amax * mult / 448 (1 for an all-zero tensor)
+__device__ __forceinline__ float pow2_scale_of(unsigned amax_bits, float mult) {
+  const float a = __uint_as_float(amax_bits);
+  if (!(a > 0.f)) return 1.0f;
+  const float t = a * mult / E4M3_MAX;
+  const unsigned b = __float_as_uint(t);
+  if ((b & 0x007fffffu) == 0u) return t;                      // already a power of two
+  return __uint_as_float(((b >> 23) + 1u) << 23);             // next power of two up
+}
+
 // 4 floats -> 4 e4m3 bytes (round to nearest even)
 __device__ __forceinline__ unsigned pack4(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -147,17 +163,18 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16* __restrict_
                                                        const float* __restrict__ signs, long long rows_q,
                                                        long long rows_k, uint8_t* __restrict__ q8,
                                                        uint8_t* __restrict__ k8, const unsigned* __restrict__ amax,
-                                                       float* __restrict__ descale) {
+                                                       float* __restrict__ descale, float c0) {
   const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int sub = threadIdx.x & 7;
   const int tensor = blockIdx.y;  // 0: Q, 1: K
   const long long rows = tensor == 0 ? rows_q : rows_k;
-  const float s = scale_of(amax[tensor]);
+  const float mult = tensor == 0 ? c0 : 1.0f;
+  const float s = pow2_scale_of(amax[tensor], mult);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     descale[tensor] = s;
     if (tensor == 0) descale[2] = scale_of(amax[2]);
   }
-  const float inv = 1.0f / s;
+  const float inv = mult / s;  // s is a power of two: the division is exact
   float x[D / 8] = {};
   const bool ok = row < rows;
   if (ok) load_row_part<D>((tensor == 0 ? q : k) + row * D, sub, x);
@@ -230,7 +247,7 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const __bf16* __restrict__
 
 template <int D>
 static hipError_t launch_prepare_d(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
-                                   float* descale, unsigned* amax, const float* signs, long long rows_q,
+                                   float* descale, unsigned* amax, const float* signs, float c0, long long rows_q,
                                    long long rows_k, long long heads_kv, int Nk, hipStream_t stream) {
   const int Nkp = (Nk + FP8_BC - 1) / FP8_BC * FP8_BC;
   hipLaunchKernelGGL(zero3_kernel, dim3(1), dim3(64), 0, stream, amax);
@@ -242,7 +259,7 @@ static hipError_t launch_prepare_d(const void* q, const void* k, const void* v, 
                      (const __bf16*)v, signs, rows_q, rows_k, amax);
   const dim3 g2((unsigned)((rmax + 31) / 32), 2);
   hipLaunchKernelGGL(quant_qk_kernel<D>, g2, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k, signs, rows_q,
-                     rows_k, (uint8_t*)q8, (uint8_t*)k8, (const unsigned*)amax, descale);
+                     rows_k, (uint8_t*)q8, (uint8_t*)k8, (const unsigned*)amax, descale, c0);
   const dim3 g3((unsigned)((long long)(Nkp / FP8_BC) * heads_kv));
   hipLaunchKernelGGL(quant_v_kernel<D>, g3, dim3(256), 0, stream, (const __bf16*)v, Nk, Nkp, (uint8_t*)v8t,
                      (const unsigned*)amax);
@@ -258,14 +275,17 @@ bool fp8_prepare_too_large(int B, int Hq, int Hkv, int Nq, int Nk) {
 }
 
 hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
-                              float* descale, unsigned* amax, const float* signs, int B, int Hq, int Hkv, int Nq,
-                              int Nk, int d, hipStream_t stream) {
+                              float* descale, unsigned* amax, const float* signs, float c0, int B, int Hq, int Hkv,
+                              int Nq, int Nk, int d, hipStream_t stream) {
   const long long rows_q = (long long)B * Hq * Nq, rows_k = (long long)B * Hkv * Nk;
   const long long heads_kv = (long long)B * Hkv;
   if (fp8_prepare_too_large(B, Hq, Hkv, Nq, Nk)) return hipErrorInvalidValue;
-  if (d == 64) return launch_prepare_d<64>(q, k, v, q8, k8, v8t, descale, amax, signs, rows_q, rows_k, heads_kv, Nk, stream);
-  if (d == 128) return launch_prepare_d<128>(q, k, v, q8, k8, v8t, descale, amax, signs, rows_q, rows_k, heads_kv, Nk, stream);
-  if (d == 256) return launch_prepare_d<256>(q, k, v, q8, k8, v8t, descale, amax, signs, rows_q, rows_k, heads_kv, Nk, stream);
+  if (d == 64) return launch_prepare_d<64>(q, k, v, q8, k8, v8t, descale, amax, signs, c0, rows_q, rows_k,
+                                                   heads_kv, Nk, stream);
+  if (d == 128) return launch_prepare_d<128>(q, k, v, q8, k8, v8t, descale, amax, signs, c0, rows_q, rows_k,
+                                                   heads_kv, Nk, stream);
+  if (d == 256) return launch_prepare_d<256>(q, k, v, q8, k8, v8t, descale, amax, signs, c0, rows_q, rows_k,
+                                                   heads_kv, Nk, stream);
   return hipErrorInvalidValue;
 }
 

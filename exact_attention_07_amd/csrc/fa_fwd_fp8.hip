@@ -35,13 +35,23 @@ namespace fa {
 //   (j/16)*32 + (j%16/4)*8 + h*4 + j%4; fa_fp8_prepare stores V^T with the
 //   keys of each 64-key block in exactly this order, so a lane's 32 bytes of
 //   a V^T row are contiguous.
-// Descales: the score scale folds s_q s_k into c, the epilogue multiplies O
-// by s_v / l.  P (at most 2^TAU = 256 < 448) is quantised unscaled.
+// Scores come out of the matrix core in the units the exponentials take:
+// fa_fp8_prepare quantises Q with the softmax scale and log2 e folded in and
+// with power-of-two scales s_q, s_k, so x = s_q s_k (K8 Q8^T) is exactly the
+// score in log2 units; the MFMA applies 2^(e_q + e_k) through its E8M0 scale
+// operands, and the first k-step of each block starts its accumulator at
+// -mu (mu the row's reference maximum), so the exponential takes the MFMA
+// result as it is: no multiply-add per score.  The epilogue multiplies O by
+// s_v / l.  P (at most 2^TAU = 256 < 448) is quantised unscaled.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x16 mfma_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+// the same with E8M0 scales (biased exponents: 127 = 2^0) on A and B
+__device__ __forceinline__ f32x16 mfma_fp8_scaled(i32x8 a, i32x8 b, f32x16 c, int ea, int eb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
 }
 __device__ __forceinline__ i32x8 lds_b256(LDS_AS const char* p) {
   const i32x4 a = *(LDS_AS const i32x4*)p, b = *(LDS_AS const i32x4*)(p + 16);
@@ -98,7 +108,7 @@ template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
 void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
                        const uint8_t* __restrict__ V8T, const float* __restrict__ descale,
-                       __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c0) {
+                       __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p) {
   constexpr int KB = BC / 32;      // 32-key blocks per tile
   constexpr int KS = D / 64;       // k-steps of S^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
@@ -143,8 +153,11 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
   const int kfull_w = CAUSAL ? min(Nk - 1, q0w + Nk - Nq) : Nk - 1;
   // tiles this wave computes (0 .. ntw - 1)
   const int ntw = (live && klast_w >= 0) ? min(nt, klast_w / BC + 1) : 0;
-  const float sq = descale[0], sk = descale[1], sv = descale[2];
-  const float c = c0 * sq * sk;
+  // E8M0 scales of the score product: the biased exponents of the power-of-two
+  // s_q (for B, the Q codes) and s_k (for A, the K codes)
+  const int e_q = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(descale[0]) >> 23) & 0xff));
+  const int e_k = __builtin_amdgcn_readfirstlane((int)((__float_as_uint(descale[1]) >> 23) & 0xff));
+  const float sv = descale[2];
 
   const size_t qoff = (size_t)(w.b * p.Hq + hq) * Nq * D;
   const size_t koff = (size_t)(w.b * p.Hkv + w.hkv) * Nk * D;
@@ -205,16 +218,22 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
     for (int kb = 0; kb < KB; ++kb) sa[kb] = (f32x16){};
 #pragma unroll
     for (int t = 0; t < NMF; ++t)
-      sa[t % KB] = mfma_fp8(lds_b256(kslot(P0{}) + koff_l + (t % KB) * 32 * RSK + (t / KB) * 64), qf[t / KB], sa[t % KB]);
+      sa[t % KB] = mfma_fp8_scaled(lds_b256(kslot(P0{}) + koff_l + (t % KB) * 32 * RSK + (t / KB) * 64), qf[t / KB],
+                                   sa[t % KB], e_k, e_q);
   }
+  // the accumulator start of a score block: -mu of the lane's row (mu = the
+  // reference maximum, 0 while the row has none)
+  f32x16 negmu;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negmu[i] = 0.f;
   i32x8 pa, pb;
 #pragma unroll
   for (int i = 0; i < 8; ++i) pb[i] = 0;
 
-  // score sc of s: exponential against mu, row-sum part; byte sc of the P
-  // fragment (the odd member of a pair packs the pair into its half-dword)
-  auto score = [&](const f32x16 (&s)[KB], i32x8& pf, int sc, float mu, float& part0, float& part1, float& even) {
-    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[sc / 16][sc % 16], c, -mu));
+  // score sc of s (already x - mu): exponential, row-sum part; byte sc of the
+  // P fragment (the odd member of a pair packs the pair into its half-dword)
+  auto score = [&](const f32x16 (&s)[KB], i32x8& pf, int sc, float& part0, float& part1, float& even) {
+    const float pv = __builtin_amdgcn_exp2f(s[sc / 16][sc % 16]);
     if (sc & 1) {
       part1 += pv;
       const int pp = sc / 2;
@@ -249,16 +268,16 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
           if ((i >> 2) * 8 + (i & 3) > kmax) s[kb][i] = NEG_INF;
       }
     }
-    float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
+    // s holds x - mu: it was started at -mu, or shifted to it when the
+    // slow path moved the reference
+    const float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
     float part0 = 0.f, part1 = 0.f, even = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sn[kb] = (f32x16){};
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
       const int m = ch / 2;
       if (ch % 2 == 0) {
         // S_{j+1}: MFMA m (k-step m / KB, key block m % KB)
-        sn[m % KB] = mfma_fp8(kbuf[m % KPF], qf[m / KB], sn[m % KB]);
+        sn[m % KB] = mfma_fp8_scaled(kbuf[m % KPF], qf[m / KB], (m / KB == 0) ? negmu : sn[m % KB], e_k, e_q);
         if (m + KPF < NMF)
           kbuf[m % KPF] = lds_b256(knext + ((m + KPF) % KB) * 32 * RSK + ((m + KPF) / KB) * 64);
       } else {
@@ -267,7 +286,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
         if (m + VPF < NPV) vbuf[m % VPF] = lds_b256(vprev + (m + VPF) * 32 * RSV);
       }
 #pragma unroll
-      for (int sc = ch * SPC; sc < (ch + 1) * SPC; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      for (int sc = ch * SPC; sc < (ch + 1) * SPC; ++sc) score(s, pf, sc, part0, part1, even);
       // the copy instructions over the first half of the chunks: each then
       // has more than half an iteration to land (measured 1-2 % faster than
       // spreading them over all chunks)
@@ -287,7 +306,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      m_run = fmaxf(m_run, xhalf_max(mx) * c);
+      m_run = fmaxf(m_run, xhalf_max(mx) + mu);
       if (__ballot(m_run > m_ref + TAU)) {
         const float alpha = (m_run == NEG_INF) ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_run);
         lsum *= alpha;
@@ -295,10 +314,20 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         m_ref = m_run;
       }
-      mu = (m_ref == NEG_INF) ? 0.f : m_ref;
+      // shift both score buffers (this tile's and S_{j+1}, complete by
+      // now) to the new reference, and start later blocks at it
+      const float mu2 = (m_ref == NEG_INF) ? 0.f : m_ref;
+      const float dm = mu - mu2;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] += dm;
+        sn[kb] += dm;
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) negmu[i] = -mu2;
       part0 = part1 = 0.f;
 #pragma unroll
-      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even);
+      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, part0, part1, even);
       part = part0 + part1;
     }
     lsum += part;
@@ -352,7 +381,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
 #define FA_INST_FP8(DD, CC, NN)                                                                              \
   template __global__ void fa_fwd_fp8_kernel<DD, CC, NN>(const uint8_t* __restrict__, const uint8_t* __restrict__, \
                                                          const uint8_t* __restrict__, const float* __restrict__,   \
-                                                         __bf16* __restrict__, float* __restrict__, fa_plan_t, float);
+                                                         __bf16* __restrict__, float* __restrict__, fa_plan_t);
 #define FA_FP8_VARIANTS(X)                                                                                  \
   X(64, false, 1) X(64, false, 2) X(64, false, 4) X(64, true, 1) X(64, true, 2) X(64, true, 4)              \
   X(128, false, 1) X(128, false, 2) X(128, false, 4) X(128, true, 1) X(128, true, 2) X(128, true, 4)        \
@@ -360,12 +389,11 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
 FA_FP8_VARIANTS(FA_INST_FP8)
 
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale, void* o, float* lse,
-                          const fa_plan_t& p, int d, float c, hipStream_t stream) {
+                          const fa_plan_t& p, int d, hipStream_t stream) {
 #define FA_CASE_FP8(DD, CC, NN)                                                                           \
   if (d == DD && (p.causal != 0) == CC && p.nw == NN) {                                                 \
     hipLaunchKernelGGL((fa_fwd_fp8_kernel<DD, CC, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream,     \
-                       (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8t, descale, (__bf16*)o, lse, p, \
-                       c);                                                                              \
+                       (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8t, descale, (__bf16*)o, lse, p); \
     return hipGetLastError();                                                                           \
   }
   FA_FP8_VARIANTS(FA_CASE_FP8)

@@ -50,20 +50,22 @@ hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, floa
 hipError_t launch_merge(const float* ows, const float* lws, void* o, float* lse, int nsplit, long long rows, int d,
                         hipStream_t stream);
 
-// Enqueue the fp8 forward kernel (operands from launch_fp8_prepare).
+// Enqueue the fp8 forward kernel (operands from launch_fp8_prepare, whose
+// Q codes carry the softmax scale in log2 units).
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale, void* o, float* lse,
-                          const fa_plan_t& p, int d, float c, hipStream_t stream);
+                          const fa_plan_t& p, int d, hipStream_t stream);
 
 // True if a preparation of this shape needs a grid of 2^31 or more
 // workgroups (such shapes are rejected).
 bool fp8_prepare_too_large(int B, int Hq, int Hkv, int Nq, int Nk);
 
-// Enqueue the fp8 preparation: optional Hadamard rotation of Q and K,
-// per-tensor amax, e4m3 quantisation, V transposed (fa.h describes the
-// layouts).  amax: 3 device words of workspace.
+// Enqueue the fp8 preparation: optional Hadamard rotation of Q and K, Q
+// multiplied by c0 = softmax scale * log2(e), per-tensor amax, e4m3
+// quantisation (power-of-two scales for Q and K), V transposed (fa.h
+// describes the layouts).  amax: 3 device words of workspace.
 hipError_t launch_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
-                              float* descale, unsigned* amax, const float* signs, int B, int Hq, int Hkv, int Nq,
-                              int Nk, int d, hipStream_t stream);
+                              float* descale, unsigned* amax, const float* signs, float c0, int B, int Hq, int Hkv,
+                              int Nq, int Nk, int d, hipStream_t stream);
 
 // Backward pass: keys per wave and most waves per workgroup of the dK/dV
 // kernel for head dimension d.

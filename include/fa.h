@@ -68,7 +68,7 @@ typedef enum fa_status {
 } fa_status;
 
 /* Version of this interface; bumped on any incompatible change. */
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 int fa_abi_version(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -158,39 +158,54 @@ fa_status fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, vo
  *             and K, H_d the Sylvester Hadamard matrix (H_1 = [1],
  *             H_2n = [[H, H], [H, -H]]); V is not rotated.  The product
  *             Q K^T is unchanged by the rotation.
+ *   scale     the softmax scale the codes are prepared for (finite, > 0;
+ *             usually 1/sqrt(d)): Q is multiplied by c0 = scale * log2(e)
+ *             before it is quantised, so that fa_fwd_fp8's score products
+ *             come out in the base-2 units its exponentials take
  *   q8, k8    OCP E4M3 codes (1 byte each), same layouts as q and k
  *   v8t       E4M3 codes of V transposed: [B][Hkv][d][Nkp], Nkp = Nk rounded
  *             up to a multiple of 64.  Within each block of 64 keys, key
  *             kk = 32 a + 8 g + 4 h + r (a, h in {0,1}, g, r in {0..3}) is
  *             stored at position 32 h + 16 a + 4 g + r; keys >= Nk are zero.
- *   descale   3 fp32 (device): s_q, s_k, s_v, with s = amax|x| / 448 over the
- *             whole (rotated) tensor (1 for an all-zero tensor); x is
- *             represented by s * decode(code).
+ *   descale   3 fp32 (device): s_q, s_k, s_v.  s_q is the smallest power of
+ *             two with amax|c0 x| / s_q <= 448 over the whole rotated Q
+ *             (x = rotated query), and c0 x is represented by
+ *             s_q * decode(code); s_k is the smallest power of two with
+ *             amax|x| / s_k <= 448 over the whole rotated K; s_v =
+ *             amax|V| / 448; x (rotated K, V) is represented by
+ *             s * decode(code); s = 1 for an all-zero tensor.  Power-of-two
+ *             s_q and s_k let the attention kernel apply them exactly through
+ *             the matrix core's scale operands; in a floating-point format the
+ *             choice of scale within a factor of two changes no code's
+ *             relative precision.
  *   amax_ws   3 uint32 of device workspace (zeroed and used inside).
  * Codes are rounded to nearest even; |x| / s <= 448 by construction.  The
  * scales stay on the device: nothing is synchronised.  Pointers of the code
  * tensors and q, k, v are 16-byte aligned; descale, amax_ws, signs 4-byte.
  */
 fa_status fa_fp8_prepare(const void* q, const void* k, const void* v, void* q8, void* k8, void* v8t,
-                         float* descale, unsigned* amax_ws, const float* signs,
+                         float* descale, unsigned* amax_ws, const float* signs, float scale,
                          int B, int Hq, int Hkv, int Nq, int Nk, int d, void* stream);
 
 /*
  * FP8 forward pass on the output of fa_fp8_prepare: O (bf16) and LSE (fp32)
- * of softmax(scale * Q K^T) V ("FlashAttention (SV)", section "Problematik
+ * of softmax(scale * Q K^T) V, with the scale given to fa_fp8_prepare (the
+ * Q codes carry it) ("FlashAttention (SV)", section "Problematik
  * med standard-attention") with Q, K, V represented by their codes and
  * scales, both products on 8-bit floating-point matrix instructions
  * ("FlashAttention-3 — 闪电注意力-3", section on the Hopper GPU's new
  * hardware features: FP8 at twice the FP16 rate; section on low precision
  * and the reduction of quantisation error: Q and K rotated before
- * quantisation, which leaves Q K^T unchanged).  Both products run on e4m3 MFMA with fp32 accumulation; the
- * probabilities multiply V as e4m3 values (unscaled, at most 2^8), while the
- * row sums and the LSE use the fp32 probabilities.  Conventions (GQA,
- * causal, errors) as for fa_fwd.
+ * quantisation, which leaves Q K^T unchanged).  Both products run on e4m3
+ * MFMA with fp32 accumulation; the probabilities multiply V as e4m3 values
+ * (unscaled, at most 2^8), while the row sums and the LSE use the fp32
+ * probabilities.  descale[0] and descale[1] must be powers of two (as
+ * fa_fp8_prepare writes them; only their exponents are used).  Conventions
+ * (GQA, causal, errors) as for fa_fwd.
  */
 fa_status fa_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale,
                      void* o, float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
-                     float scale, int causal, void* stream);
+                     int causal, void* stream);
 
 /*
  * Backward pass (bfloat16): the gradients of L with respect to Q, K and V for

@@ -149,7 +149,8 @@ def compare_fp8_all_heads(q, k, v, scale: float, runs, workers: int | None = Non
 
     q, k, v: the bf16 source (uint16 bit patterns), [B, H, N, d] (MHA).
     runs: {name: (o [B, H, N, d] bf16 bits, q8, k8, v8 (e4m3 codes; v8 in
-    [B, Hkv, Nk, d] key order), (s_q, s_k, s_v))}.
+    [B, Hkv, Nk, d] key order), (s_q, s_k, s_v))}, each tensor represented
+    by s * decode(code) (for Q codes that carry a factor c0, s_q / c0).
     Returns {name: {"gpu_true", "gpu_deq", "deq_true"}}, each with cosine,
     rmse, mean_abs, max_abs over all elements: the GPU output against the
     oracle on the source (the accuracy of the fp8 path), against the oracle on

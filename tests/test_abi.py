@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.fa_abi_version() == 1
+    assert lib.fa_abi_version() == 2
     for s in range(11):
         assert len(lib.fa_status_string(s)) > 0
     assert lib.fa_status_string(123) == b"unknown status"
@@ -71,8 +71,8 @@ def test_invalid_arguments_are_rejected_on_the_host(lib, fn, kw, status):
     assert call(lib, fn, **kw) == status
 
 
-FP8_GOOD = dict(q=P, k=P, v=P, q8=P, k8=P, v8t=P, descale=P, amax=P, signs=P, B=1, Hq=4, Hkv=2, Nq=10, Nk=10,
-                d=128)
+FP8_GOOD = dict(q=P, k=P, v=P, q8=P, k8=P, v8t=P, descale=P, amax=P, signs=P, scale=0.1, B=1, Hq=4, Hkv=2, Nq=10,
+                Nk=10, d=128)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -80,25 +80,25 @@ FP8_GOOD = dict(q=P, k=P, v=P, q8=P, k8=P, v8t=P, descale=P, amax=P, signs=P, B=
     (dict(v8t=None), 1), (dict(descale=None), 1), (dict(amax=None), 1),
     (dict(B=0), 2), (dict(Nk=0), 2), (dict(Nq=-3), 2), (dict(d=96), 3), (dict(Hq=5, Hkv=2), 4),
     (dict(q8=P + 8), 5), (dict(v8t=P + 1), 5), (dict(descale=P + 2), 5), (dict(amax=P + 1), 5),
-    (dict(signs=P + 2), 5),
+    (dict(signs=P + 2), 5), (dict(scale=0.0), 6), (dict(scale=-1.0), 6), (dict(scale=float("nan")), 6),
+    (dict(scale=float("inf")), 6),
 ])
 def test_fp8_prepare_rejects_invalid_arguments(lib, kw, status):
     a = dict(FP8_GOOD)
     a.update(kw)
     assert lib.fa_fp8_prepare(a["q"], a["k"], a["v"], a["q8"], a["k8"], a["v8t"], a["descale"], a["amax"],
-                              a["signs"], a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"], None) == status
+                              a["signs"], ctypes.c_float(a["scale"]), a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                              a["d"], None) == status
 
 
-FWD8_GOOD = dict(q8=P, k8=P, v8t=P, descale=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=10, Nk=10, d=128, scale=0.1,
-                 causal=0)
+FWD8_GOOD = dict(q8=P, k8=P, v8t=P, descale=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=10, Nk=10, d=128, causal=0)
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q8=None), 1), (dict(k8=None), 1), (dict(v8t=None), 1), (dict(descale=None), 1), (dict(o=None), 1),
     (dict(Hkv=0), 2), (dict(d=64 + 16), 3), (dict(Hq=3, Hkv=2), 4),
     (dict(o=P + 8), 5), (dict(lse=P + 4), 5), (dict(descale=P + 1), 5),
-    (dict(scale=0.0), 6), (dict(scale=float("nan")), 6), (dict(causal=3), 8),
-    (dict(Nk=(1 << 31) // (4 * 256)), 2),
+    (dict(causal=3), 8), (dict(Nk=(1 << 31) // (4 * 256)), 2),
 ])
 def test_fp8_forward_rejects_invalid_arguments(lib, kw, status):
     a = dict(FWD8_GOOD)
@@ -106,7 +106,7 @@ def test_fp8_forward_rejects_invalid_arguments(lib, kw, status):
     if "Nk" in kw:
         a["d"] = 256
     assert lib.fa_fwd_fp8(a["q8"], a["k8"], a["v8t"], a["descale"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
-                          a["Nq"], a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], None) == status
+                          a["Nq"], a["Nk"], a["d"], a["causal"], None) == status
 
 
 SPLIT_GOOD = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=8, Hkv=2, Nq=1, Nk=4096, d=128, scale=0.1, causal=0, nsplit=0,

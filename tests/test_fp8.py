@@ -67,7 +67,7 @@ def bf16_from_f64(a):
     return bits
 
 
-def run_prepare(api, q, k, v, signs=None, descale=None, amax_ws=None):
+def run_prepare(api, q, k, v, signs=None, descale=None, amax_ws=None, scale=None):
     """fa_fp8_prepare on device bf16 tensors; returns host copies (q8, k8, v8t, descale)."""
     B, Hq, Nq, d = q.shape
     _, Hkv, Nk, _ = k.shape
@@ -76,14 +76,21 @@ def run_prepare(api, q, k, v, signs=None, descale=None, amax_ws=None):
     v8t = torch.full((B, Hkv, d, api.padded_keys(Nk)), 0x55, dtype=torch.uint8, device="cuda")
     descale = torch.empty(3, dtype=torch.float32, device="cuda") if descale is None else descale
     amax_ws = torch.full((3,), 12345, dtype=torch.int32, device="cuda") if amax_ws is None else amax_ws
-    api.fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs)
+    api.fa_fp8_prepare(q, k, v, q8, k8, v8t, descale, amax_ws, signs, scale)
     torch.cuda.synchronize()
     return q8.cpu().numpy(), k8.cpu().numpy(), v8t.cpu().numpy(), descale.cpu().numpy().astype(np.float64)
 
 
-def dequantise_gpu(q8, k8, v8t, descale, nk):
-    """fp64 Q, K, V that the GPU codes stand for (V back in [B, Hkv, Nk, d])."""
-    q = e4m3_decode(q8) * descale[0]
+def gpu_c0(scale):
+    """The factor fa_fp8_prepare folds into Q: scale (passed as fp32) times
+    log2(e), rounded to fp32."""
+    return float(np.float32(float(np.float32(scale)) * np.log2(np.e)))
+
+
+def dequantise_gpu(q8, k8, v8t, descale, nk, scale):
+    """fp64 Q, K, V that the GPU codes stand for (V back in [B, Hkv, Nk, d]);
+    the Q codes carry c0, which is divided out."""
+    q = e4m3_decode(q8) * (descale[0] / gpu_c0(scale))
     k = e4m3_decode(k8) * descale[1]
     v = np.swapaxes(e4m3_decode(key_order(v8t)[..., :nk]) * descale[2], 2, 3)
     return q, k, v
@@ -158,14 +165,20 @@ def test_prepare_matches_the_oracle(api, d, rotate):
     signs = torch.from_numpy(x["signs"]).cuda() if rotate else None
     ws = torch.full((3,), -1, dtype=torch.int32, device="cuda")
     ds = torch.empty(3, dtype=torch.float32, device="cuda")
+    scale = 0.7 / np.sqrt(d)
     # a first call on 4x larger tensors leaves a larger amax in the workspace:
     # the second call must not see it
-    run_prepare(api, q * 4, k * 4, v * 4, signs, ds, ws)
-    q8, k8, v8t, descale = run_prepare(api, q, k, v, signs, ds, ws)
+    run_prepare(api, q * 4, k * 4, v * 4, signs, ds, ws, scale)
+    q8, k8, v8t, descale = run_prepare(api, q, k, v, signs, ds, ws, scale)
     qf, kf, vf = (bf16_bits_to_f64(x[t]) for t in "qkv")
-    ref = ofp8.prepare(qf, kf, vf, x["signs"] if rotate else None)
-    np.testing.assert_allclose(descale, ref["scales"], rtol=1e-5 if rotate else 2 ** -23)
-    check_codes(q8, ref["qr"], descale[0], "Q")
+    ref = ofp8.prepare(qf, kf, vf, x["signs"] if rotate else None, scale)
+    # s_q and s_k are powers of two (equal unless the fp32 and fp64 amax
+    # straddle one, which these inputs do not), s_v amax / 448
+    for s in descale[:2]:
+        assert np.frexp(s)[0] == 0.5, descale
+    np.testing.assert_array_equal(descale[:2], ref["scales"][:2])
+    np.testing.assert_allclose(descale[2], ref["scales"][2], rtol=2 ** -23)
+    check_codes(q8, gpu_c0(scale) * ref["qr"], descale[0], "Q")
     check_codes(k8, ref["kr"], descale[1], "K")
     vk = key_order(v8t)
     check_codes(np.swapaxes(vk[..., :Nk], 2, 3), vf, descale[2], "V")
@@ -195,7 +208,9 @@ def integer_logit_inputs(B, Hq, Hkv, Nq, Nk, d, seed):
     = K[0,0,0,0] = 7, which makes key 0 dominate that one query row.  With
     scale = ln 2 every probability the kernel uses is 2^(integer) in
     [2^-8, 2^8] (masked keys 0; in the dominated row the other keys fall
-    below the e4m3 range), exactly representable in e4m3.  All code products
+    below the e4m3 range), exactly representable in e4m3.  The factor
+    c0 = scale * log2(e) that the Q codes carry is 1 in fp32 for this scale,
+    so the Q scale stays 2^-6.  All code products
     of Q K^T are multiples of 64 * 64, far above the granularity of the fp8
     MFMA's grouped sums, so the logits are exact.
     """
@@ -312,7 +327,7 @@ def run_fp8(api, x, w, rotate):
     o, lse, prep = api.attention_fp8(q, k, v, causal=w.causal, scale=w.softmax_scale, signs=signs)
     torch.cuda.synchronize()
     deq = dequantise_gpu(prep["q8"].cpu().numpy(), prep["k8"].cpu().numpy(), prep["v8t"].cpu().numpy(),
-                         prep["descale"].cpu().numpy().astype(np.float64), w.Nk)
+                         prep["descale"].cpu().numpy().astype(np.float64), w.Nk, w.softmax_scale)
     return out_to_f64(o), lse.cpu().numpy().astype(np.float64), deq
 
 
@@ -375,7 +390,7 @@ def test_fp8_deterministic_and_writes_stay_inside_outputs(api):
         lbuf = torch.full((2 * 77 + 64,), 7.0, dtype=torch.float32, device="cuda")
         o = buf[:n].view(q.shape)
         lse = lbuf[:2 * 77].view(1, 2, 77)
-        api.fa_fwd_fp8(prep["q8"], prep["k8"], prep["v8t"], prep["descale"], o, lse, 1 / np.sqrt(128), True)
+        api.fa_fwd_fp8(prep["q8"], prep["k8"], prep["v8t"], prep["descale"], o, lse, True)
         torch.cuda.synchronize()
         assert (buf[n:] == 7.0).all() and (lbuf[2 * 77:] == 7.0).all()
         outs.append((o.clone(), lse.clone()))
@@ -406,7 +421,7 @@ def test_fp8_workload_sampled_rows(api):
         report[rotate] = fp8_errors(got, o_true)
         # LSE against the oracle on the dequantised codes of the sampled rows
         qq, kq, vq = dequantise_gpu(prep["q8"].cpu().numpy(), prep["k8"].cpu().numpy(), prep["v8t"].cpu().numpy(),
-                                    prep["descale"].cpu().numpy().astype(np.float64), w.Nk)
+                                    prep["descale"].cpu().numpy().astype(np.float64), w.Nk, w.softmax_scale)
         _, lse_q = attention_rows_fp64(qq, kq, vq, w.softmax_scale, False, rows)
         g = w.Hq // w.Hkv
         bound = np.array([score_error_bound(qq[b:b + 1, h:h + 1, i:i + 1], kq[b:b + 1, h // g:h // g + 1],
@@ -451,7 +466,7 @@ def test_fp8_workload_every_element(api):
         v8 = np.ascontiguousarray(np.swapaxes(key_order(prep["v8t"].cpu().numpy())[..., :w.Nk], 2, 3))
         runs["rotated" if rotate else "unrotated"] = (
             o.view(torch.int16).cpu().numpy().view(np.uint16), prep["q8"].cpu().numpy(), prep["k8"].cpu().numpy(),
-            v8, prep["descale"].cpu().numpy().astype(np.float64))
+            v8, prep["descale"].cpu().numpy().astype(np.float64) / [gpu_c0(w.softmax_scale), 1.0, 1.0])
         del o, lse, prep
     del q, k, v
     st = compare_fp8_all_heads(x["q"], x["k"], x["v"], w.softmax_scale, runs)

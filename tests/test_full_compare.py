@@ -63,17 +63,18 @@ def test_fp8_pool_separates_format_error_from_kernel_error():
     w = gen.workload(1, 3, 3, 50, 90, 64, dtype="fp8", outlier_prob=0.01)
     x = gen.make_inputs(w, (13,))
     q, k, v = (bf16_bits_to_f64(x[t]) for t in "qkv")
-    prep = ofp8.prepare(q, k, v, x["signs"])
+    prep = ofp8.prepare(q, k, v, x["signs"], w.softmax_scale)
     qd, kd, vd = ofp8.dequantised(prep)
     o_deq, _ = attention_fp64(qd, kd, vd, w.softmax_scale, False)
     o_true, _ = attention_fp64(q, k, v, w.softmax_scale, False)
     o_bits = gen.f32_to_bf16_bits(o_deq.astype(np.float32))
     v8 = np.ascontiguousarray(np.swapaxes(prep["v8t"], 2, 3))
+    sq, sk, sv = prep["scales"]
     st = compare_fp8_all_heads(x["q"], x["k"], x["v"], w.softmax_scale,
-                               {"r": (o_bits, prep["q8"], prep["k8"], v8, prep["scales"])}, workers=2)["r"]
+                               {"r": (o_bits, prep["q8"], prep["k8"], v8, (sq / prep["c0"], sk, sv))}, workers=2)["r"]
     assert st["gpu_deq"]["max_abs"] <= 2.0 ** -8 * np.abs(o_deq).max()
     assert st["gpu_deq"]["cosine"] > 0.99999
     ref = _direct(o_deq, o_true)
     for key, val in ref.items():
         assert abs(st["deq_true"][key] - val) <= 1e-12 * max(1.0, abs(val)), (key, st["deq_true"][key], val)
-    assert np.array_equal(e4m3_decode(prep["q8"]) * prep["scales"][0], qd)
+    np.testing.assert_allclose(e4m3_decode(prep["q8"]) * (sq / prep["c0"]), qd, rtol=1e-15, atol=0)

@@ -326,13 +326,33 @@ def test_quantise_per_tensor():
     assert s0 == 1.0 and (formats.e4m3_decode(z) == 0).all()
 
 
+@pytest.mark.parametrize("amax", [448.0, 447.0, 449.0, 1.0, 3.5, 2.0 ** -20, 7e5])
+def test_quantise_power_of_two_scale(amax):
+    # the scale is a power of two s with amax / s in (224, 448]; a tensor whose
+    # amax is 448 times a power of two gets exactly that power
+    x = np.array([0.25 * amax, -amax, 0.0])
+    codes, s = fp8.quantise(x, pow2=True)
+    m, e = math.frexp(s)
+    assert m == 0.5
+    assert 224.0 < amax / s <= 448.0
+    if amax == 448.0:
+        assert s == 1.0
+    deq = formats.e4m3_decode(codes) * s
+    assert abs(deq[1] + amax) <= amax * 2.0 ** -4   # within half a step of the top binade
+    assert deq[2] == 0.0
+
+
 def test_prepare_layouts_and_product():
     rng = np.random.default_rng(14)
     d = 16
     q, k, v = _rand(rng, 1, 2, 5, d), _rand(rng, 1, 1, 6, d), _rand(rng, 1, 1, 6, d)
     signs = rng.integers(0, 2, d) * 2 - 1.0
-    p = fp8.prepare(q, k, v, signs)
+    p = fp8.prepare(q, k, v, signs, scale=0.3)
     assert p["q8"].shape == q.shape and p["k8"].shape == k.shape and p["v8t"].shape == (1, 1, d, 6)
+    assert abs(p["c0"] - 0.3 / math.log(2.0)) <= 1e-15
+    # the query codes carry c0: decode(q8) * s_q approximates c0 * (rotated Q)
+    qc = formats.e4m3_decode(p["q8"]) * p["scales"][0]
+    assert np.abs(qc - p["c0"] * p["qr"]).max() <= p["c0"] * np.abs(p["qr"]).max() / 16
     qd, kd, vd = fp8.dequantised(p)
     assert vd.shape == v.shape
     # quantised rotated product approximates the unrotated product
