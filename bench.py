@@ -34,6 +34,14 @@ five matrix products of the gradient; the roofline is the dK/dV kernel with
 its four of them (S, dP, dV, dK) against its own launch time.  The dQ kernel
 recomputes S and dP, so only its dQ product counts as algorithmic work.
 
+--ceiling-sweep measures only fa_mfma_ceiling (bf16 and fp8 MFMA loops, two
+waves per SIMD) with random operands and with constant ones, and prints one
+JSON line with the rate of each and the clock that rate implies (the loop is
+bound by the matrix pipe: rate / (CUs x 4 SIMDs x flops per clock per SIMD)).
+Under rocprofv3 counters (GRBM_GUI_ACTIVE) the same run shows the clock
+directly: the evidence that on this chip the clock under dense matrix work,
+and hence the reachable matrix rate, depends on the data the MFMAs toggle.
+
 --config decode measures the key-split path (fa_fwd_splitkv: parts over key
 ranges merged on the GPU) on a GQA decoding step, B=8 sequences, Hq=32,
 Hkv=8, one query each over Nk=32768 keys, d=128.  That path is bound by HBM
@@ -303,6 +311,39 @@ def measured_ceiling(torch, api, fp8: bool, stream, span_ms: float):
                     f"two waves per SIMD, toggling operands, median of {n} launches right after the timed steps"}
 
 
+def ceiling_sweep(torch, api, launches: int, warm: int):
+    """fa_mfma_ceiling for bf16 and fp8 with random operands, then constant
+    ones: median rate over `launches` launches, after `warm` untimed ones
+    that bring the clock to its steady state under that load, and the clock
+    the rate implies.  Dispatch order (for counter runs): per dtype, random
+    then constant, each `warm` + `launches` launches."""
+    stream = torch.cuda.current_stream()
+    out = torch.empty(api.mfma_ceiling_out_bytes() // 4, dtype=torch.float32, device="cuda")
+    rows = []
+    for fp8 in (False, True):
+        iters = 250 if fp8 else 500
+        per_clock = 256 * 4 * (2048 if fp8 else 1024)   # dense flops per clock of the chip
+        for random in (True, False):
+            for _ in range(warm):
+                api.mfma_ceiling(out, fp8, iters, random, stream)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+            for a, b in ev:
+                a.record(stream)
+                api.mfma_ceiling(out, fp8, iters, random, stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+            ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+            tf = api.mfma_ceiling_flops(fp8, iters) / (ms * 1e-3) / 1e12
+            rows.append({"mfma": "v_mfma_f32_32x32x64_f8f6f4" if fp8 else "v_mfma_f32_32x32x16_bf16",
+                         "operands": "random" if random else "constant", "launch_ms": round(ms, 4),
+                         "tflops": round(tf, 1), "implied_clock_ghz": round(tf * 1e12 / per_clock / 1e9, 3),
+                         "nominal_peak_tflops": 5000.0 if fp8 else 2500.0})
+            log(f"ceiling {rows[-1]['mfma']} {rows[-1]['operands']}: {tf:.1f} TFLOP/s, "
+                f"{rows[-1]['implied_clock_ghz']} GHz implied ({launches} launches of {ms:.3f} ms)")
+    print(json.dumps({"metric": "MFMA-only loop rate by operand data", "unit": "TFLOP/s", "launches": launches,
+                      "warm_launches": warm, "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +356,10 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured MFMA ceiling (profiling runs)")
     ap.add_argument("--no-compare", action="store_true",
                     help="decode: skip the comparison run without the key split (profiling runs)")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="measure only the MFMA-only loop, random against constant operands (see above)")
+    ap.add_argument("--sweep-launches", type=int, default=60)
+    ap.add_argument("--sweep-warm", type=int, default=600, help="untimed launches before each case")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one 1 GiB device copy (reference for rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -327,6 +372,9 @@ def main():
     import torch
     from exact_attention_07_amd import api, gen
 
+    if args.ceiling_sweep:
+        ceiling_sweep(torch, api, args.sweep_launches, args.sweep_warm)
+        return
     if args.config == "backward":
         bench_backward(args, torch, api, gen)
         return

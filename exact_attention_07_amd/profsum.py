@@ -43,6 +43,7 @@ KERNEL_SOURCES = {
     "f32": [_CSRC + f for f in ("fa_fwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
     "fp8": [_CSRC + f for f in ("fa_fwd_fp8.hip", "fa_device.h", "plan.h")],
     "bwd": [_CSRC + f for f in ("fa_bwd.hip", "fa_frag.h", "fa_device.h", "plan.h")],
+    "ceiling": [_CSRC + "fa_ceiling.hip"],
 }
 KERNEL_NAME = {"bf16": "fa_fwd_bf16_kernel", "f32": "fa_fwd_f32_kernel", "fp8": "fa_fwd_fp8_kernel",
                "bwd": "fa_bwd_dkdv_kernel"}
@@ -147,6 +148,54 @@ def summarize(config, dirs, commands, out_path):
     return out_path
 
 
+def summarize_ceiling(dirs, commands, out_path, launches, warm):
+    """Counters of a `bench.py --ceiling-sweep` run: per MFMA loop (bf16,
+    fp8) and operand data (random, then constant, in dispatch order; each
+    `warm` untimed + `launches` timed launches), the mean clock and
+    matrix-pipe share over the timed launches."""
+    groups = {}
+    for d in dirs:
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        disp = _dispatch_counters(files[0], "mfma_loop_kernel")
+        for did in sorted(disp, key=int):
+            r = disp[did]
+            name = "fp8" if "<true>" in _kernel_name(files[0], did) else "bf16"
+            groups.setdefault((d, name), []).append(r)
+    lines = ["# rocprofv3 counters of fa_mfma_ceiling (MFMA-only loops, two waves per SIMD):",
+             "# random operands, then constant ones (bf16: 0.5 and 0.25; fp8: 1.0 in every byte)",
+             "# commands (from the repository root on the MI355X box), one counter pass each:"]
+    lines += [f"#   {c}" for c in commands]
+    lines.append("# values: mean over the timed launches of each case")
+    for (d, name), rows in sorted(groups.items(), key=lambda t: (t[0][1] != "bf16", t[0][0])):
+        per = warm + launches
+        if len(rows) != 2 * per:
+            raise SystemExit(f"{d} {name}: {len(rows)} dispatches, expected {2 * per}")
+        for k, what in enumerate(("random", "constant")):
+            part = rows[k * per + warm:(k + 1) * per]
+            ns = sum(r["_ns"] for r in part) / len(part)
+            lines.append(f"{name}_{what}_kernel_ns_under_counters: {ns:.0f}")
+            if "GRBM_GUI_ACTIVE" in part[0]:
+                clk = sum(r["GRBM_GUI_ACTIVE"] / N_XCD / r["_ns"] for r in part) / len(part)
+                lines.append(f"{name}_{what}_clock_ghz: {clk:.4f}")
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in part[0]:
+                    busy = sum(r["SQ_VALU_MFMA_BUSY_CYCLES"] / (r["GRBM_GUI_ACTIVE"] / N_XCD * 4 * N_CU)
+                               for r in part) / len(part)
+                    lines.append(f"{name}_{what}_mfma_busy: {busy:.4f}")
+    lines.append(f"kernel_source_sha256: {source_hash('ceiling')}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
+
+
+def _kernel_name(path: str, dispatch_id: str) -> str:
+    for r in csv.DictReader(open(path)):
+        if r["Dispatch_Id"] == dispatch_id:
+            return r["Kernel_Name"]
+    return ""
+
+
 def summary_name(config) -> str:
     """File name of a workload's counter summary under profiles/."""
     return f"counters_config{config}.txt" if isinstance(config, int) else f"counters_{config}.txt"
@@ -170,11 +219,16 @@ def load(config, root=ROOT):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", required=True)
+    ap.add_argument("--config", required=True, help="workload (1..5, decode, backward) or ceiling")
+    ap.add_argument("--launches", type=int, default=60, help="ceiling: timed launches per case")
+    ap.add_argument("--warm", type=int, default=600, help="ceiling: untimed launches before each case")
     ap.add_argument("--out", required=True)
     ap.add_argument("--cmd", action="append", default=[], help="command of a pass (repeat, in order)")
     ap.add_argument("dirs", nargs="+")
     a = ap.parse_args(argv)
+    if a.config == "ceiling":
+        print(summarize_ceiling(a.dirs, a.cmd, a.out, a.launches, a.warm))
+        return
     cfg = int(a.config) if a.config.isdigit() else a.config
     print(summarize(cfg, a.dirs, a.cmd, a.out))
 
