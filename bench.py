@@ -15,8 +15,9 @@ on the stream the kernels run on.  Prints one JSON line on stdout
   roofline  the attention kernel (its own launch time, from events around
             each launch: mean, median and min over the K launches) against
             the MI355X dense MFMA peak for its dtype; the HBM traffic, the
-            sustained clock and the MFMA-busy share measured by rocprofv3
-            counters on the same kernel source (profiles/counters_config<N>.txt;
+            sustained clock, the MFMA-busy share, the LDS bank-conflict rate
+            and the VALU mix measured by rocprofv3 counters on the same kernel
+            source (profiles/counters_config<N>.txt;
             omitted or null when the source changed since they were taken),
             with the fraction of the peak at that clock; and the measured MFMA
             ceiling (fa_mfma_ceiling, a loop of the same matrix instruction on
@@ -547,6 +548,9 @@ def main():
             "sustained_clock_ghz": round(clk, 4), "mfma_busy": float(counters.get("mfma_busy", "nan")),
             "peak_at_sustained_clock": round(peak_clk, 1),
             "frac_at_sustained_clock": round(kernel_tflops / peak_clk, 4),
+            "lds_bank_conflict_rate": float(counters.get("lds_bank_conflict_rate", "nan")),
+            "valu_insts_per_mfma": float(counters.get("valu_insts_per_mfma", "nan")),
+            "trans_share_of_valu": float(counters.get("trans_share", "nan")),
             "counters": "profiles/" + profsum.summary_name(args.config)})
     if ceiling:
         line["roofline"].update({"measured_mfma_ceiling": ceiling["tflops"],
