@@ -43,6 +43,10 @@ Under rocprofv3 counters (GRBM_GUI_ACTIVE) the same run shows the clock
 directly: the evidence that on this chip the clock under dense matrix work,
 and hence the reachable matrix rate, depends on the data the MFMAs toggle.
 
+--exp2-emulated Q times fa_fwd_exp2_emulated (Q of every four exponentials
+computed by a polynomial on the FMA pipe) in place of fa_fwd on a bf16
+workload; the line's config then names it.
+
 --config decode measures the key-split path (fa_fwd_splitkv: parts over key
 ranges merged on the GPU) on a GQA decoding step, B=8 sequences, Hq=32,
 Hkv=8, one query each over Nk=32768 keys, d=128.  That path is bound by HBM
@@ -357,6 +361,9 @@ def main():
     ap.add_argument("--no-ceiling", action="store_true", help="skip the measured MFMA ceiling (profiling runs)")
     ap.add_argument("--no-compare", action="store_true",
                     help="decode: skip the comparison run without the key split (profiling runs)")
+    ap.add_argument("--exp2-emulated", type=int, default=0, choices=(0, 1, 2),
+                    help="time fa_fwd_exp2_emulated with 1 or 2 of every 4 exponentials on the FMA pipe "
+                         "(bf16, d = 64 or 128) instead of fa_fwd")
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="measure only the MFMA-only loop, random against constant operands (see above)")
     ap.add_argument("--sweep-launches", type=int, default=60)
@@ -417,6 +424,15 @@ def main():
 
         def attend():
             api.fa_fwd_fp8(q8, k8, v8t, descale, o, lse, w.causal, stream)
+    elif args.exp2_emulated:
+        if w.dtype != "bf16" or w.d not in (64, 128):
+            raise SystemExit("--exp2-emulated needs a bf16 workload with d = 64 or 128")
+
+        def prepare():
+            pass
+
+        def attend():
+            api.fa_fwd_exp2_emulated(q, k, v, o, lse, w.softmax_scale, w.causal, args.exp2_emulated, stream)
     else:
         fwd = api.fa_fwd if w.dtype == "bf16" else api.fa_fwd_f32
 
@@ -510,8 +526,9 @@ def main():
         return
 
     peak = PEAK_TFLOPS[w.dtype]
-    counters = load_counters(args.config)
-    traffic = load_traffic(f"config{args.config}", w.dtype, counters)
+    # the counter summaries describe fa_fwd's kernels, not the emulated variant
+    counters = None if args.exp2_emulated else load_counters(args.config)
+    traffic = None if args.exp2_emulated else load_traffic(f"config{args.config}", w.dtype, counters)
     ceiling = None if args.no_ceiling else measured_ceiling(torch, api, w.dtype == "fp8", stream,
                                                             args.steps * kernel_ms)
     data = "synthetic (seeded N(0,1), generated on the host, resident in HBM before timing)"
@@ -556,6 +573,9 @@ def main():
         line["roofline"].update({"measured_mfma_ceiling": ceiling["tflops"],
                                  "frac_of_measured_ceiling": round(kernel_tflops / ceiling["tflops"], 4),
                                  "ceiling_measurement": ceiling["what"]})
+    if args.exp2_emulated:
+        line["config"]["entry_point"] = (f"fa_fwd_exp2_emulated: {args.exp2_emulated} of every 4 exponentials "
+                                         "on the FMA pipe")
     if w.dtype == "fp8":
         line["config"]["steps_in_a_step"] = "fa_fp8_prepare (rotation, scales, e4m3) + fa_fwd_fp8"
         line["prepare_ms"] = round(ms - kernel_ms, 5)

@@ -41,6 +41,8 @@ def lib() -> ctypes.CDLL:
         fn = getattr(L, name)
         fn.argtypes = fwd_args
         fn.restype = ctypes.c_int
+    L.fa_fwd_exp2_emulated.argtypes = fwd_args[:-1] + [i, vp]
+    L.fa_fwd_exp2_emulated.restype = ctypes.c_int
     L.fa_fp8_prepare.argtypes = [vp] * 9 + [f] + [i] * 6 + [vp]
     L.fa_fp8_prepare.restype = ctypes.c_int
     L.fa_fwd_fp8.argtypes = [vp] * 6 + [i] * 6 + [i, vp]
@@ -114,6 +116,18 @@ def fa_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v, o, lse)
     _check(lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
                         float(scale), int(bool(causal)), _stream(stream)), "fa_fwd")
+
+
+def fa_fwd_exp2_emulated(q, k, v, o, lse, scale: float, causal: bool, quarters: int, stream=None) -> None:
+    """fa_fwd with `quarters` (1 or 2) of every four exponentials computed on the FMA pipe (d = 64, 128)."""
+    import torch
+    for t in (q, k, v, o):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("fa_fwd_exp2_emulated takes bfloat16 q, k, v, o")
+    B, Hq, Hkv, Nq, Nk, d = _shapes(q, k, v, o, lse)
+    _check(lib().fa_fwd_exp2_emulated(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                                      float(scale), int(bool(causal)), int(quarters), _stream(stream)),
+           "fa_fwd_exp2_emulated")
 
 
 def fa_fwd_f32(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:

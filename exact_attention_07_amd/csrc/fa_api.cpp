@@ -47,13 +47,13 @@ enum { KIND_BF16 = 0, KIND_F32 = 1, KIND_FP8 = 2 };
 fa_plan_t plan_for(int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, int kind);
 
 fa_status forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
-                  int Nk, int d, float scale, int causal, void* stream, int f32) {
+                  int Nk, int d, float scale, int causal, void* stream, int f32, int emu = 0) {
   fa_status st = validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
   if (st != FA_OK) return st;
   const fa_plan_t p = plan_for(B, Hq, Hkv, Nq, Nk, d, causal, f32 ? KIND_F32 : KIND_BF16);
   if (p.nwg > 0x7fffffffLL) return FA_ERR_SHAPE;
   const float c = (float)((double)scale * LOG2E);
-  hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, nullptr, nullptr, (hipStream_t)stream);
+  hipError_t e = fa::launch_fwd(q, k, v, o, lse, p, d, c, f32, nullptr, nullptr, (hipStream_t)stream, emu);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -220,6 +220,15 @@ const char* fa_status_string(fa_status s) {
 fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Nq,
                  int Nk, int d, float scale, int causal, void* stream) {
   return forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream, 0);
+}
+
+fa_status fa_fwd_exp2_emulated(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+                               int Hkv, int Nq, int Nk, int d, float scale, int causal, int quarters, void* stream) {
+  const fa_status st = validate(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal);
+  if (st != FA_OK) return st;
+  if (d == 256) return FA_ERR_HEAD_DIM;  // its variants are built for d = 64 and 128
+  if (quarters != 1 && quarters != 2) return FA_ERR_FLAG;
+  return forward(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale, causal, stream, 0, quarters);
 }
 
 fa_status fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int Hq, int Hkv,

@@ -54,6 +54,7 @@
 #include <type_traits>
 
 #include "fa_device.h"
+#include "fa_exp2.h"
 #include "fa_frag.h"
 #include "fa_kernels.h"
 #include "plan.h"
@@ -326,7 +327,9 @@ __device__ __forceinline__ void mask_scores(Scores<D>& s, int j0, int query, int
 //
 // One work item (fa_decode of id) per call; a persistent workgroup calls it
 // once per item, with a barrier in between (the LDS ring is reused).
-template <int D, bool CAUSAL, int NW>
+// EMU: how many of every four exponentials run as the FMA-pipe polynomial
+// exp2_poly (fa_exp2.h) instead of v_exp_f32 (0 for fa_fwd).
+template <int D, bool CAUSAL, int NW, int EMU>
 __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                               const __bf16* __restrict__ V, __bf16* __restrict__ O,
                                               float* __restrict__ LSE, const fa_plan_t& p, float c,
@@ -463,7 +466,8 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
   auto score = [&](const Scores<D>& s, Probs& pf, int sc, float mu, float& part0, float& part1, float& even,
                    float& partq) {
     const int skb = sc / 16, si = sc % 16;
-    const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s.v[skb][0][si], c, -mu));
+    const float arg = __builtin_fmaf(s.v[skb][0][si], c, -mu);
+    const float pv = (EMU > 0 && (sc & 3) >= 4 - EMU) ? exp2_poly(arg) : __builtin_amdgcn_exp2f(arg);
     if (sc & 1) {
       part1 += pv;
       const unsigned pk = pack_bf16(even, pv);
@@ -636,19 +640,19 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
 // workgroup then takes its items one after another, so a CU's next item
 // starts without a new workgroup's dispatch, and the snake order over the
 // heaviest-first causal work gives every workgroup an even share.
-template <int D, bool CAUSAL, int NW>
+template <int D, bool CAUSAL, int NW, int EMU>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Cfg<D, false>::WAVES_PER_SIMD)))
 void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
                         __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p, float c,
                         float* __restrict__ OWS, float* __restrict__ LWS) {
   if constexpr (!((D == 128 && NW == 8) || (D == 256 && NW == 4) || (CAUSAL && NW == 4 && (D == 64 || D == 128)))) {
-    fwd_bf16_item<D, CAUSAL, NW>(Q, K, V, O, LSE, p, c, OWS, LWS, blockIdx.x);
+    fwd_bf16_item<D, CAUSAL, NW, EMU>(Q, K, V, O, LSE, p, c, OWS, LWS, blockIdx.x);
   } else {
     for (unsigned r = 0;; ++r) {
       const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
       if (id == ~0u) break;
       if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
-      fwd_bf16_item<D, CAUSAL, NW>(Q, K, V, O, LSE, p, c, OWS, LWS, id);
+      fwd_bf16_item<D, CAUSAL, NW, EMU>(Q, K, V, O, LSE, p, c, OWS, LWS, id);
     }
   }
 }
@@ -662,11 +666,12 @@ void fa_fwd_bf16_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__
                                                      float* __restrict__, fa_plan_t, float);
 #define FA_F32_VARIANTS(X) X(64, false) X(64, true) X(128, false) X(128, true) X(256, false) X(256, true)
 FA_F32_VARIANTS(FA_INST_F32)
-#define FA_INST_BF16(DD, CC, NN)                                                                          \
-  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN>(const __bf16* __restrict__, const __bf16* __restrict__, \
-                                                          const __bf16* __restrict__, __bf16* __restrict__,     \
-                                                          float* __restrict__, fa_plan_t, float, float* __restrict__, \
-                                                          float* __restrict__);
+#define FA_INST_BF16_E(DD, CC, NN, EE)                                                                    \
+  template __global__ void fa_fwd_bf16_kernel<DD, CC, NN, EE>(const __bf16* __restrict__, const __bf16* __restrict__, \
+                                                              const __bf16* __restrict__, __bf16* __restrict__,     \
+                                                              float* __restrict__, fa_plan_t, float,                \
+                                                              float* __restrict__, float* __restrict__);
+#define FA_INST_BF16(DD, CC, NN) FA_INST_BF16_E(DD, CC, NN, 0)
 // (head dim, causal, waves per workgroup)
 #define FA_BF16_VARIANTS(X)                                                                                \
   X(64, false, 1) X(64, false, 2) X(64, false, 4) X(64, true, 1) X(64, true, 2) X(64, true, 4)              \
@@ -674,6 +679,14 @@ FA_F32_VARIANTS(FA_INST_F32)
   X(128, true, 1) X(128, true, 2) X(128, true, 4) X(128, true, 8)                                           \
   X(256, false, 1) X(256, false, 2) X(256, false, 4) X(256, true, 1) X(256, true, 2) X(256, true, 4)
 FA_BF16_VARIANTS(FA_INST_BF16)
+// the same at d = 64 and 128 with a quarter (EMU 1) or half (EMU 2) of the
+// exponentials on the FMA pipe (fa_fwd_exp2_emulated)
+#define FA_BF16_EMU_VARIANTS(X, EE)                                                                        \
+  X(64, false, 1, EE) X(64, false, 2, EE) X(64, false, 4, EE) X(64, true, 1, EE) X(64, true, 2, EE)        \
+  X(64, true, 4, EE) X(128, false, 1, EE) X(128, false, 2, EE) X(128, false, 4, EE) X(128, false, 8, EE)   \
+  X(128, true, 1, EE) X(128, true, 2, EE) X(128, true, 4, EE) X(128, true, 8, EE)
+FA_BF16_EMU_VARIANTS(FA_INST_BF16_E, 1)
+FA_BF16_EMU_VARIANTS(FA_INST_BF16_E, 2)
 
 // ---------------------------------------------------------------- merge of key ranges
 // One wave per output row (b, h, i): with L = ln sum_s exp(lse_s),
@@ -756,24 +769,28 @@ static unsigned fwd_grid(const fa_plan_t& p, int d) {
 }
 
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
-                      float c, int f32, float* ows, float* lws, hipStream_t stream) {
+                      float c, int f32, float* ows, float* lws, hipStream_t stream, int emu) {
 #define FA_CASE_F32(DD, CC)                                                                               \
   if (f32 && d == DD && (p.causal != 0) == CC) {                                                        \
     hipLaunchKernelGGL((fa_fwd_f32_kernel<DD, CC>), dim3((unsigned)p.nwg), dim3(256), 0, stream, (const float*)q, \
                        (const float*)k, (const float*)v, (float*)o, lse, p, c);                        \
     return hipGetLastError();                                                                           \
   }
-#define FA_CASE_BF16(DD, CC, NN)                                                                       \
-  if (!f32 && d == DD && (p.causal != 0) == CC && p.nw == NN) {                                         \
-    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN>), dim3(fwd_grid(p, d)), dim3(64 * NN), 0, stream,      \
+#define FA_CASE_BF16_E(DD, CC, NN, EE)                                                                 \
+  if (!f32 && emu == EE && d == DD && (p.causal != 0) == CC && p.nw == NN) {                            \
+    hipLaunchKernelGGL((fa_fwd_bf16_kernel<DD, CC, NN, EE>), dim3(fwd_grid(p, d)), dim3(64 * NN), 0, stream,  \
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, p, c, ows, lws); \
     return hipGetLastError();                                                                           \
   }
+#define FA_CASE_BF16(DD, CC, NN) FA_CASE_BF16_E(DD, CC, NN, 0)
   if (f32 && p.nsplit > 1) return hipErrorInvalidValue;  // the fp32 kernel has no key split
   FA_F32_VARIANTS(FA_CASE_F32)
   FA_BF16_VARIANTS(FA_CASE_BF16)
+  FA_BF16_EMU_VARIANTS(FA_CASE_BF16_E, 1)
+  FA_BF16_EMU_VARIANTS(FA_CASE_BF16_E, 2)
 #undef FA_CASE_F32
 #undef FA_CASE_BF16
+#undef FA_CASE_BF16_E
   return hipErrorInvalidValue;
 }
 

@@ -42,8 +42,10 @@ hipError_t launch_mfma_ceiling(float* out, int fp8, int iters, int random, hipSt
 // operands (split into bf16 hi/lo parts inside the kernel).  With a key
 // split (p.nsplit > 1, bf16 only) the kernel writes the partial results of
 // every range to ows ([nsplit][B][Hq][Nq][d] fp32) and lws ([nsplit][B][Hq][Nq]).
+// emu (bf16, d = 64 and 128 only): 1 or 2 of every four exponentials on the
+// FMA pipe (exp2_poly) instead of the exponential unit.
 hipError_t launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const fa_plan_t& p, int d,
-                      float c, int f32, float* ows, float* lws, hipStream_t stream);
+                      float c, int f32, float* ows, float* lws, hipStream_t stream, int emu = 0);
 
 // Enqueue the merge of nsplit partial results of rows = B*Hq*Nq rows into o
 // (bf16) and lse (fp32, may be NULL).

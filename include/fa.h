@@ -84,6 +84,27 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  float scale, int causal, void* stream);
 
 /*
+ * fa_fwd with part of the exponentials computed on the FMA pipe instead of
+ * the hardware exponential unit ("FlashAttention-4震撼发布：性能再攀新高",
+ * second algorithmic improvement: a polynomial emulation of the exponential
+ * for some of the scores, where the exponential unit is the bottleneck).
+ * For `quarters` (1 or 2) of every four scores of a row, 2^x is formed as
+ * p(f) * 2^n with x = n + f, n = floor(x), and p the cubic of largest
+ * relative error 7.5e-5 on [0, 1) (csrc/fa_exp2_coef.h, fitted by
+ * exact_attention_07_amd/exp2_fit.py); the others take v_exp_f32.  Masked
+ * keys still weigh exactly 0.  The result equals fa_fwd's up to that error
+ * in the probabilities.  On gfx950 the exponential unit does not limit the
+ * kernel, so this variant is slower than fa_fwd (it exists to measure that
+ * trade); fa_fwd remains the path to use.
+ *   quarters  1 or 2, else FA_ERR_FLAG
+ *   d         64 or 128 (FA_ERR_HEAD_DIM for 256)
+ * Everything else as for fa_fwd (no key split).
+ */
+fa_status fa_fwd_exp2_emulated(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                               float scale, int causal, int quarters, void* stream);
+
+/*
  * float32 forward pass: q, k, v, o hold float32 values.  The operation is
  * fa_fwd's, the definition on "FlashAttention (SV)", section "Problematik
  * med standard-attention", computed by the same tiled, fused, online-softmax

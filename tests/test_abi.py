@@ -71,6 +71,19 @@ def test_invalid_arguments_are_rejected_on_the_host(lib, fn, kw, status):
     assert call(lib, fn, **kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(B=0), 2), (dict(d=96), 3), (dict(d=256), 3), (dict(Hq=6, Hkv=4), 4),
+    (dict(o=P + 4), 5), (dict(scale=float("nan")), 6), (dict(causal=2), 8),
+    (dict(quarters=0), 8), (dict(quarters=3), 8), (dict(quarters=-1), 8),
+])
+def test_exp2_emulated_rejects_invalid_arguments(lib, kw, status):
+    a = dict(GOOD, quarters=1)
+    a.update(kw)
+    assert lib.fa_fwd_exp2_emulated(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                                    a["Nk"], a["d"], ctypes.c_float(a["scale"]), a["causal"], a["quarters"],
+                                    None) == status
+
+
 FP8_GOOD = dict(q=P, k=P, v=P, q8=P, k8=P, v8t=P, descale=P, amax=P, signs=P, scale=0.1, B=1, Hq=4, Hkv=2, Nq=10,
                 Nk=10, d=128)
 
