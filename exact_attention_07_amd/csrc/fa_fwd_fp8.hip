@@ -105,10 +105,10 @@ struct TileCopy {
 // refills the slots of K_j and V_{j-2} with K_{j+2} and V_j; each copy has
 // one iteration to land before the barrier that publishes it.
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
-void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
-                       const uint8_t* __restrict__ V8T, const float* __restrict__ descale,
-                       __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p) {
+__device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
+                                             const uint8_t* __restrict__ V8T, const float* __restrict__ descale,
+                                             __bf16* __restrict__ O, float* __restrict__ LSE, const fa_plan_t& p,
+                                             unsigned item) {
   constexpr int KB = BC / 32;      // 32-key blocks per tile
   constexpr int KS = D / 64;       // k-steps of S^T
   constexpr int DB = D / 32;       // 32-row blocks of O^T
@@ -140,7 +140,7 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
   auto vslot = [&](auto par) { return (LDS_AS char*)(decltype(par)::value == 0 ? lv0_ : lv1_); };
   LDS_AS char* const spare = (LDS_AS char*)lsp_;
 
-  const fa_work_t w = fa_decode(p, blockIdx.x);
+  const fa_work_t w = fa_decode(p, item);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hq = w.hq0 + wave % p.hw;
   const int q0w = w.qpos0 + (wave / p.hw) * 32;
@@ -389,6 +389,34 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
     LSE[(size_t)(w.b * p.Hq + hq) * Nq + query] = lt > 0.f ? (m_ref + log2f(lt)) * LN2 : NEG_INF;
 }
 
+// The causal 4-wave kernels (two workgroups per CU at d <= 128, one at
+// d = 256) and the non-causal 4-wave d = 256 kernel, which holds a CU alone,
+// run as persistent grids (fa_persistent_item): each workgroup takes work
+// items in rounds, in the snake order that evens out causal work, so a CU's
+// next item starts without a new workgroup's dispatch.  The other forms run
+// one item per workgroup.
+template <int D, bool CAUSAL, int NW>
+constexpr bool fp8_persistent() {
+  return NW == 4 && (CAUSAL || D == 256);
+}
+
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1)))
+void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict__ K8,
+                       const uint8_t* __restrict__ V8T, const float* __restrict__ descale,
+                       __bf16* __restrict__ O, float* __restrict__ LSE, fa_plan_t p) {
+  if constexpr (!fp8_persistent<D, CAUSAL, NW>()) {
+    fwd_fp8_item<D, CAUSAL, NW>(Q8, K8, V8T, descale, O, LSE, p, blockIdx.x);
+  } else {
+    for (unsigned r = 0;; ++r) {
+      const unsigned id = fa_persistent_item(gridDim.x, p.nwg, blockIdx.x, r);
+      if (id == ~0u) break;
+      if (r > 0) __syncthreads();  // every wave is done with the last item's LDS
+      fwd_fp8_item<D, CAUSAL, NW>(Q8, K8, V8T, descale, O, LSE, p, id);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launcher
 #define FA_INST_FP8(DD, CC, NN)                                                                              \
   template __global__ void fa_fwd_fp8_kernel<DD, CC, NN>(const uint8_t* __restrict__, const uint8_t* __restrict__, \
@@ -400,11 +428,17 @@ void fa_fwd_fp8_kernel(const uint8_t* __restrict__ Q8, const uint8_t* __restrict
   X(256, false, 1) X(256, false, 2) X(256, false, 4) X(256, true, 1) X(256, true, 2) X(256, true, 4)
 FA_FP8_VARIANTS(FA_INST_FP8)
 
+// workgroups of a launch: the persistent forms above get one or two per CU
+static unsigned fp8_grid(const fa_plan_t& p, int d) {
+  if (p.nw == 4 && (p.causal || d == 256)) return persistent_grid(p.nwg, d == 256 ? 1 : 2);
+  return (unsigned)p.nwg;
+}
+
 hipError_t launch_fwd_fp8(const void* q8, const void* k8, const void* v8t, const float* descale, void* o, float* lse,
                           const fa_plan_t& p, int d, hipStream_t stream) {
 #define FA_CASE_FP8(DD, CC, NN)                                                                           \
   if (d == DD && (p.causal != 0) == CC && p.nw == NN) {                                                 \
-    hipLaunchKernelGGL((fa_fwd_fp8_kernel<DD, CC, NN>), dim3((unsigned)p.nwg), dim3(64 * NN), 0, stream,     \
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<DD, CC, NN>), dim3(fp8_grid(p, d)), dim3(64 * NN), 0, stream,      \
                        (const uint8_t*)q8, (const uint8_t*)k8, (const uint8_t*)v8t, descale, (__bf16*)o, lse, p); \
     return hipGetLastError();                                                                           \
   }

@@ -18,6 +18,8 @@ int queries_per_wave(int d, int f32);
 // their workgroups per CU:
 //   forward: 8 waves at d = 128 and 4 at d = 256 (one); causal 4 waves at
 //     d = 64 and 128 (two);
+//   fp8 forward: 4 waves at d = 256 (one); causal 4 waves at d = 64 and
+//     128 (two);
 //   dQ: 8 waves at d = 128, 4 at d = 256 up to Nq = 4096 (one); causal
 //     4 waves at d = 128 up to Nq = 4096 (two);
 //   dK/dV, up to Nq = 4096 with two items per workgroup: 8 waves at

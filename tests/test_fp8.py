@@ -351,6 +351,48 @@ def test_random_inputs_against_the_oracle(api, shape, d, causal):
     assert cq >= 0.999, f"cosine against the dequantised oracle {cq:.6f}"
 
 
+FP8_PERSISTENT = [
+    # B, Hq, Hkv, N, d, causal: more work items than the persistent grid holds
+    (4, 16, 16, 2050, 128, True),    # two workgroups per CU, items not a multiple of the grid
+    (3, 12, 4, 4000, 64, True),
+    (2, 16, 8, 2000, 256, True),     # one workgroup per CU
+    (2, 16, 16, 2000, 256, False),
+]
+
+
+@pytest.mark.parametrize("case", FP8_PERSISTENT, ids=lambda c: "x".join(map(str, c)))
+def test_persistent_grid_covers_every_row(api, case):
+    """The causal 4-wave fp8 kernels and the non-causal d = 256 one run grids
+    with more work items than fit the GPU at once as persistent workgroups
+    taking items in rounds.  O and LSE start as NaN and must be written
+    everywhere; sampled rows (block ends, the tail, random) match the oracle
+    on the dequantised codes (cosine, and the LSE within the per-row bound)."""
+    B, Hq, Hkv, n, d, causal = case
+    w = gen.workload(B, Hq, Hkv, n, n, d, dtype="fp8", causal=causal)
+    x = gen.make_inputs(w, (n, d, int(causal), 78))
+    print(f"case: fp8 persistent grid {w.name}", flush=True)
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    o, lse, prep = api.attention_fp8(q, k, v, causal=causal, scale=w.softmax_scale)
+    o.fill_(float("nan"))
+    lse.fill_(float("nan"))
+    api.fa_fwd_fp8(prep["q8"], prep["k8"], prep["v8t"], prep["descale"], o, lse, causal)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item(), "rows left unwritten"
+    of, lf = out_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    qq, kq, vq = dequantise_gpu(prep["q8"].cpu().numpy(), prep["k8"].cpu().numpy(), prep["v8t"].cpu().numpy(),
+                                prep["descale"].cpu().numpy().astype(np.float64), n, w.softmax_scale)
+    rng = np.random.default_rng(n)
+    rows = [(0, 0, 0), (B - 1, Hq - 1, n - 1), (0, Hq - 1, 127), (B - 1, 0, 128), (0, 1, n - 2)]
+    rows += [(int(rng.integers(B)), int(rng.integers(Hq)), int(rng.integers(n))) for _ in range(35)]
+    o_q, lse_q = attention_rows_fp64(qq, kq, vq, w.softmax_scale, causal, rows)
+    got = np.stack([of[b, h, i] for b, h, i in rows])
+    assert cosine(got, o_q) >= 0.999, cosine(got, o_q)
+    g = Hq // Hkv
+    bound = np.array([score_error_bound(qq[b:b + 1, h:h + 1, i:i + 1], kq[b:b + 1, h // g:h // g + 1],
+                                        w.softmax_scale)[0, 0, 0] for b, h, i in rows])
+    check_lse_against_dequantised(np.array([lf[b, h, i] for b, h, i in rows]), lse_q, bound, w.name)
+
+
 def fp8_errors(o, o_true):
     err = o - o_true
     return dict(cos=cosine(o, o_true), rmse=float(np.sqrt((err ** 2).mean())), maxabs=float(np.abs(err).max()))
