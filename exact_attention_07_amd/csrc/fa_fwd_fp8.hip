@@ -7,7 +7,8 @@
 // bf16, with fp32 accumulation.  The operands come from fa_fp8_prepare (Q
 // and K rotated by a signed Hadamard matrix and quantised with one scale per
 // tensor, V quantised and stored transposed).  The structure is that of the
-// bf16 kernel: 32 query rows per wave with their Q codes resident in VGPRs,
+// bf16 kernel (the Q codes carry the softmax scale in log2 units, so the
+// scores need no multiply): 32 query rows per wave with their Q codes resident in VGPRs,
 // K and V^T tiles of 64 keys copied HBM -> LDS with bounds-checked buffer
 // loads, double buffered; scores transposed (S^T = K Q^T) so that a lane
 // holds the scores of one query; the online softmax with the output
