@@ -148,11 +148,12 @@ def _oracle_head(args):
     return _t.perf_counter() - t0
 
 
-def cpu_baseline_pool(w, x, budget_s: float, dout=None):
+def cpu_baseline_pool(w, x, budget_s: float, dout=None, bytes_total=None):
     """The fp64 oracle timed on this host: whole (b, h) heads of the workload,
     one per task over a pool of host processes (one BLAS thread each), until
     budget_s of wall time has passed; value = oracle flops of the finished
-    heads / wall time."""
+    heads / wall time, or, given the workload's algorithmic bytes
+    (bytes_total), that share of them per second in GB/s."""
     import multiprocessing as mp
     cores = host_cores()
     g = w.Hq // w.Hkv
@@ -176,7 +177,10 @@ def cpu_baseline_pool(w, x, budget_s: float, dout=None):
     wall = t_last - t0
     what = "fp64 gradient oracle (P, dP, dS materialised)" if dout is not None else \
         "fp64 two-pass oracle (S and P materialised)"
-    return {"value": done * per_head / wall / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    value, unit = done * per_head / wall / 1e12, "TFLOP/s"
+    if bytes_total is not None:
+        value, unit = bytes_total * done / len(heads) / wall / 1e9, "GB/s"
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle",
             "cpu_model": cpu_model(),
             "sample": f"{done} of {len(heads)} (b,h) heads of the same workload, {what}, one head per task on "
                       f"{cores} processes with one BLAS thread each, {wall:.1f} s wall"}
@@ -522,6 +526,8 @@ def main():
                          "frac": round(gbs / 8000.0, 4), "traffic": load_traffic("decode", "bf16", load_counters("decode")),
                          "step_ms": round(ms, 5), "call_ms": round(kernel_ms, 5), "tflops": round(tflops, 2)},
         }
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline_pool(w, x, args.cpu_budget, bytes_total=nbytes)
         print(json.dumps(line), flush=True)
         return
 
