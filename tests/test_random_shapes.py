@@ -83,3 +83,30 @@ def test_random_shape_backward(api, case):
         compare_grad(dq, rq, f"{w.name} dQ")
         compare_grad(dk, rk, f"{w.name} dK")
     compare_grad(dv, rv, f"{w.name} dV")
+
+
+@pytest.mark.parametrize("case", CASES[:16], ids=lambda c: "x".join(map(str, c)))
+def test_random_shape_fp8(api, case):
+    """The same drawn shapes through fa_fp8_prepare (with the rotation) and
+    fa_fwd_fp8, against the fp64 oracle on exactly the e4m3 values the GPU
+    consumed: cosine >= 0.999, rows with no key O = 0 and LSE = -inf, the LSE
+    within the per-row bound of the fp8 MFMA's grouped sums."""
+    from tests.test_fp8 import check_lse_against_dequantised, cosine, dequantise_gpu, score_error_bound
+    B, Hq, Hkv, Nq, Nk, d, causal, _ = case
+    w = gen.workload(B, Hq, Hkv, Nq, Nk, d, dtype="fp8", causal=causal)
+    x = gen.make_inputs(w, (53, sum(case)))
+    print(f"case: random fp8 {w.name}", flush=True)
+    q, k, v = (to_device(x[t], "bf16") for t in "qkv")
+    signs = torch.from_numpy(x["signs"]).cuda()
+    o, lse, prep = api.attention_fp8(q, k, v, causal=causal, scale=w.softmax_scale, signs=signs)
+    torch.cuda.synchronize()
+    o, lse = out_to_f64(o), lse.cpu().numpy().astype(np.float64)
+    qq, kq, vq = dequantise_gpu(prep["q8"].cpu().numpy(), prep["k8"].cpu().numpy(), prep["v8t"].cpu().numpy(),
+                                prep["descale"].cpu().numpy().astype(np.float64), Nk, w.softmax_scale)
+    o_q, lse_q = attention_fp64(qq, kq, vq, w.softmax_scale, causal)
+    assert np.isfinite(o).all()
+    none = np.isneginf(lse_q)
+    assert (o[none] == 0).all()
+    if (~none).any():
+        assert cosine(o[~none], o_q[~none]) >= 0.999, cosine(o[~none], o_q[~none])
+    check_lse_against_dequantised(lse, lse_q, score_error_bound(qq, kq, w.softmax_scale), w.name)
