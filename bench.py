@@ -566,11 +566,14 @@ def main():
         # the same kernel under rocprofv3 counters: the clock it sustains and
         # the share of SIMD cycles its matrix pipe was busy
         clk = float(counters.get("sustained_clock_ghz", "nan"))
+        if not clk <= NOMINAL_CLOCK_GHZ:
+            clk = float("nan")  # the counter spanned more than the kernel: no clock (see the summary)
         peak_clk = peak * clk / NOMINAL_CLOCK_GHZ
         line["roofline"].update({
-            "sustained_clock_ghz": round(clk, 4), "mfma_busy": float(counters.get("mfma_busy", "nan")),
-            "peak_at_sustained_clock": round(peak_clk, 1),
-            "frac_at_sustained_clock": round(kernel_tflops / peak_clk, 4),
+            "sustained_clock_ghz": None if clk != clk else round(clk, 4),
+            "mfma_busy": float(counters.get("mfma_busy", "nan")),
+            "peak_at_sustained_clock": None if clk != clk else round(peak_clk, 1),
+            "frac_at_sustained_clock": None if clk != clk else round(kernel_tflops / peak_clk, 4),
             "lds_bank_conflict_rate": float(counters.get("lds_bank_conflict_rate", "nan")),
             "valu_insts_per_mfma": float(counters.get("valu_insts_per_mfma", "nan")),
             "trans_share_of_valu": float(counters.get("trans_share", "nan")),

@@ -119,6 +119,12 @@ def summarize(config, dirs, commands, out_path):
     if clocks:
         clk = sum(clocks) / len(clocks)  # GHz
         lines.append(f"sustained_clock_ghz: {clk:.4f}")
+        if clk > 2.4:
+            # above the chip's maximum: the counter spans more than the
+            # kernel's own duration (short or memory-bound launches), so this
+            # is no clock
+            lines.append("sustained_clock_note: above the 2.4 GHz maximum, not a clock (GRBM_GUI_ACTIVE spans "
+                         "more than this kernel's duration)")
         per_simd = 1024.0 * (2 if dtype == "fp8" else 1)
         lines.append(f"mfma_peak_at_clock_tflops: {N_CU * 4 * per_simd * clk * 1e9 / 1e12:.1f}")
     if busy is not None:
