@@ -5,7 +5,7 @@
 A step is one pass of the attention over one batch of synthetic input of the
 chosen standing workload (default: the causal GQA long-context workload B=2,
 Hq=32, Hkv=8, N=8192, d=128, bf16): one fa_fwd (or fa_fwd_f32) call, or for
-the fp8 workload (config 5) fa_fp8_prepare (Hadamard rotation of Q and K,
+the fp8 workload (--config 5: B=4, H=16, N=8192, d=128, e4m3) fa_fp8_prepare (Hadamard rotation of Q and K,
 per-tensor scales, e4m3 codes) followed by fa_fwd_fp8.  Inputs are resident
 in HBM before timing starts; K steps are timed back to back with HIP events
 on the stream the kernels run on.  Prints one JSON line on stdout
