@@ -531,11 +531,12 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
     float part = part0 + part1;
 
     // slow path: if some probability may exceed 2^TAU (a lane's partial row
-    // sum does), or a row has no reference yet, form the row maximum, rescale
-    // O (which already holds P_{j-1} V_{j-1}) and l when it grew by more than
-    // TAU, and redo the exponentials.  Otherwise every probability is at most
-    // 2^TAU and the reference maximum stands, exactly as the max-first rule
-    // would decide.
+    // sum does), or a row has no reference yet, form the row maximum; when
+    // it grew by more than TAU, rescale O (which already holds
+    // P_{j-1} V_{j-1}) and l and redo the exponentials.  Otherwise every
+    // probability is at most 2^TAU and the reference maximum stands, exactly
+    // as the max-first rule would decide, and the exponentials already taken
+    // are the ones it gives.
     if (__ballot(!(part <= TAU_EXP2) || m_ref == NEG_INF)) {
       float mx = NEG_INF;
 #pragma unroll
@@ -550,12 +551,12 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         m_ref = m_run;
-      }
-      mu = (m_ref == NEG_INF) ? 0.f : m_ref;
-      part0 = part1 = partq = 0.f;
+        mu = (m_ref == NEG_INF) ? 0.f : m_ref;
+        part0 = part1 = partq = 0.f;
 #pragma unroll
-      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even, partq);
-      part = part0 + part1;
+        for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even, partq);
+        part = part0 + part1;
+      }
     }
     lsum += part;
     lsumq += partq;

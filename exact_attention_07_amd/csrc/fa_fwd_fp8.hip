@@ -231,33 +231,49 @@ __device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, con
 #pragma unroll
   for (int i = 0; i < 8; ++i) pb[i] = 0;
 
-  // score sc of s (already x - mu): exponential, row-sum part; byte sc of the
-  // P fragment (the odd member of a pair packs the pair into its half-dword).
-  // With `pin`, the low half is written over the dword's stale contents
-  // (which the high half then replaces) instead of over a zero, and an empty
-  // asm takes each finished dword as an input where it is formed: the
-  // compiler otherwise moves the packing of the common path below the
-  // slow-path branch (where the slow path repacks), into one burst after the
-  // last MFMA of the iteration.  Pinned, it stays beside the MFMAs: measured
-  // +2-3.5 % on causal shapes and at d = 256, -1 % on the non-causal d = 128
-  // workload, hence PIN below.
-  auto score = [&](const f32x16 (&s)[KB], i32x8& pf, int sc, float& part0, float& part1, float& even, bool pin) {
+  // score sc of s (already x - mu): exponential and row-sum part.  Packing
+  // into byte sc of the P fragment (the odd member of a pair packs the pair
+  // into its half-dword) takes one of three forms:
+  //   HOLD: the probability is kept in pvs and the whole tile is packed
+  //     after the slow-path check (pack_held);
+  //   PACK: packed where it is formed;
+  //   PIN:  as PACK, with the low half written over the dword's stale
+  //     contents (which the high half then replaces) instead of over a zero,
+  //     and an empty asm taking each finished dword as an input where it is
+  //     formed, so that the compiler keeps the packing beside the MFMAs.
+  // Measured: packing beside the MFMAs is 2-3.5 % faster on causal shapes
+  // and at d = 256, holding 1-1.5 % faster on the non-causal d = 128
+  // workload, hence the choice below.
+  enum { HOLD, PACK, PIN };
+  float pvs[NSC];
+  auto score = [&](const f32x16 (&s)[KB], i32x8& pf, int sc, float& part0, float& part1, float& even, int mode) {
     const float pv = __builtin_amdgcn_exp2f(s[sc / 16][sc % 16]);
     if (sc & 1) {
       part1 = sc == 1 ? pv : part1 + pv;
       const int pp = sc / 2;
-      if (pp & 1) {
+      if (mode == HOLD) {
+        pvs[sc] = pv;
+      } else if (pp & 1) {
         pf[pp / 2] = __builtin_amdgcn_cvt_pk_fp8_f32(even, pv, pf[pp / 2], true);
-        if (pin) asm volatile("" ::"v"(pf[pp / 2]));
+        if (mode == PIN) asm volatile("" ::"v"(pf[pp / 2]));
       } else {
-        pf[pp / 2] = __builtin_amdgcn_cvt_pk_fp8_f32(even, pv, pin ? pf[pp / 2] : 0, false);
+        pf[pp / 2] = __builtin_amdgcn_cvt_pk_fp8_f32(even, pv, mode == PIN ? pf[pp / 2] : 0, false);
       }
     } else {
       part0 = sc == 0 ? pv : part0 + pv;
       even = pv;
+      if (mode == HOLD) pvs[sc] = pv;
     }
   };
-  constexpr bool PIN = CAUSAL || D != 128;
+  // (each dword's two halves are both written, so its old contents do not matter)
+  auto pack_held = [&](i32x8& pf) {
+#pragma unroll
+    for (int pp = 0; pp < NSC / 2; ++pp)
+      pf[pp / 2] = (pp & 1) ? __builtin_amdgcn_cvt_pk_fp8_f32(pvs[2 * pp], pvs[2 * pp + 1], pf[pp / 2], true)
+                            : __builtin_amdgcn_cvt_pk_fp8_f32(pvs[2 * pp], pvs[2 * pp + 1], pf[pp / 2], false);
+  };
+  constexpr bool HELD = !CAUSAL && D == 128;
+  constexpr int FIRST = HELD ? HOLD : PIN, AGAIN = HELD ? HOLD : PACK;
 
   // the exponentials of tile j (scores in s, probabilities into pf), the
   // MFMAs of S_{j+1} (into sn) and of O += V_{j-1} P_{j-1} (pprev).  At the
@@ -300,7 +316,7 @@ __device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, con
         if (m + VPF < NPV) vbuf[m % VPF] = lds_b256(vprev + (m + VPF) * 32 * RSV);
       }
 #pragma unroll
-      for (int sc = ch * SPC; sc < (ch + 1) * SPC; ++sc) score(s, pf, sc, part0, part1, even, PIN);
+      for (int sc = ch * SPC; sc < (ch + 1) * SPC; ++sc) score(s, pf, sc, part0, part1, even, FIRST);
       // the copy instructions over the first half of the chunks: each then
       // has more than half an iteration to land (measured 1-2 % faster than
       // spreading them over all chunks)
@@ -312,8 +328,11 @@ __device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, con
     float part = part0 + part1;
     // slow path, as in the bf16 kernel: if some probability may exceed
     // 2^TAU (a lane's partial row sum does) or a row has no reference yet,
-    // form the row maximum, rescale O (which already holds P_{j-1} V_{j-1})
-    // and l when it grew by more than TAU, and redo the exponentials
+    // form the row maximum; when it grew by more than TAU, rescale O (which
+    // already holds P_{j-1} V_{j-1}) and l, shift both score buffers (this
+    // tile's and S_{j+1}, complete by now) to the new reference, start later
+    // blocks at it and redo the exponentials.  When the reference stands the
+    // exponentials already taken are the ones it gives.
     if (__ballot(!(part <= TAU_EXP2) || m_ref == NEG_INF)) {
       float mx = NEG_INF;
 #pragma unroll
@@ -327,22 +346,21 @@ __device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, con
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[db] *= alpha;
         m_ref = m_run;
+        const float mu2 = (m_ref == NEG_INF) ? 0.f : m_ref;
+        const float dm = mu - mu2;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] += dm;
+          sn[kb] += dm;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) negmu[i] = -mu2;
+#pragma unroll
+        for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, part0, part1, even, AGAIN);
+        part = part0 + part1;
       }
-      // shift both score buffers (this tile's and S_{j+1}, complete by
-      // now) to the new reference, and start later blocks at it
-      const float mu2 = (m_ref == NEG_INF) ? 0.f : m_ref;
-      const float dm = mu - mu2;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] += dm;
-        sn[kb] += dm;
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) negmu[i] = -mu2;
-#pragma unroll
-      for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, part0, part1, even, false);
-      part = part0 + part1;
     }
+    if constexpr (HELD) pack_held(pf);
     lsum += part;
   };
 
