@@ -43,6 +43,12 @@ Under rocprofv3 counters (GRBM_GUI_ACTIVE) the same run shows the clock
 directly: the evidence that on this chip the clock under dense matrix work,
 and hence the reachable matrix rate, depends on the data the MFMAs toggle.
 
+--issue-sweep measures only fa_issue_cost: rounds of bf16 MFMAs with
+exponentials, e4m3 packings and FMAs beside them (the bf16 and fp8 kernels'
+mixes per four MFMAs, and the same with part of the exponentials replaced
+by seven FMA-pipe instructions each), each case's median launch time against
+the MFMA-only case; --issue-summary PATH writes the table to PATH.
+
 --exp2-emulated Q times fa_fwd_exp2_emulated (Q of every four exponentials
 computed by a polynomial on the FMA pipe) in place of fa_fwd on a bf16
 workload; the line's config then names it.
@@ -353,6 +359,46 @@ def ceiling_sweep(torch, api, launches: int, warm: int):
                       "warm_launches": warm, "rows": rows}), flush=True)
 
 
+def issue_sweep(torch, api, launches: int, warm: int, iters: int, summary: str | None, command: str):
+    """fa_issue_cost: every case (rounds of bf16 MFMAs with exponentials, e4m3
+    packings and FMAs beside them, two waves per SIMD), median launch time
+    over `launches` launches after `warm` untimed ones, against the
+    MFMA-only case.  With `summary`, also writes the table there."""
+    stream = torch.cuda.current_stream()
+    out = torch.empty(api.mfma_ceiling_out_bytes() // 4, dtype=torch.float32, device="cuda")
+    cases = api.issue_cost_cases()
+    rows = []
+    for i, c in enumerate(cases):
+        for _ in range(warm):
+            api.issue_cost(out, i, iters, stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(launches)]
+        for a, b in ev:
+            a.record(stream)
+            api.issue_cost(out, i, iters, stream)
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+        rows.append(dict(c, case=i, launch_ms=round(ms, 4)))
+    base = rows[0]["launch_ms"]
+    for r in rows:
+        r["vs_mfma_only"] = round(r["launch_ms"] / base, 3)
+        log(f"issue cost case {r['case']}: {r['mfmas']} MFMA, {r['exps']} exp, {r['cvts']} e4m3 packings, "
+            f"{r['fmas']} FMA per round: {r['launch_ms']:.4f} ms ({r['vs_mfma_only']:.3f} x MFMA only)")
+    line = {"metric": "issue cost of vector work beside MFMA", "unit": "ms per launch", "iters": iters,
+            "launches": launches, "warm_launches": warm, "rows": rows}
+    print(json.dumps(line), flush=True)
+    if summary:
+        with open(summary, "w") as f:
+            f.write("# fa_issue_cost: rounds of v_mfma_f32_32x32x16_bf16 (random operands) with v_exp_f32,\n"
+                    "# v_cvt_pk_fp8_f32 and v_fma_f32 beside them, per wave, two waves per SIMD on every CU;\n"
+                    f"# median launch time of {launches} launches after {warm} untimed ones, {iters} rounds per wave\n"
+                    f"# command (from the repository root on the MI355X box):\n#   {command}\n")
+            f.write("case  mfmas  exps  cvts  fmas  launch_ms  vs_mfma_only\n")
+            for r in rows:
+                f.write(f"{r['case']:4d}  {r['mfmas']:5d}  {r['exps']:4d}  {r['cvts']:4d}  {r['fmas']:4d}  "
+                        f"{r['launch_ms']:9.4f}  {r['vs_mfma_only']:12.3f}\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +416,9 @@ def main():
                          "(bf16, d = 64 or 128) instead of fa_fwd")
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="measure only the MFMA-only loop, random against constant operands (see above)")
+    ap.add_argument("--issue-sweep", action="store_true",
+                    help="measure only fa_issue_cost (vector work beside MFMA) and exit")
+    ap.add_argument("--issue-summary", default=None, help="with --issue-sweep: write the table to this file")
     ap.add_argument("--sweep-launches", type=int, default=60)
     ap.add_argument("--sweep-warm", type=int, default=600, help="untimed launches before each case")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -386,6 +435,10 @@ def main():
 
     if args.ceiling_sweep:
         ceiling_sweep(torch, api, args.sweep_launches, args.sweep_warm)
+        return
+    if args.issue_sweep:
+        issue_sweep(torch, api, args.sweep_launches, min(args.sweep_warm, 200), 4000, args.issue_summary,
+                    "python3 " + " ".join(sys.argv))
         return
     if args.config == "backward":
         bench_backward(args, torch, api, gen)

@@ -67,6 +67,13 @@ def lib() -> ctypes.CDLL:
     L.fa_mfma_ceiling_flops.restype = ctypes.c_double
     L.fa_mfma_ceiling.argtypes = [vp, ctypes.c_size_t, i, i, i, vp]
     L.fa_mfma_ceiling.restype = ctypes.c_int
+    L.fa_issue_cost_cases.argtypes = []
+    L.fa_issue_cost_cases.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int)
+    L.fa_issue_cost_case.argtypes = [i, ip, ip, ip, ip]
+    L.fa_issue_cost_case.restype = ctypes.c_int
+    L.fa_issue_cost.argtypes = [vp, ctypes.c_size_t, i, i, vp]
+    L.fa_issue_cost.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
     L.fa_status_string.restype = ctypes.c_char_p
     L.fa_abi_version.argtypes = []
@@ -351,6 +358,25 @@ def mfma_ceiling(out, fp8: bool, iters: int, random: bool = True, stream=None) -
         raise ValueError("out must be a contiguous float32 GPU tensor")
     _check(lib().fa_mfma_ceiling(_ptr(out), out.numel() * 4, int(bool(fp8)), int(iters), int(bool(random)),
                                  _stream(stream)), "fa_mfma_ceiling")
+
+
+def issue_cost_cases() -> list:
+    """The issue-cost loop's cases: one dict of per-round counts per case."""
+    L = lib()
+    out = []
+    for i in range(int(L.fa_issue_cost_cases())):
+        c = [ctypes.c_int() for _ in range(4)]
+        _check(L.fa_issue_cost_case(i, *[ctypes.byref(x) for x in c]), "fa_issue_cost_case")
+        out.append(dict(zip(("mfmas", "exps", "cvts", "fmas"), (x.value for x in c))))
+    return out
+
+
+def issue_cost(out, case: int, iters: int, stream=None) -> None:
+    """Enqueue case `case` of the issue-cost loop into `out` (a float32 GPU tensor)."""
+    import torch
+    if out.dtype != torch.float32 or not out.is_cuda or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 GPU tensor")
+    _check(lib().fa_issue_cost(_ptr(out), out.numel() * 4, int(case), int(iters), _stream(stream)), "fa_issue_cost")
 
 
 def fa_fwd_splitkv_noalloc(q, k, v, o, lse, scale: float, causal: bool, nsplit: int = 0, stream=None) -> None:

@@ -391,4 +391,20 @@ fa_status fa_mfma_ceiling(float* out, size_t out_bytes, int fp8, int iters, int 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+int fa_issue_cost_cases(void) { return fa::issue_cost_cases(); }
+
+fa_status fa_issue_cost_case(int i, int* mfmas, int* exps, int* cvts, int* fmas) {
+  if (!mfmas || !exps || !cvts || !fmas) return FA_ERR_NULL;
+  return fa::issue_cost_case(i, mfmas, exps, cvts, fmas) ? FA_OK : FA_ERR_FLAG;
+}
+
+fa_status fa_issue_cost(float* out, size_t out_bytes, int i, int iters, void* stream) {
+  if (!out) return FA_ERR_NULL;
+  if (i < 0 || i >= fa::issue_cost_cases()) return FA_ERR_FLAG;
+  if (iters < 1) return FA_ERR_SHAPE;
+  if (!aligned4(out) || out_bytes < fa_mfma_ceiling_out_bytes()) return FA_ERR_WORKSPACE;
+  const hipError_t e = fa::launch_issue_cost(out, i, iters, (hipStream_t)stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // extern "C"

@@ -39,6 +39,12 @@ int cu_count();
 unsigned mfma_ceiling_workgroups();
 double mfma_ceiling_flops(int fp8, int iters);
 hipError_t launch_mfma_ceiling(float* out, int fp8, int iters, int random, hipStream_t stream);
+// The issue-cost loop (fa_ceiling.hip): case i of issue_cost_cases() rounds
+// of MFMAs with exponentials, e4m3 packings and FMAs beside them; the same
+// grid and output size as the ceiling loop.
+int issue_cost_cases();
+bool issue_cost_case(int i, int* mfmas, int* exps, int* cvts, int* fmas);
+hipError_t launch_issue_cost(float* out, int i, int iters, hipStream_t stream);
 
 // Enqueue the forward kernel.  c = scale * log2(e).  f32 selects fp32
 // operands (split into bf16 hi/lo parts inside the kernel).  With a key

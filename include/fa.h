@@ -318,6 +318,33 @@ size_t fa_mfma_ceiling_out_bytes(void);
 double fa_mfma_ceiling_flops(int fp8, int iters);
 fa_status fa_mfma_ceiling(float* out, size_t out_bytes, int fp8, int iters, int random, void* stream);
 
+/*
+ * Measurement helper, not part of the attention computation: the cost of
+ * vector work beside the matrix core.  "FlashAttention-4震撼发布：性能再攀新高"
+ * (second algorithmic improvement) computes part of the exponentials with a
+ * polynomial on the FMA units because on its GPU the exponential unit is
+ * the narrow one.  Whether that can pay depends on what an exponential
+ * costs against an FMA when both sit beside matrix work.  Case i is a loop
+ * whose rounds hold `mfmas` v_mfma_f32_32x32x16_bf16 (random operands),
+ * `exps` v_exp_f32, `cvts` v_cvt_pk_fp8_f32 and `fmas` v_fma_f32 per wave,
+ * spread evenly, two waves per SIMD on every CU; the caller times launches
+ * of each case against the MFMA-only case 0.  The cases include the bf16
+ * and fp8 kernels' mixes per four MFMAs, each also with a quarter and with
+ * half of its exponentials replaced by seven fast instructions.
+ *
+ *   fa_issue_cost_cases()     number of cases
+ *   fa_issue_cost_case(i, …)  the case's per-round counts (FA_ERR_NULL for a
+ *                             null pointer, FA_ERR_FLAG for i out of range)
+ *   out, out_bytes            as for fa_mfma_ceiling
+ *   iters                     rounds per wave, >= 1
+ * Errors: FA_ERR_NULL (out), FA_ERR_FLAG (i out of range), FA_ERR_SHAPE
+ * (iters < 1), FA_ERR_WORKSPACE (out_bytes too small or out misaligned),
+ * FA_ERR_HIP (launch).
+ */
+int fa_issue_cost_cases(void);
+fa_status fa_issue_cost_case(int i, int* mfmas, int* exps, int* cvts, int* fmas);
+fa_status fa_issue_cost(float* out, size_t out_bytes, int i, int iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

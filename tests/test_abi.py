@@ -241,6 +241,29 @@ def test_mfma_ceiling_rejects_arguments_on_the_host(lib):
     assert f(P, 1 << 20, 0, 0, 1, None) == 2             # FA_ERR_SHAPE (iters)
 
 
+def test_issue_cost_cases_and_rejections_on_the_host(lib):
+    n = lib.fa_issue_cost_cases()
+    assert n >= 4
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.fa_issue_cost_case.argtypes = [ctypes.c_int, ip, ip, ip, ip]
+    c = [ctypes.c_int() for _ in range(4)]
+    refs = [ctypes.byref(x) for x in c]
+    assert lib.fa_issue_cost_case(0, *refs) == 0
+    assert [x.value for x in c] == [4, 0, 0, 0]          # case 0: matrix work alone
+    for i in range(n):
+        assert lib.fa_issue_cost_case(i, *refs) == 0
+        assert all(x.value >= 0 for x in c) and sum(x.value for x in c) > 0
+    assert lib.fa_issue_cost_case(n, *refs) == 8          # FA_ERR_FLAG
+    assert lib.fa_issue_cost_case(-1, *refs) == 8
+    assert lib.fa_issue_cost_case(0, None, *refs[1:]) == 1  # FA_ERR_NULL
+    f = lib.fa_issue_cost
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    assert f(None, 1 << 20, 0, 10, None) == 1             # FA_ERR_NULL
+    assert f(P, 1 << 20, n, 10, None) == 8                # FA_ERR_FLAG (case)
+    assert f(P, 1 << 20, 0, 0, None) == 2                 # FA_ERR_SHAPE (iters)
+    assert f(P, 16, 0, 10, None) == 9                     # FA_ERR_WORKSPACE
+
+
 def test_noalloc_refuses_a_call_beyond_its_scratch_on_the_host(lib):
     """More parts than the fixed scratch holds: FA_ERR_SCRATCH_LIMIT before any
     HIP call (fake, never dereferenced pointers)."""
@@ -255,3 +278,17 @@ def test_noalloc_refuses_a_call_beyond_its_scratch_on_the_host(lib):
     assert f(P, P, P, P, P, 1, 64, 64, 1024, 65536, 256, ctypes.c_float(0.1), 0, -1, None) == 2
     assert f(None, P, P, P, P, 1, 4, 2, 10, 10, 128, ctypes.c_float(0.1), 0, 0, None) == 1
     assert f(P, P, P, P, P, 1, 4, 2, 10, 10, 128, ctypes.c_float(-1.0), 0, 0, None) == 6
+
+
+@pytest.mark.gpu
+def test_measurement_loops_run_on_the_gpu():
+    """The measurement helpers (MFMA ceiling, issue-cost cases) launch and
+    complete on the device; their sums only keep the work alive."""
+    import torch
+    from exact_attention_07_amd import api
+    out = torch.empty(api.mfma_ceiling_out_bytes() // 4, dtype=torch.float32, device="cuda")
+    for fp8 in (False, True):
+        api.mfma_ceiling(out, fp8, 2, True)
+    for i in range(len(api.issue_cost_cases())):
+        api.issue_cost(out, i, 2)
+    torch.cuda.synchronize()
