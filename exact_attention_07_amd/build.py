@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfa.so")
-SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_fp8_prepare.hip", "fa_ceiling.hip", "fa_noalloc.hip", "fa_api.cpp"]
+SOURCES = ["fa_fwd.hip", "fa_bwd.hip", "fa_fwd_fp8.hip", "fa_fp8_prepare.hip", "fa_ceiling.hip", "fa_issue.hip", "fa_noalloc.hip", "fa_api.cpp"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of the device code on purpose.

@@ -75,89 +75,7 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* __restrict__ out,
   out[tid] = s;
 }
 
-// The cost of vector work beside the matrix core.  Each wave runs `iters`
-// rounds; a round is NM bf16 MFMAs (the ceiling loop's instruction, random
-// operands) with NE exponentials (v_exp_f32), NC e4m3 packings
-// (v_cvt_pk_fp8_f32) and NF fused multiply-adds spread evenly over them,
-// each kind on 8 independent chains.  Timed against the MFMA-only round,
-// the rounds show what a mix of vector work costs the matrix pipe, and
-// whether replacing an exponential by a polynomial on the FMA units (one
-// v_exp_f32 by seven fast instructions) can pay.
-template <int NM, int NE, int NC, int NF>
-__global__ __launch_bounds__(256) void issue_loop_kernel(float* __restrict__ out, int iters) {
-  const unsigned tid = blockIdx.x * blockDim.x + threadIdx.x;
-  f32x16c acc[4] = {};
-  bf16x8c a[2], b[2];
-  for (int s = 0; s < 2; ++s)
-    for (int i = 0; i < 8; ++i) {
-      const unsigned h = mix(tid * 131u + s * 17u + i * 7u);
-      a[s][i] = (__bf16)((float)(h & 0xffff) / 16384.0f - 2.0f);
-      b[s][i] = (__bf16)((float)(h >> 16) / 16384.0f - 2.0f);
-    }
-  float e[8], f[8], x[8];
-  int c[8];
-  for (int i = 0; i < 8; ++i) {
-    e[i] = -(float)(tid & 7) - 0.125f * i;
-    f[i] = 0.5f + 0.01f * i;
-    x[i] = (float)(tid & 3) + 0.5f * i;
-    c[i] = (int)tid;
-  }
-  const float g = 0.999f, h = 0.001f;
-  constexpr int SLOTS = NM > 0 ? NM : 1;
-  for (int it = 0; it < iters; ++it) {
-#pragma unroll
-    for (int m = 0; m < SLOTS; ++m) {
-      if constexpr (NM > 0)
-        acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[m & 1], b[(m >> 1) & 1], acc[m & 3], 0, 0, 0);
-#pragma unroll
-      for (int k = m * NE / SLOTS; k < (m + 1) * NE / SLOTS; ++k) e[k % 8] = __builtin_amdgcn_exp2f(e[k % 8]);
-#pragma unroll
-      for (int k = m * NC / SLOTS; k < (m + 1) * NC / SLOTS; ++k)
-        c[k % 8] = __builtin_amdgcn_cvt_pk_fp8_f32(x[k % 8], x[(k + 1) % 8], c[k % 8], false);
-#pragma unroll
-      for (int k = m * NF / SLOTS; k < (m + 1) * NF / SLOTS; ++k) f[k % 8] = __builtin_fmaf(f[k % 8], g, h);
-    }
-  }
-  float s = 0.f;
-  for (int i = 0; i < 8; ++i) s += e[i] + f[i] + (float)c[i];
-  for (int i = 0; i < 4; ++i)
-    for (int j = 0; j < 16; ++j) s += acc[i][j];
-  out[tid] = s;
-}
-
 }  // namespace
-
-// The rounds of the issue-cost loop: {MFMAs, exponentials, e4m3 packings,
-// FMAs}.  Four MFMAs take as long as the bf16 kernel spends on one score
-// per lane for each of 4 MFMAs' worth of keys; per four MFMAs that kernel
-// issues 4 exponentials and ~10 fast instructions (4 FMAs, 4 adds, 2 bf16
-// packings), the fp8 kernel (whose MFMA does twice the work in twice the
-// time) 8 exponentials, 4 e4m3 packings and ~8 adds.
-static const int kIssueCases[][4] = {
-    {4, 0, 0, 0},   // matrix work alone
-    {0, 8, 0, 0},   // exponentials alone
-    {0, 0, 0, 16},  // FMAs alone
-    {0, 8, 0, 16},  // both, no matrix work
-    {4, 8, 0, 0},   {4, 16, 0, 0},  {4, 0, 0, 16}, {4, 0, 0, 32},
-    {4, 4, 0, 10},  // the bf16 kernel's mix
-    {4, 3, 0, 17},  // ... with a quarter of its exponentials on the FMA units
-    {4, 2, 0, 24},  // ... with half
-    {4, 8, 4, 8},   // the fp8 kernel's mix
-    {4, 6, 4, 22},  // ... with a quarter of its exponentials on the FMA units
-    {4, 4, 4, 36},  // ... with half
-};
-constexpr int kNumIssueCases = sizeof(kIssueCases) / sizeof(kIssueCases[0]);
-
-int issue_cost_cases() { return kNumIssueCases; }
-
-bool issue_cost_case(int i, int* mfmas, int* exps, int* cvts, int* fmas) {
-  if (i < 0 || i >= kNumIssueCases) return false;
-  *mfmas = kIssueCases[i][0];
-  *exps = kIssueCases[i][1];
-  *cvts = kIssueCases[i][2];
-  *fmas = kIssueCases[i][3];
-  return true;
-}
 
 // Two workgroups of four waves per CU: two waves per SIMD.
 unsigned mfma_ceiling_workgroups() {
@@ -178,22 +96,6 @@ hipError_t launch_mfma_ceiling(float* out, int fp8, int iters, int random, hipSt
   else
     hipLaunchKernelGGL(mfma_loop_kernel<false>, dim3(nwg), dim3(256), 0, stream, out, iters, random);
   return hipGetLastError();
-}
-
-hipError_t launch_issue_cost(float* out, int i, int iters, hipStream_t stream) {
-  if (iters < 1 || i < 0 || i >= kNumIssueCases) return hipErrorInvalidValue;
-  const unsigned nwg = mfma_ceiling_workgroups();
-#define FA_ISSUE_CASE(NM, NE, NC, NF)                                                                        \
-  if (kIssueCases[i][0] == NM && kIssueCases[i][1] == NE && kIssueCases[i][2] == NC && kIssueCases[i][3] == NF) { \
-    hipLaunchKernelGGL((issue_loop_kernel<NM, NE, NC, NF>), dim3(nwg), dim3(256), 0, stream, out, iters);       \
-    return hipGetLastError();                                                                                \
-  }
-  FA_ISSUE_CASE(4, 0, 0, 0) FA_ISSUE_CASE(0, 8, 0, 0) FA_ISSUE_CASE(0, 0, 0, 16) FA_ISSUE_CASE(0, 8, 0, 16)
-  FA_ISSUE_CASE(4, 8, 0, 0) FA_ISSUE_CASE(4, 16, 0, 0) FA_ISSUE_CASE(4, 0, 0, 16) FA_ISSUE_CASE(4, 0, 0, 32)
-  FA_ISSUE_CASE(4, 4, 0, 10) FA_ISSUE_CASE(4, 3, 0, 17) FA_ISSUE_CASE(4, 2, 0, 24)
-  FA_ISSUE_CASE(4, 8, 4, 8) FA_ISSUE_CASE(4, 6, 4, 22) FA_ISSUE_CASE(4, 4, 4, 36)
-#undef FA_ISSUE_CASE
-  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

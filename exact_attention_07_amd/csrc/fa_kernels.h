@@ -39,7 +39,7 @@ int cu_count();
 unsigned mfma_ceiling_workgroups();
 double mfma_ceiling_flops(int fp8, int iters);
 hipError_t launch_mfma_ceiling(float* out, int fp8, int iters, int random, hipStream_t stream);
-// The issue-cost loop (fa_ceiling.hip): case i of issue_cost_cases() rounds
+// The issue-cost loop (fa_issue.hip): case i of issue_cost_cases() rounds
 // of MFMAs with exponentials, e4m3 packings and FMAs beside them; the same
 // grid and output size as the ceiling loop.
 int issue_cost_cases();
