@@ -195,21 +195,29 @@ __device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, con
   // byte offsets of tile t (past the last tile: past the buffer, reads zeros)
   auto tile_k = [&](int t) { return t < nt ? t * BC * D : Nk * D; };
   auto tile_v = [&](int t) { return t < nt ? t * BC : D * Nkp; };
+  // Without a causal mask the key tiles are taken in a rotated order: pass
+  // i < nt takes tile (i + rot) mod nt, with rot spread evenly over the
+  // head's query blocks, so that the workgroups of one head, which run side
+  // by side, each fetch a different tile at a time: a tile's first fetch
+  // (from HBM) then stalls one workgroup, not all of them at once, and the
+  // others find it in L2.  Passes from nt on are past the last tile.
+  const int rot = CAUSAL ? 0 : (int)((unsigned long long)(w.qpos0 / p.pos) * (unsigned)nt / (unsigned)p.nqb);
+  auto tile_of = [&](int i) { return (CAUSAL || i >= nt) ? i : (i + rot < nt ? i + rot : i + rot - nt); };
   // copy instruction i of this wave in iteration j (of parity par): K_{j+2}
   // into K slot par, then V_j into V slot par
   auto copy_one = [&](int j, auto par, int i) {
-    if (i < KCopy::MI) kc.issue_one(kres, tile_k(j + 2), kslot(par), spare, wave, i);
-    else vc.issue_one(vres, tile_v(j), vslot(par), spare, wave, i - KCopy::MI);
+    if (i < KCopy::MI) kc.issue_one(kres, tile_k(tile_of(j + 2)), kslot(par), spare, wave, i);
+    else vc.issue_one(vres, tile_v(tile_of(j)), vslot(par), spare, wave, i - KCopy::MI);
   };
   auto copy_all = [&](int j, auto par) {
-    kc.issue_all(kres, tile_k(j + 2), kslot(par), spare, wave);
-    vc.issue_all(vres, tile_v(j), vslot(par), spare, wave);
+    kc.issue_all(kres, tile_k(tile_of(j + 2)), kslot(par), spare, wave);
+    vc.issue_all(vres, tile_v(tile_of(j)), vslot(par), spare, wave);
   };
 
   // prologue: K_0, K_1, zeros into V slot 1, which iteration 0 reads (its
   // P V product then adds 0 x 0); S_0
-  kc.issue_all(kres, tile_k(0), kslot(P0{}), spare, wave);
-  kc.issue_all(kres, tile_k(1), kslot(P1{}), spare, wave);
+  kc.issue_all(kres, tile_k(tile_of(0)), kslot(P0{}), spare, wave);
+  kc.issue_all(kres, tile_k(tile_of(1)), kslot(P1{}), spare, wave);
   vc.issue_all(vres, D * Nkp, vslot(P1{}), spare, wave);
   vm_wait<0>();
   __syncthreads();
@@ -280,7 +288,7 @@ __device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, con
   // wave's tile ntw, past its last key, the mask turns every score into -inf.
   auto fused = [&](int j, auto par, f32x16 (&s)[KB], f32x16 (&sn)[KB], i32x8& pf, const i32x8& pprev) {
     using other = std::integral_constant<int, 1 - decltype(par)::value>;
-    const int j0 = j * BC;
+    const int j0 = tile_of(j) * BC;
     LDS_AS const char* knext = kslot(other{}) + koff_l;
     LDS_AS const char* vprev = vslot(other{}) + voff_l;
     i32x8 kbuf[KPF], vbuf[VPF];
