@@ -64,12 +64,27 @@ __device__ __forceinline__ void load_row_part(const __bf16* row, int sub, float 
   }
 }
 
-// x <- (x * signs) H_d / sqrt(d) for the row spread over 8 lanes.
+// The signs of the lane's D/8 elements (the same for every row), loaded
+// once per thread; all ones without a rotation.
 template <int D>
-__device__ __forceinline__ void rotate(float (&x)[D / 8], const float* signs, int sub) {
+__device__ __forceinline__ void load_signs(const float* signs, int sub, float (&sg)[D / 8]) {
+  constexpr int EPL = D / 8;
+  if (signs == nullptr) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) sg[e] = 1.0f;
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) sg[e] = signs[sub * EPL + e];
+}
+
+// x <- (x * signs) H_d / sqrt(d) for the row spread over 8 lanes (sg: the
+// lane's signs from load_signs).
+template <int D>
+__device__ __forceinline__ void rotate(float (&x)[D / 8], const float (&sg)[D / 8], int sub) {
   constexpr int EPL = D / 8;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) x[e] *= signs[sub * EPL + e];
+  for (int e = 0; e < EPL; ++e) x[e] *= sg[e];
   // in-lane butterflies, strides 1 .. EPL/2
 #pragma unroll
   for (int h = 1; h < EPL; h <<= 1)
@@ -80,15 +95,29 @@ __device__ __forceinline__ void rotate(float (&x)[D / 8], const float* signs, in
         x[e] = a + b;
         x[e + h] = a - b;
       }
-  // cross-lane butterflies, strides EPL, 2 EPL, 4 EPL (lanes sub ^ 1, 2, 4)
+  // cross-lane butterflies, strides EPL, 2 EPL, 4 EPL (lanes sub ^ 1, 2, 4):
+  // the partner's value by DPP (a VALU operand swizzle, no LDS round trip),
+  // then x <- other + s x with s = -1 in the upper lane of the pair (the
+  // fma rounds once, as the add or subtract would).  The 8 lanes of a row
+  // are aligned in the wave's rows of 16: lane ^ 1 and lane ^ 2 are quad
+  // permutations; lane ^ 4 is lane + 4 for banks 0 and 2 of a row (lanes
+  // 0-3, 8-11: sub < 4) and lane - 4 for banks 1 and 3.
 #pragma unroll
-  for (int bit = 1; bit < 8; bit <<= 1) {
-    const bool upper = (sub & bit) != 0;
+  for (int e = 0; e < EPL; ++e) {
+    const float o1 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[e]), 0xB1, 0xF, 0xF, false));
+    x[e] = __builtin_fmaf((sub & 1) ? -1.f : 1.f, x[e], o1);
+  }
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      const float other = __shfl_xor(x[e], bit, 64);
-      x[e] = upper ? other - x[e] : x[e] + other;
-    }
+  for (int e = 0; e < EPL; ++e) {
+    const float o2 = __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x[e]), 0x4E, 0xF, 0xF, false));
+    x[e] = __builtin_fmaf((sub & 2) ? -1.f : 1.f, x[e], o2);
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    const int xi = __builtin_bit_cast(int, x[e]);
+    int o4 = __builtin_amdgcn_update_dpp(0, xi, 0x104, 0xF, 0x5, false);   // row_shl:4, banks 0, 2
+    o4 = __builtin_amdgcn_update_dpp(o4, xi, 0x114, 0xF, 0xA, false);      // row_shr:4, banks 1, 3
+    x[e] = __builtin_fmaf((sub & 4) ? -1.f : 1.f, x[e], __builtin_bit_cast(float, o4));
   }
   const float inv = 1.0f / __builtin_sqrtf((float)D);
 #pragma unroll
@@ -144,27 +173,32 @@ __global__ __launch_bounds__(256) void amax_kernel(const __bf16* __restrict__ q,
   const int tensor = blockIdx.y;  // 0: Q, 1: K, 2: V
   const long long rows = tensor == 0 ? rows_q : rows_k;
   const __bf16* base = tensor == 0 ? q : tensor == 1 ? k : v;
+  const bool rot = tensor < 2 && signs != nullptr;
+  float sg[D / 8];
+  load_signs<D>(rot ? signs : nullptr, sub, sg);
   float m = 0.f;
   for (long long r0 = (long long)blockIdx.x * 32; r0 < rows; r0 += (long long)gridDim.x * 32) {
     const long long row = r0 + (threadIdx.x >> 3);
     // rows past the end are zero (the shuffles of rotate() stay uniform)
     float x[D / 8] = {};
     if (row < rows) load_row_part<D>(base + row * D, sub, x);
-    if (tensor < 2 && signs != nullptr) rotate<D>(x, signs, sub);
+    if (rot) rotate<D>(x, sg, sub);
 #pragma unroll
     for (int e = 0; e < D / 8; ++e) m = fmaxf(m, fabsf(x[e]));
   }
   amax_to(&amax[tensor], m);
 }
 
-// pass 2 for Q and K: rotate again and quantise; descale written by block 0
+// pass 2 for Q and K: rotate again and quantise; descale written by block 0.
+// A workgroup takes QK_GROUPS consecutive groups of 32 rows, so that each
+// thread loads its signs once for that many rows.
+constexpr int QK_GROUPS = 4;
 template <int D>
 __global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16* __restrict__ q, const __bf16* __restrict__ k,
                                                        const float* __restrict__ signs, long long rows_q,
                                                        long long rows_k, uint8_t* __restrict__ q8,
                                                        uint8_t* __restrict__ k8, const unsigned* __restrict__ amax,
                                                        float* __restrict__ descale, float c0) {
-  const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int sub = threadIdx.x & 7;
   const int tensor = blockIdx.y;  // 0: Q, 1: K
   const long long rows = tensor == 0 ? rows_q : rows_k;
@@ -175,26 +209,32 @@ __global__ __launch_bounds__(256) void quant_qk_kernel(const __bf16* __restrict_
     if (tensor == 0) descale[2] = scale_of(amax[2]);
   }
   const float inv = mult / s;  // s is a power of two: the division is exact
-  float x[D / 8] = {};
-  const bool ok = row < rows;
-  if (ok) load_row_part<D>((tensor == 0 ? q : k) + row * D, sub, x);
-  if (signs != nullptr) rotate<D>(x, signs, sub);
-  if (!ok) return;
-  uint8_t* out = (tensor == 0 ? q8 : k8) + row * D + sub * (D / 8);
+  float sg[D / 8];
+  if (signs != nullptr) load_signs<D>(signs, sub, sg);
+  for (int gi = 0; gi < QK_GROUPS; ++gi) {
+    const long long row = ((long long)blockIdx.x * QK_GROUPS + gi) * 32 + (threadIdx.x >> 3);
+    if (((long long)blockIdx.x * QK_GROUPS + gi) * 32 >= rows) break;  // uniform over the workgroup
+    float x[D / 8] = {};
+    const bool ok = row < rows;
+    if (ok) load_row_part<D>((tensor == 0 ? q : k) + row * D, sub, x);
+    if (signs != nullptr) rotate<D>(x, sg, sub);
+    if (!ok) continue;
+    uint8_t* out = (tensor == 0 ? q8 : k8) + row * D + sub * (D / 8);
 #pragma unroll
-  for (int c = 0; c < D / 8 / 16; ++c) {
-    u32x4 w;
+    for (int c = 0; c < D / 8 / 16; ++c) {
+      u32x4 w;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = c * 16 + e * 4;
-      w[e] = pack4(x[i] * inv, x[i + 1] * inv, x[i + 2] * inv, x[i + 3] * inv);
+      for (int e = 0; e < 4; ++e) {
+        const int i = c * 16 + e * 4;
+        w[e] = pack4(x[i] * inv, x[i + 1] * inv, x[i + 2] * inv, x[i + 3] * inv);
+      }
+      *(u32x4*)(out + c * 16) = w;
     }
-    *(u32x4*)(out + c * 16) = w;
-  }
-  if constexpr (D / 8 < 16) {  // d = 64: 8 bytes per lane
-    unsigned w0 = pack4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
-    unsigned w1 = pack4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
-    *(unsigned long long*)out = ((unsigned long long)w1 << 32) | w0;
+    if constexpr (D / 8 < 16) {  // d = 64: 8 bytes per lane
+      unsigned w0 = pack4(x[0] * inv, x[1] * inv, x[2] * inv, x[3] * inv);
+      unsigned w1 = pack4(x[4] * inv, x[5] * inv, x[6] * inv, x[7] * inv);
+      *(unsigned long long*)out = ((unsigned long long)w1 << 32) | w0;
+    }
   }
 }
 
@@ -260,7 +300,7 @@ static hipError_t launch_prepare_d(const void* q, const void* k, const void* v, 
   const dim3 g1((unsigned)(groups < 512 ? groups : 512), 3);
   hipLaunchKernelGGL(amax_kernel<D>, g1, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k,
                      (const __bf16*)v, signs, rows_q, rows_k, amax);
-  const dim3 g2((unsigned)((rmax + 31) / 32), 2);
+  const dim3 g2((unsigned)((groups + QK_GROUPS - 1) / QK_GROUPS), 2);
   hipLaunchKernelGGL(quant_qk_kernel<D>, g2, dim3(256), 0, stream, (const __bf16*)q, (const __bf16*)k, signs, rows_q,
                      rows_k, (uint8_t*)q8, (uint8_t*)k8, (const unsigned*)amax, descale, c0);
   const dim3 g3((unsigned)((long long)(Nkp / FP8_BC) * heads_kv));
