@@ -227,6 +227,12 @@ def integer_logit_inputs(B, Hq, Hkv, Nq, Nk, d, seed):
     return q, k, v
 
 
+# Many query blocks over a ragged key range: non-causal workgroups take their
+# key tiles in an order rotated by their query block, so the partial last
+# tile falls in the middle of most workgroups' loops.
+ROTATED_SHAPES = [(1, 2, 2, 1024, 1000), (1, 4, 4, 2048, 2000)]
+
+
 # gfx950's fp8 MFMA adds each group of 8 consecutive products of a lane with
 # the bits below 2^(e-14) of every product dropped, e the exponent of the
 # group's largest product: at most 8 * 2^-13 = 2^-10 of that product per group
@@ -258,6 +264,11 @@ def test_exact_probabilities_elementwise(api, shape, d, causal):
     np.testing.assert_array_equal(np.isneginf(lse), inf_ref)
     le = np.abs(lse[~inf_ref] - lse_ref[~inf_ref])
     assert (le <= 4e-7 * np.abs(lse_ref[~inf_ref]) + 1e-5).all(), f"max |dLSE| {le.max():.3e}"
+
+
+@pytest.mark.parametrize("shape", ROTATED_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_exact_probabilities_rotated_key_order(api, shape):
+    test_exact_probabilities_elementwise(api, shape, 128, False)
 
 
 def test_fp8_mfma_group_sum_granularity(api):
