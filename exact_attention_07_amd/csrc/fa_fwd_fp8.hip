@@ -198,9 +198,10 @@ __device__ __forceinline__ void fwd_fp8_item(const uint8_t* __restrict__ Q8, con
   // Without a causal mask the key tiles are taken in a rotated order: pass
   // i < nt takes tile (i + rot) mod nt, with rot spread evenly over the
   // head's query blocks, so that the workgroups of one head, which run side
-  // by side, each fetch a different tile at a time: a tile's first fetch
-  // (from HBM) then stalls one workgroup, not all of them at once, and the
-  // others find it in L2.  Passes from nt on are past the last tile.
+  // by side, each fetch a different tile at a time instead of all waiting
+  // on the same first fetch (measured 1-1.5 % faster on the non-causal
+  // d = 128 workload, though L2 then fetches some tiles again).  Passes
+  // from nt on are past the last tile.
   const int rot = CAUSAL ? 0 : (int)((unsigned long long)(w.qpos0 / p.pos) * (unsigned)nt / (unsigned)p.nqb);
   auto tile_of = [&](int i) { return (CAUSAL || i >= nt) ? i : (i + rot < nt ? i + rot : i + rot - nt); };
   // copy instruction i of this wave in iteration j (of parity par): K_{j+2}
