@@ -24,7 +24,7 @@ context, a head dimension of 256, and FP8 with outliers):
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 
 import numpy as np
 
