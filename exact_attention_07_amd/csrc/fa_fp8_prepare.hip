@@ -46,11 +46,9 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 constexpr float E4M3_MAX = 448.0f;
 constexpr int FP8_BC = 64;  // key block of the V^T permutation (the attention kernel's tile)
 
-// Position of key k (0..63) of a 64-key block in the permuted V^T order:
-// key bits [b5 | b4 b3 | b2 | b1 b0] -> position bits [b2 | b5 | b4 b3 | b1 b0].
-__device__ __forceinline__ int v_perm64(int k) {
-  return (((k >> 2) & 1) << 5) | (((k >> 5) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
-}
+// The permuted V^T order of a 64-key block: key k with bits
+// [b5 | b4 b3 | b2 | b1 b0] goes to position [b2 | b5 | b4 b3 | b1 b0]
+// (the order in which the attention kernel's P fragment holds its keys).
 
 // Load the EPL = D/8 elements of lane `sub` (0..7) of a row as fp32.
 template <int D>
@@ -267,7 +265,8 @@ __global__ __launch_bounds__(256) void quant_v_kernel(const __bf16* __restrict__
     }
   }
   __syncthreads();
-  // write: row d of V^T gets 64 bytes, byte p = key with v_perm64(key) == p
+  // write: row d of V^T gets 64 bytes, byte p = the key that the permuted
+  // order puts at position p
   uint8_t* dst = v8t + head * (long long)D * Nkp + (long long)blk * FP8_BC;
   for (int idx = threadIdx.x; idx < D * (FP8_BC / 4); idx += blockDim.x) {
     const int d = idx / (FP8_BC / 4), p4 = (idx % (FP8_BC / 4)) * 4;
