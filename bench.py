@@ -43,11 +43,12 @@ Under rocprofv3 counters (GRBM_GUI_ACTIVE) the same run shows the clock
 directly: the evidence that on this chip the clock under dense matrix work,
 and hence the reachable matrix rate, depends on the data the MFMAs toggle.
 
---issue-sweep measures only fa_issue_cost: rounds of bf16 MFMAs with
-exponentials, e4m3 packings and FMAs beside them (the bf16 and fp8 kernels'
-mixes per four MFMAs, and the same with part of the exponentials replaced
-by seven FMA-pipe instructions each), each case's median launch time against
-the MFMA-only case; --issue-summary PATH writes the table to PATH.
+--issue-sweep measures only fa_issue_cost: rounds of MFMAs (bf16, or the
+fp8 kernel's e4m3 forms) with exponentials, e4m3 packings and FMAs beside
+them (the bf16 and fp8 kernels' mixes, and the same with part of the
+exponentials replaced by seven FMA-pipe instructions each), each case's
+median launch time against the MFMA-only case of the same instruction;
+--issue-summary PATH writes the table to PATH.
 
 --exp2-emulated Q times fa_fwd_exp2_emulated (Q of every four exponentials
 computed by a polynomial on the FMA pipe) in place of fa_fwd on a bf16
@@ -360,10 +361,11 @@ def ceiling_sweep(torch, api, launches: int, warm: int):
 
 
 def issue_sweep(torch, api, launches: int, warm: int, iters: int, summary: str | None, command: str):
-    """fa_issue_cost: every case (rounds of bf16 MFMAs with exponentials, e4m3
+    """fa_issue_cost: every case (rounds of MFMAs with exponentials, e4m3
     packings and FMAs beside them, two waves per SIMD), median launch time
     over `launches` launches after `warm` untimed ones, against the
-    MFMA-only case.  With `summary`, also writes the table there."""
+    MFMA-only case of the same matrix instruction.  With `summary`, also
+    writes the table there."""
     stream = torch.cuda.current_stream()
     out = torch.empty(api.mfma_ceiling_out_bytes() // 4, dtype=torch.float32, device="cuda")
     cases = api.issue_cost_cases()
@@ -379,24 +381,33 @@ def issue_sweep(torch, api, launches: int, warm: int, iters: int, summary: str |
         torch.cuda.synchronize()
         ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
         rows.append(dict(c, case=i, launch_ms=round(ms, 4)))
-    base = rows[0]["launch_ms"]
+    # each case against the MFMA-only round of its own instruction (the
+    # cases without matrix work against the bf16 one)
+    base = {}
     for r in rows:
-        r["vs_mfma_only"] = round(r["launch_ms"] / base, 3)
-        log(f"issue cost case {r['case']}: {r['mfmas']} MFMA, {r['exps']} exp, {r['cvts']} e4m3 packings, "
-            f"{r['fmas']} FMA per round: {r['launch_ms']:.4f} ms ({r['vs_mfma_only']:.3f} x MFMA only)")
+        if r["mfmas"] > 0 and r["exps"] == r["cvts"] == r["fmas"] == 0:
+            base.setdefault(r["mfma"], r["launch_ms"])
+    for r in rows:
+        ref = base[r["mfma"]] if r["mfmas"] > 0 else base["bf16"]
+        r["vs_mfma_only"] = round(r["launch_ms"] / ref, 3)
+        log(f"issue cost case {r['case']}: {r['mfmas']} {r['mfma']} MFMA, {r['exps']} exp, {r['cvts']} e4m3 "
+            f"packings, {r['fmas']} FMA per round: {r['launch_ms']:.4f} ms ({r['vs_mfma_only']:.3f} x MFMA only)")
     line = {"metric": "issue cost of vector work beside MFMA", "unit": "ms per launch", "iters": iters,
             "launches": launches, "warm_launches": warm, "rows": rows}
     print(json.dumps(line), flush=True)
     if summary:
         with open(summary, "w") as f:
-            f.write("# fa_issue_cost: rounds of v_mfma_f32_32x32x16_bf16 (random operands) with v_exp_f32,\n"
-                    "# v_cvt_pk_fp8_f32 and v_fma_f32 beside them, per wave, two waves per SIMD on every CU;\n"
+            f.write("# fa_issue_cost: rounds of MFMAs (random operands; bf16 = v_mfma_f32_32x32x16_bf16,\n"
+                    "# fp8 = v_mfma_f32_32x32x64_f8f6f4 on e4m3, fp8_scaled = the same with E8M0 scale operands,\n"
+                    "# fp8_alternating = the two e4m3 forms in turn) with v_exp_f32, v_cvt_pk_fp8_f32 and\n"
+                    "# v_fma_f32 beside them, per wave, two waves per SIMD on every CU; each case against the\n"
+                    "# MFMA-only case of the same instruction (cases without MFMAs against the bf16 one);\n"
                     f"# median launch time of {launches} launches after {warm} untimed ones, {iters} rounds per wave\n"
                     f"# command (from the repository root on the MI355X box):\n#   {command}\n")
-            f.write("case  mfmas  exps  cvts  fmas  launch_ms  vs_mfma_only\n")
+            f.write("case  mfmas  mfma             exps  cvts  fmas  launch_ms  vs_mfma_only\n")
             for r in rows:
-                f.write(f"{r['case']:4d}  {r['mfmas']:5d}  {r['exps']:4d}  {r['cvts']:4d}  {r['fmas']:4d}  "
-                        f"{r['launch_ms']:9.4f}  {r['vs_mfma_only']:12.3f}\n")
+                f.write(f"{r['case']:4d}  {r['mfmas']:5d}  {r['mfma']:15s}  {r['exps']:4d}  {r['cvts']:4d}  "
+                        f"{r['fmas']:4d}  {r['launch_ms']:9.4f}  {r['vs_mfma_only']:12.3f}\n")
 
 
 def main():

@@ -72,6 +72,8 @@ def lib() -> ctypes.CDLL:
     ip = ctypes.POINTER(ctypes.c_int)
     L.fa_issue_cost_case.argtypes = [i, ip, ip, ip, ip]
     L.fa_issue_cost_case.restype = ctypes.c_int
+    L.fa_issue_cost_case_mfma.argtypes = [i, ip]
+    L.fa_issue_cost_case_mfma.restype = ctypes.c_int
     L.fa_issue_cost.argtypes = [vp, ctypes.c_size_t, i, i, vp]
     L.fa_issue_cost.restype = ctypes.c_int
     L.fa_status_string.argtypes = [ctypes.c_int]
@@ -360,14 +362,20 @@ def mfma_ceiling(out, fp8: bool, iters: int, random: bool = True, stream=None) -
                                  _stream(stream)), "fa_mfma_ceiling")
 
 
+# matrix instruction of an issue-cost case, by the kind number fa.h gives
+ISSUE_MFMA = ("bf16", "fp8", "fp8_scaled", "fp8_alternating")
+
+
 def issue_cost_cases() -> list:
-    """The issue-cost loop's cases: one dict of per-round counts per case."""
+    """The issue-cost loop's cases: one dict of per-round counts (and the MFMA kind) per case."""
     L = lib()
     out = []
     for i in range(int(L.fa_issue_cost_cases())):
         c = [ctypes.c_int() for _ in range(4)]
         _check(L.fa_issue_cost_case(i, *[ctypes.byref(x) for x in c]), "fa_issue_cost_case")
-        out.append(dict(zip(("mfmas", "exps", "cvts", "fmas"), (x.value for x in c))))
+        kind = ctypes.c_int()
+        _check(L.fa_issue_cost_case_mfma(i, ctypes.byref(kind)), "fa_issue_cost_case_mfma")
+        out.append(dict(zip(("mfmas", "exps", "cvts", "fmas"), (x.value for x in c)), mfma=ISSUE_MFMA[kind.value]))
     return out
 
 

@@ -398,6 +398,11 @@ fa_status fa_issue_cost_case(int i, int* mfmas, int* exps, int* cvts, int* fmas)
   return fa::issue_cost_case(i, mfmas, exps, cvts, fmas) ? FA_OK : FA_ERR_FLAG;
 }
 
+fa_status fa_issue_cost_case_mfma(int i, int* kind) {
+  if (!kind) return FA_ERR_NULL;
+  return fa::issue_cost_case_mfma(i, kind) ? FA_OK : FA_ERR_FLAG;
+}
+
 fa_status fa_issue_cost(float* out, size_t out_bytes, int i, int iters, void* stream) {
   if (!out) return FA_ERR_NULL;
   if (i < 0 || i >= fa::issue_cost_cases()) return FA_ERR_FLAG;

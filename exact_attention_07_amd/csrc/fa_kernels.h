@@ -44,6 +44,9 @@ hipError_t launch_mfma_ceiling(float* out, int fp8, int iters, int random, hipSt
 // grid and output size as the ceiling loop.
 int issue_cost_cases();
 bool issue_cost_case(int i, int* mfmas, int* exps, int* cvts, int* fmas);
+// the case's matrix instruction: 0 bf16 32x32x16, 1 e4m3 32x32x64, 2 the
+// same with E8M0 scale operands, 3 the two e4m3 forms alternating
+bool issue_cost_case_mfma(int i, int* kind);
 hipError_t launch_issue_cost(float* out, int i, int iters, hipStream_t stream);
 
 // Enqueue the forward kernel.  c = scale * log2(e).  f32 selects fp32

@@ -325,16 +325,21 @@ fa_status fa_mfma_ceiling(float* out, size_t out_bytes, int fp8, int iters, int 
  * polynomial on the FMA units because on its GPU the exponential unit is
  * the narrow one.  Whether that can pay depends on what an exponential
  * costs against an FMA when both sit beside matrix work.  Case i is a loop
- * whose rounds hold `mfmas` v_mfma_f32_32x32x16_bf16 (random operands),
+ * whose rounds hold `mfmas` MFMAs of the case's kind (random operands),
  * `exps` v_exp_f32, `cvts` v_cvt_pk_fp8_f32 and `fmas` v_fma_f32 per wave,
  * spread evenly, two waves per SIMD on every CU; the caller times launches
- * of each case against the MFMA-only case 0.  The cases include the bf16
- * and fp8 kernels' mixes per four MFMAs, each also with a quarter and with
- * half of its exponentials replaced by seven fast instructions.
+ * of each case against the MFMA-only case of the same kind.  The kinds:
+ * 0 v_mfma_f32_32x32x16_bf16, 1 v_mfma_f32_32x32x64_f8f6f4 on e4m3,
+ * 2 the same with E8M0 scale operands (both 2^0), 3 kinds 2 and 1
+ * alternating (the fp8 kernel's S and P V products).  The cases include the
+ * bf16 and fp8 kernels' mixes per four bf16 MFMAs, each also with a quarter
+ * and with half of its exponentials replaced by seven fast instructions,
+ * and the fp8 kernel's mix per two of its own MFMAs.
  *
  *   fa_issue_cost_cases()     number of cases
  *   fa_issue_cost_case(i, …)  the case's per-round counts (FA_ERR_NULL for a
  *                             null pointer, FA_ERR_FLAG for i out of range)
+ *   fa_issue_cost_case_mfma(i, kind)  the case's MFMA kind (same errors)
  *   out, out_bytes            as for fa_mfma_ceiling
  *   iters                     rounds per wave, >= 1
  * Errors: FA_ERR_NULL (out), FA_ERR_FLAG (i out of range), FA_ERR_SHAPE
@@ -343,6 +348,7 @@ fa_status fa_mfma_ceiling(float* out, size_t out_bytes, int fp8, int iters, int 
  */
 int fa_issue_cost_cases(void);
 fa_status fa_issue_cost_case(int i, int* mfmas, int* exps, int* cvts, int* fmas);
+fa_status fa_issue_cost_case_mfma(int i, int* kind);
 fa_status fa_issue_cost(float* out, size_t out_bytes, int i, int iters, void* stream);
 
 #ifdef __cplusplus

@@ -256,6 +256,19 @@ def test_issue_cost_cases_and_rejections_on_the_host(lib):
     assert lib.fa_issue_cost_case(n, *refs) == 8          # FA_ERR_FLAG
     assert lib.fa_issue_cost_case(-1, *refs) == 8
     assert lib.fa_issue_cost_case(0, None, *refs[1:]) == 1  # FA_ERR_NULL
+    lib.fa_issue_cost_case_mfma.argtypes = [ctypes.c_int, ip]
+    kind = ctypes.c_int()
+    kinds = []
+    for i in range(n):
+        assert lib.fa_issue_cost_case_mfma(i, ctypes.byref(kind)) == 0
+        kinds.append(kind.value)
+    assert kinds[0] == 0 and set(kinds) <= {0, 1, 2, 3}
+    # every kind with a case of matrix work alone, which its other cases are timed against
+    for k in set(kinds):
+        assert any(kinds[i] == k and lib.fa_issue_cost_case(i, *refs) == 0 and c[0].value > 0
+                   and c[1].value == c[2].value == c[3].value == 0 for i in range(n))
+    assert lib.fa_issue_cost_case_mfma(n, ctypes.byref(kind)) == 8   # FA_ERR_FLAG
+    assert lib.fa_issue_cost_case_mfma(0, None) == 1                 # FA_ERR_NULL
     f = lib.fa_issue_cost
     f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     assert f(None, 1 << 20, 0, 10, None) == 1             # FA_ERR_NULL
