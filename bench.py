@@ -7,8 +7,12 @@ chosen standing workload (default: the causal GQA long-context workload B=2,
 Hq=32, Hkv=8, N=8192, d=128, bf16): one fa_fwd (or fa_fwd_f32) call, or for
 the fp8 workload (--config 5: B=4, H=16, N=8192, d=128, e4m3) fa_fp8_prepare (Hadamard rotation of Q and K,
 per-tensor scales, e4m3 codes) followed by fa_fwd_fp8.  Inputs are resident
-in HBM before timing starts; K steps are timed back to back with HIP events
-on the stream the kernels run on.  Prints one JSON line on stdout
+in HBM before timing starts; the step first runs untimed for --prewarm-ms
+(default 250 ms of wall time; from a cold start the GPU's clocks need tens
+of milliseconds of load to leave their idle state, and launches of the
+default step fall from ~1.2 ms to a steady ~0.92 ms over the first ~30),
+then W warmup steps; K steps are timed back to back with HIP events on the
+stream the kernels run on.  Prints one JSON line on stdout
 (diagnostics go to stderr):
 
   value     attention forward TFLOP/s = 4*B*Hq*Nq*Nk*d (halved when causal) / step time
@@ -193,6 +197,41 @@ def cpu_baseline_pool(w, x, budget_s: float, dout=None, bytes_total=None):
                       f"{cores} processes with one BLAS thread each, {wall:.1f} s wall"}
 
 
+
+def prewarm(torch, step, ms: float) -> int:
+    """Run `step` untimed, in batches of 10 with a synchronisation after each,
+    until `ms` milliseconds of wall time have passed; returns the number of
+    steps run.  From a cold start the GPU's clocks take tens of milliseconds
+    of load to leave their idle state: launches of the causal GQA step fall
+    from about 1.2 ms to a steady 0.92 ms over the first ~30 (one box), so a
+    few warmup steps alone would time the ramp rather than the kernel."""
+    n = 0
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        n += 10
+    return n
+
+def cold_start_trace(torch, stream, step, n: int, flops: float):
+    """`n` steps right after setup, no untimed ones before them, each timed
+    with its own events: the launch-by-launch settling the prewarm exists
+    for.  Prints one JSON line with the per-launch milliseconds."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = [round(a.elapsed_time(b), 4) for a, b in ev]
+    tail = ms[len(ms) // 2:]
+    log(f"cold start: launches 1-10 {ms[:10]}; second half mean {np.mean(tail):.4f} ms")
+    print(json.dumps({"metric": "per-launch time from a cold start", "unit": "ms", "launch_ms": ms,
+                      "second_half_mean_ms": round(float(np.mean(tail)), 4),
+                      "second_half_tflops": round(flops / (float(np.mean(tail)) * 1e-3) / 1e12, 2)}), flush=True)
+
+
 def bench_backward(args, torch, api, gen):
     w, x = gen.make_config(3)
     dout = gen.make_dout(w, (3,))
@@ -217,6 +256,7 @@ def bench_backward(args, torch, api, gen):
     def stage_dkdv():
         api.fa_bwd_dkdv(q, k, v, o, lse, do, dk, dv, w.softmax_scale, w.causal, ws, stream)
 
+    prewarm_steps = prewarm(torch, lambda: (stage_dq(), stage_dkdv()), args.prewarm_ms)
     for _ in range(args.warmup):
         stage_dq()
         stage_dkdv()
@@ -276,6 +316,7 @@ def bench_backward(args, torch, api, gen):
     line = {
         "metric": "attention bwd TFLOP/s + % of MFMA peak (bf16, causal GQA, N=8K, d=128)",
         "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "prewarm": {"ms": args.prewarm_ms, "steps": prewarm_steps},
         "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) Q, K, V, dO; O and LSE from fa_fwd; resident in HBM before timing)",
@@ -415,6 +456,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cold-start", type=int, default=0, metavar="N",
+                    help="time N launches one by one right after setup (no prewarm, no warmup), print them, exit")
+    ap.add_argument("--prewarm-ms", type=float, default=250.0,
+                    help="untimed steps for at least this long (wall time) before the warmup steps, so that the "
+                         "GPU's clocks have left their idle state")
     ap.add_argument("--config", default="3", help="standing workload 1..5, decode or backward")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -510,6 +556,10 @@ def main():
         def attend():
             fwd(q, k, v, o, lse, w.softmax_scale, w.causal, stream)
 
+    if args.cold_start:
+        cold_start_trace(torch, stream, lambda: (prepare(), attend()), args.cold_start, w.flops())
+        return
+    prewarm_steps = prewarm(torch, lambda: (prepare(), attend()), args.prewarm_ms)
     for _ in range(args.warmup):
         prepare()
         attend()
@@ -579,6 +629,7 @@ def main():
         line = {
             "metric": "attention decode step HBM GB/s (bf16, GQA, Nq=1, Nk=32K, d=128)",
             "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "prewarm": {"ms": args.prewarm_ms, "steps": prewarm_steps},
             "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16", "data": "synthetic (seeded N(0,1), resident in HBM before timing)",
             "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
@@ -612,6 +663,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm": {"ms": args.prewarm_ms, "steps": prewarm_steps},
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

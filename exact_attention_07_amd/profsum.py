@@ -195,6 +195,35 @@ def summarize_ceiling(dirs, commands, out_path, launches, warm):
     return out_path
 
 
+def summarize_cold_start(dirs, commands, out_path, first: int = 40):
+    """GRBM_GUI_ACTIVE per dispatch of a `bench.py --cold-start N` run: the
+    clock (counter / 8 XCDs / duration) and duration of each of the first
+    `first` dispatches of the attention kernel, then the mean over the rest."""
+    files = glob.glob(os.path.join(dirs[0], "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {dirs[0]}")
+    disp = _dispatch_counters(files[0], "fa_fwd_bf16_kernel")
+    rows = [disp[d] for d in sorted(disp, key=int)]
+    if len(rows) <= first:
+        raise SystemExit(f"{len(rows)} dispatches, need more than {first}")
+    lines = ["# rocprofv3 GRBM_GUI_ACTIVE of fa_fwd_bf16_kernel, launch by launch from a cold start",
+             "# (no untimed launches before them), with the clock each launch ran at",
+             "# (GRBM_GUI_ACTIVE / 8 XCDs / duration)",
+             "# command (from the repository root on the MI355X box):"]
+    lines += [f"#   {c}" for c in commands]
+    lines.append("launch  ms  clock_ghz")
+    for i, r in enumerate(rows[:first]):
+        lines.append(f"{i + 1:4d}  {r['_ns'] * 1e-6:.4f}  {r['GRBM_GUI_ACTIVE'] / N_XCD / r['_ns']:.3f}")
+    rest = rows[first:]
+    ns = sum(r["_ns"] for r in rest) / len(rest)
+    clk = sum(r["GRBM_GUI_ACTIVE"] / N_XCD / r["_ns"] for r in rest) / len(rest)
+    lines.append(f"launches {first + 1}-{len(rows)}: mean {ns * 1e-6:.4f} ms at {clk:.3f} GHz")
+    lines.append(f"kernel_source_sha256: {source_hash('bf16')}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out_path
+
+
 def _kernel_name(path: str, dispatch_id: str) -> str:
     for r in csv.DictReader(open(path)):
         if r["Dispatch_Id"] == dispatch_id:
@@ -225,7 +254,7 @@ def load(config, root=ROOT):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    ap.add_argument("--config", required=True, help="workload (1..5, decode, backward) or ceiling")
+    ap.add_argument("--config", required=True, help="workload (1..5, decode, backward), ceiling or cold_start")
     ap.add_argument("--launches", type=int, default=60, help="ceiling: timed launches per case")
     ap.add_argument("--warm", type=int, default=600, help="ceiling: untimed launches before each case")
     ap.add_argument("--out", required=True)
@@ -234,6 +263,9 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.config == "ceiling":
         print(summarize_ceiling(a.dirs, a.cmd, a.out, a.launches, a.warm))
+        return
+    if a.config == "cold_start":
+        print(summarize_cold_start(a.dirs, a.cmd, a.out))
         return
     cfg = int(a.config) if a.config.isdigit() else a.config
     print(summarize(cfg, a.dirs, a.cmd, a.out))

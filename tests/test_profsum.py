@@ -114,3 +114,27 @@ def test_ceiling_summary_splits_random_and_constant(tmp_path):
     assert abs(float(s["fp8_random_mfma_busy"]) - 0.9) < 1e-4
     with pytest.raises(SystemExit):
         profsum.summarize_ceiling([a], ["cmd"], out, launches + 1, warm)
+
+
+def test_cold_start_summary_lists_each_early_launch_and_averages_the_rest(tmp_path):
+    k = "void fa::fa_fwd_bf16_kernel<128, true, 8, 0>(...)"
+    d = str(tmp_path / "c")
+    # 50 launches: the clock dips on launches 3-5, then holds 1.8 GHz; each
+    # launch's duration follows from a fixed cycle count at its clock
+    clocks = [1.75, 1.73, 1.45, 1.5, 1.6] + [1.8] * 45
+    cycles = 1.7e6
+    disp = []
+    for i, c in enumerate(clocks):
+        ns = int(round(cycles / c))
+        disp.append((i + 1, k, ns, {"GRBM_GUI_ACTIVE": c * ns * profsum.N_XCD}))
+    disp.append((99, "other_kernel", 10, {"GRBM_GUI_ACTIVE": 1.0}))
+    write_pass(d, disp)
+    out = str(tmp_path / "cold.txt")
+    profsum.summarize_cold_start([d], ["cmd"], out, first=10)
+    lines = [l for l in open(out) if not l.startswith("#")]
+    rows = [l.split() for l in lines[1:11]]
+    assert [int(r[0]) for r in rows] == list(range(1, 11))
+    assert [float(r[2]) for r in rows] == pytest.approx(clocks[:10], abs=2e-3)
+    assert float(rows[2][1]) == pytest.approx(cycles / 1.45 * 1e-6, rel=1e-3)
+    assert "launches 11-50" in lines[11] and "1.800 GHz" in lines[11]
+    assert fields_of(out)["kernel_source_sha256"] == profsum.source_hash("bf16")
