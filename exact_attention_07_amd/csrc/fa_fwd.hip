@@ -340,6 +340,11 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
   constexpr int NMF = DS * KB;        // MFMAs of one S^T tile
   constexpr int NPV = DB * PS;        // MFMAs of one P V product
   static_assert(NMF == NPV, "S and P V streams alternate");
+  // At d <= 128 the MFMAs go in pairs of the same product, S S P V P V
+  // (0.4-0.65 % faster than strict alternation at d = 128, on two boxes);
+  // at d = 256 they alternate P V, S (1.3 % faster there).
+  constexpr int GRP = D == 256 ? 1 : 2;
+  static_assert(NMF % GRP == 0, "whole groups of each product");
   constexpr int NSC = KB * 16;        // scores per lane per tile
   constexpr int NCH = NMF + NPV;      // chunks of the fused phase
   constexpr int KPF = 2, VPF = 2;     // LDS fragment reads in flight per stream
@@ -503,10 +508,8 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
     for (int kb = 0; kb < KB; ++kb) sn.v[kb][0] = (f32x16){};
 #pragma unroll
     for (int ch = 0; ch < NCH; ++ch) {
-      const int m = ch / 2;
-      // a chunk pair: the P V MFMA first, then the S MFMA (measured 0.5-2 %
-      // faster than the other order)
-      if (ch % 2 == 1) {
+      const int m = (ch / (2 * GRP)) * GRP + (ch % GRP);
+      if (GRP > 1 ? (ch % (2 * GRP)) < GRP : (ch % 2) == 1) {
         // S_{j+1}: MFMA m, reading the K fragment KPF MFMAs ahead
         const int ds = m / KB, kb = m % KB;
         sn.v[kb][0] = mfma(kbuf[m % KPF], qf[0][ds], sn.v[kb][0]);
