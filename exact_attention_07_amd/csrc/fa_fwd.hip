@@ -483,10 +483,20 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
   // score (flush_pair; after the last score the caller flushes it).
   // Otherwise the odd member of a pair adds itself and packs the pair.
   constexpr bool DEFER = D == 128;
+  auto arg_of = [&](const Scores<D>& s, int sc, float mu) {
+    return __builtin_fmaf(s.v[sc / 16][0][sc % 16], c, -mu);
+  };
   auto score = [&](const Scores<D>& s, Probs& pf, int sc, float mu, float& part0, float& part1, float& even,
-                   float& odd, float& partq) {
+                   float& odd, float& partq, float& next_arg) {
     const int skb = sc / 16, si = sc % 16;
-    const float arg = __builtin_fmaf(s.v[skb][0][si], c, -mu);
+    float arg;
+    if constexpr (DEFER) {
+      // the argument was formed one score ahead
+      arg = next_arg;
+      if (sc + 1 < NSC) next_arg = arg_of(s, sc + 1, mu);
+    } else {
+      arg = arg_of(s, sc, mu);
+    }
     const float pv = (EMU > 0 && (sc & 3) >= 4 - EMU) ? exp2_poly(arg) : __builtin_amdgcn_exp2f(arg);
     if constexpr (DEFER) {
       if (sc & 1) {
@@ -524,6 +534,7 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
 
     float mu = (m_ref == NEG_INF) ? 0.f : m_ref;
     float part0 = 0.f, part1 = 0.f, even = 0.f, odd = 0.f, partq = 0.f;
+    float next_arg = DEFER ? arg_of(s, 0, mu) : 0.f;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) sn.v[kb][0] = (f32x16){};
 #pragma unroll
@@ -542,7 +553,8 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
       }
       // scores [ch * NSC / NCH, (ch + 1) * NSC / NCH)
 #pragma unroll
-      for (int sc = ch * NSC / NCH; sc < (ch + 1) * NSC / NCH; ++sc) score(s, pf, sc, mu, part0, part1, even, odd, partq);
+      for (int sc = ch * NSC / NCH; sc < (ch + 1) * NSC / NCH; ++sc)
+        score(s, pf, sc, mu, part0, part1, even, odd, partq, next_arg);
       // the NCP copy instructions over the first half of the chunks, so each
       // has more than half an iteration to land (against spreading them over
       // all chunks: +1 % at d = 128, +5 % at d = 64 causal, +10 % at d = 256;
@@ -577,8 +589,9 @@ __device__ __forceinline__ void fwd_bf16_item(const __bf16* __restrict__ Q, cons
         m_ref = m_run;
         mu = (m_ref == NEG_INF) ? 0.f : m_ref;
         part0 = part1 = partq = 0.f;
+        next_arg = arg_of(s, 0, mu);
 #pragma unroll
-        for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even, odd, partq);
+        for (int sc = 0; sc < NSC; ++sc) score(s, pf, sc, mu, part0, part1, even, odd, partq, next_arg);
         if constexpr (DEFER) flush_pair(pf, NSC - 1, part1, even, odd, partq);
         part = part0 + part1;
       }
