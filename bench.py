@@ -21,7 +21,7 @@ stream the kernels run on.  Prints one JSON line on stdout
             the MI355X dense MFMA peak for its dtype; the HBM traffic, the
             sustained clock, the MFMA-busy share, the LDS bank-conflict rate
             and the VALU mix measured by rocprofv3 counters on the same kernel
-            source (profiles/counters_config<N>.txt;
+            source (profiles/counters_config<N>.txt; hbm_gbs = those bytes over the launch time;
             omitted or null when the source changed since they were taken),
             with the fraction of the peak at that clock; and the measured MFMA
             ceiling (fa_mfma_ceiling, a loop of the same matrix instruction on
@@ -678,6 +678,11 @@ def main():
                      "kernel_ms_median": round(float(np.median(launch_ms)), 5),
                      "kernel_ms_min": round(float(np.min(launch_ms)), 5), "launches": len(launch_ms)},
     }
+    if traffic:
+        # the HBM bytes the counters saw per launch over this run's launch time,
+        # against the 8 TB/s of HBM3E (the kernel is matrix-bound; this shows by how far)
+        hbm_gbs = traffic / (kernel_ms * 1e-3) / 1e9
+        line["roofline"].update({"hbm_gbs": round(hbm_gbs, 1), "hbm_frac": round(hbm_gbs / 8000.0, 4)})
     if counters:
         # the same kernel under rocprofv3 counters: the clock it sustains and
         # the share of SIMD cycles its matrix pipe was busy
